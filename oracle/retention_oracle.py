@@ -1,0 +1,236 @@
+"""Plain fp64 CPU oracle for Multi-Scale Retention (test infrastructure only).
+
+This module is the checker, not the product. Only the test suite, the smoke
+check in ``__graft_entry__`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import it. It shares no code with the HIP library and imports nothing from it.
+
+Sources (the pages this follows; cited by tag below):
+  [KR]  "RetNet - Retentive Network - A Successor to Transformer for LLMs"
+        (irregular6612.github.io blog): Methods; Key components (1. Retention,
+        2. Multi-Scale Retention); Key Equations (recurrent, parallel and
+        chunkwise recurrent forms).
+  [JP]  jisaku.com glossary entry on RetNet: the retention definition with the
+        causal decay mask, and the three computation modes.
+  [EN]  "What Is RetNet ? could it challenge the dominance of the Transformer ?"
+        (medium.com, Publicis Sapient): "How is this dual representation
+        achieved?" (the matrix D and the GroupNorm that follows it).
+
+Conventions (readings where the pages are silent, all listed in the design doc):
+  * positions n, m and the head index h are 0-based;
+  * shapes: q, k are [B, H, N, dk]; v is [B, H, N, dv]; a state is
+    [B, H, dk, dv]; gamma is [H];
+  * a recurrent step updates the state first and then reads it out, so token
+    n sees itself with weight gamma^0 = 1;
+  * the chunkwise form uses xi_j = gamma^(j+1) on the cross-chunk read-out and
+    zeta_j = gamma^(L-1-j) inside the state update, for local row j of a chunk
+    of length L; these are the only factors that make it equal the recurrence.
+
+Every function widens its inputs to float64 and runs in float64. Nothing here
+is blocked, fused or reordered beyond what the cited definition states.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(x):
+    """Exact widening of a numpy array or CPU torch tensor to float64."""
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu").double().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _zero_state(q, v):
+    B, H, _, dk = q.shape
+    dv = v.shape[-1]
+    return np.zeros((B, H, dk, dv), dtype=np.float64)
+
+
+def decay_mask(N, gamma):
+    """The N x N causal decay matrix of one head.
+
+    [KR] Key Equations, parallel form; [JP] retention definition:
+    D[n, m] = gamma^(n - m) for n >= m and 0 for n < m. With gamma = 0 the
+    diagonal stays 1 (0^0 = 1), so the gamma -> 0 limit is well defined.
+    """
+    n = np.arange(N)[:, None]
+    m = np.arange(N)[None, :]
+    diff = n - m
+    g = float(gamma)
+    out = np.where(diff >= 0, np.power(g, np.maximum(diff, 0).astype(np.float64)), 0.0)
+    return out
+
+
+def parallel(q, k, v, gamma, state_in=None):
+    """Parallel form, O = (Q K^T * D) V per head.
+
+    [KR] Key Equations, parallel form; [JP] retention definition and the
+    parallel mode. Multi-Scale Retention runs this independently per head h
+    with that head's own gamma_h ([KR] Key components, 2. Multi-Scale
+    Retention).
+
+    When ``state_in`` S0 is given the output also carries the contribution of
+    the history summarised by S0: the recurrence unrolled from S_{-1} = S0
+    adds gamma^(n+1) q_n S0 to row n. The parallel form on the pages has no
+    state; this term only exists so the three forms can be compared with a
+    starting state.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    g = _f64(gamma)
+    B, H, N, _ = q.shape
+    out = np.empty((B, H, N, v.shape[-1]), dtype=np.float64)
+    S0 = None if state_in is None else _f64(state_in)
+    for h in range(H):
+        D = decay_mask(N, g[h])
+        for b in range(B):
+            scores = (q[b, h] @ k[b, h].T) * D
+            out[b, h] = scores @ v[b, h]
+            if S0 is not None:
+                xi = np.power(g[h], np.arange(1, N + 1, dtype=np.float64))
+                out[b, h] += xi[:, None] * (q[b, h] @ S0[b, h])
+    return out
+
+
+def parallel_rows(q, k, v, gamma, rows, state_in=None):
+    """Selected output rows of the parallel form, one row at a time.
+
+    Row n of [KR] Key Equations, parallel form, written as the sum it is:
+    o_n = sum_{m <= n} gamma^(n-m) (q_n . k_m) v_m  (+ gamma^(n+1) q_n S0).
+    Used to sample outputs at sizes where the full N x N product is too big.
+    Returns an array [B, H, len(rows), dv].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    g = _f64(gamma)
+    B, H, N, _ = q.shape
+    rows = [int(r) for r in rows]
+    out = np.empty((B, H, len(rows), v.shape[-1]), dtype=np.float64)
+    S0 = None if state_in is None else _f64(state_in)
+    for i, n in enumerate(rows):
+        for h in range(H):
+            w = np.power(g[h], np.arange(n, -1, -1, dtype=np.float64))  # gamma^(n-m), m=0..n
+            for b in range(B):
+                s = (k[b, h, : n + 1] @ q[b, h, n]) * w
+                out[b, h, i] = s @ v[b, h, : n + 1]
+                if S0 is not None:
+                    out[b, h, i] += (g[h] ** (n + 1)) * (q[b, h, n] @ S0[b, h])
+    return out
+
+
+def recurrent_step(q, k, v, gamma, state):
+    """One token of the recurrent form.
+
+    [KR] Methods and Key Equations, recurrent form; [JP] recurrent mode:
+    S_n = gamma * S_{n-1} + k_n^T v_n (a dk x dv outer product), then
+    o_n = q_n S_n. Shapes: q, k [B, H, dk]; v [B, H, dv]; state [B, H, dk, dv].
+    Returns (o [B, H, dv], new state).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    g = _f64(gamma)
+    S = _f64(state)
+    S_new = g[None, :, None, None] * S + k[..., :, None] * v[..., None, :]
+    o = np.einsum("bhk,bhkv->bhv", q, S_new)
+    return o, S_new
+
+
+def recurrent(q, k, v, gamma, state_in=None):
+    """Recurrent form over a whole sequence, token by token.
+
+    [KR] Key Equations, recurrent form, iterated from S_{-1} = state_in
+    (zeros when absent). Returns (o [B, H, N, dv], S_{N-1}).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    N = q.shape[2]
+    S = _zero_state(q, v) if state_in is None else _f64(state_in).copy()
+    out = np.empty(q.shape[:3] + (v.shape[-1],), dtype=np.float64)
+    for n in range(N):
+        out[:, :, n], S = recurrent_step(q[:, :, n], k[:, :, n], v[:, :, n], gamma, S)
+    return out, S
+
+
+def chunkwise(q, k, v, gamma, chunk, state_in=None):
+    """Chunkwise recurrent form: parallel inside a chunk, recurrent across.
+
+    [KR] Key Equations, chunkwise recurrent form (inner parallel term plus the
+    cross-chunk term (Q_[i] * xi) R_{i-1}) and Key components, 1. Retention
+    (the chunk-state carry); [JP] chunkwise mode.
+
+    For chunk i with rows [i*C, i*C + L) and local row j:
+      O_[i] = (Q_[i] K_[i]^T * D_L) V_[i] + diag(xi) Q_[i] R_{i-1},
+      R_i   = gamma^L R_{i-1} + K_[i]^T diag(zeta) V_[i],
+    with xi_j = gamma^(j+1), zeta_j = gamma^(L-1-j), R_{-1} = state_in (or 0).
+    The carry printed on the page lacks the in-chunk factor zeta; taken
+    literally it would break the equality with the recurrence that the same
+    page asserts, so zeta is included (reading recorded in the design doc).
+    Returns (o [B, H, N, dv], R_last).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    g = _f64(gamma)
+    B, H, N, _ = q.shape
+    C = int(chunk)
+    if C < 1:
+        raise ValueError("chunk must be >= 1")
+    R = _zero_state(q, v) if state_in is None else _f64(state_in).copy()
+    out = np.empty((B, H, N, v.shape[-1]), dtype=np.float64)
+    for start in range(0, N, C):
+        L = min(C, N - start)
+        sl = slice(start, start + L)
+        j = np.arange(L, dtype=np.float64)
+        for h in range(H):
+            D = decay_mask(L, g[h])
+            xi = np.power(g[h], j + 1.0)
+            zeta = np.power(g[h], (L - 1.0) - j)
+            carry = g[h] ** L
+            for b in range(B):
+                Qi, Ki, Vi = q[b, h, sl], k[b, h, sl], v[b, h, sl]
+                inner = ((Qi @ Ki.T) * D) @ Vi
+                cross = xi[:, None] * (Qi @ R[b, h])
+                out[b, h, sl] = inner + cross
+                R[b, h] = carry * R[b, h] + Ki.T @ (zeta[:, None] * Vi)
+    return out, R
+
+
+def state_after(k, v, gamma, state_in=None):
+    """State after all N tokens, the recurrence unrolled in closed form.
+
+    Unrolling [KR] Key Equations, recurrent form, from S_{-1} = S0 gives
+    S_{N-1} = gamma^N S0 + sum_m gamma^(N-1-m) k_m^T v_m.
+    """
+    k, v = _f64(k), _f64(v)
+    g = _f64(gamma)
+    B, H, N, dk = k.shape
+    S = np.empty((B, H, dk, v.shape[-1]), dtype=np.float64)
+    for h in range(H):
+        w = np.power(g[h], np.arange(N - 1, -1, -1, dtype=np.float64))
+        for b in range(B):
+            S[b, h] = k[b, h].T @ (w[:, None] * v[b, h])
+            if state_in is not None:
+                S[b, h] += (g[h] ** N) * _f64(state_in)[b, h]
+    return S
+
+
+def group_norm(o, eps=1e-5, weight=None, bias=None):
+    """Per-head GroupNorm applied to retention outputs.
+
+    [KR] Methods (block: MSR, then GroupNorm) and Key components, 4. block;
+    [EN] "How is this dual representation achieved?" (a GroupNorm after the
+    retention product). One group per head: for each (b, h, n) the mean and
+    the biased variance are taken over that head's dv outputs, then
+    y = (o - mean) / sqrt(var + eps) * weight[h] + bias[h]. ``weight`` and
+    ``bias`` are [H, dv] (or flat [H*dv]); absent means identity.
+    """
+    o = _f64(o)
+    H, dv = o.shape[1], o.shape[-1]
+    mu = o.mean(axis=-1, keepdims=True)
+    var = ((o - mu) ** 2).mean(axis=-1, keepdims=True)
+    y = (o - mu) / np.sqrt(var + float(eps))
+    if weight is not None:
+        y = y * _f64(weight).reshape(1, H, 1, dv)
+    if bias is not None:
+        y = y + _f64(bias).reshape(1, H, 1, dv)
+    return y
+
+
+def group_norm_rows(o_rows, eps=1e-5, weight=None, bias=None):
+    """GroupNorm of sampled rows [B, H, R, dv]; same definition as group_norm."""
+    return group_norm(o_rows, eps, weight, bias)

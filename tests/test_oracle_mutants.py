@@ -1,0 +1,83 @@
+"""Plant plausible mistakes in copies of the oracle and check a pin catches each.
+
+The mutants live here, on the CPU; the oracle itself is untouched. Each
+mutant is one slip a reader could make when writing the forms from the pages
+(a dropped decay term, an off-by-one exponent, a transposed mask or operand,
+read-out before update). The pins are the brute-force double loop and the
+hand-worked fixture.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import retention_oracle as orc
+from tests.test_oracle import _brute_parallel, _brute_state_one_based, _inputs
+
+
+def _chunkwise_mutant(q, k, v, gamma, chunk, kind):
+    B, H, N, _ = q.shape
+    R = np.zeros((B, H, q.shape[-1], v.shape[-1]))
+    out = np.empty((B, H, N, v.shape[-1]))
+    for start in range(0, N, chunk):
+        L = min(chunk, N - start)
+        sl = slice(start, start + L)
+        j = np.arange(L, dtype=np.float64)
+        for h in range(H):
+            g = gamma[h]
+            D = orc.decay_mask(L, g)
+            xi = g ** (j + 1.0)
+            zeta = g ** (L - 1.0 - j)
+            carry = g ** L
+            if kind == "no_zeta":  # the carry exactly as printed, without in-chunk decay
+                zeta = np.ones(L)
+            elif kind == "xi_off_by_one":
+                xi = g ** j
+            elif kind == "mask_transposed":
+                D = D.T
+            elif kind == "carry_off_by_one":
+                carry = g ** (L - 1)
+            for b in range(B):
+                Qi, Ki, Vi = q[b, h, sl], k[b, h, sl], v[b, h, sl]
+                out[b, h, sl] = ((Qi @ Ki.T) * D) @ Vi + xi[:, None] * (Qi @ R[b, h])
+                R[b, h] = carry * R[b, h] + Ki.T @ (zeta[:, None] * Vi)
+    return out, R
+
+
+def _recurrent_readout_first(q, k, v, gamma):
+    B, H, N, dk = q.shape
+    S = np.zeros((B, H, dk, v.shape[-1]))
+    out = np.empty((B, H, N, v.shape[-1]))
+    for n in range(N):
+        out[:, :, n] = np.einsum("bhk,bhkv->bhv", q[:, :, n], S)
+        S = gamma[None, :, None, None] * S + k[:, :, n, :, None] * v[:, :, n, None, :]
+    return out, S
+
+
+@pytest.mark.parametrize("kind", ["no_zeta", "xi_off_by_one", "mask_transposed", "carry_off_by_one"])
+def test_chunkwise_mutants_are_caught(kind):
+    q, k, v = _inputs(1, 2, 11, 3, 2, seed=7)
+    g = np.array([0.9, 0.6])
+    ref_o = _brute_parallel(q, k, v, g)
+    ref_S = _brute_state_one_based(k, v, g)
+    o, S = _chunkwise_mutant(q, k, v, g, 4, kind)
+    caught = np.max(np.abs(o - ref_o)) > 1e-6 or np.max(np.abs(S - ref_S)) > 1e-6
+    assert caught, kind
+    # The unmutated copy of the same code passes, so the harness itself is sound.
+    o0, S0 = _chunkwise_mutant(q, k, v, g, 4, "none")
+    assert np.max(np.abs(o0 - ref_o)) < 1e-10 and np.max(np.abs(S0 - ref_S)) < 1e-10
+
+
+def test_readout_before_update_is_caught():
+    q, k, v = _inputs(1, 1, 6, 2, 2, seed=9)
+    g = np.array([0.5])
+    o, _ = _recurrent_readout_first(q, k, v, g)
+    assert np.max(np.abs(o - _brute_parallel(q, k, v, g))) > 1e-6
+
+
+def test_transposed_operand_is_caught():
+    """Swapping K and V roles (dk != dv) cannot even run; swapping Q and K changes the result."""
+    q, k, v = _inputs(1, 1, 8, 3, 3, seed=11)
+    g = np.array([0.8])
+    ref = _brute_parallel(q, k, v, g)
+    swapped = orc.parallel(k, q, v, g)
+    assert np.max(np.abs(swapped - ref)) > 1e-6
