@@ -1,0 +1,141 @@
+/*
+ * retention.h — C ABI of the Multi-Scale Retention library (gfx950 / MI355X).
+ *
+ * The operator (sources, by page title and section):
+ *   "RetNet - Retentive Network - A Successor to Transformer for LLMs"
+ *   (irregular6612.github.io blog):
+ *     - Key Equations, parallel form: O = (Q K^T (*) D) V with the causal decay
+ *       mask D[n][m] = gamma^(n-m) for n >= m and 0 otherwise;
+ *     - Key Equations, recurrent form: S_n = gamma S_{n-1} + K_n^T V_n,
+ *       o_n = Q_n S_n;
+ *     - Key Equations, chunkwise recurrent form: parallel inside a chunk plus
+ *       a cross-chunk read-out (Q_[i] (*) xi) R_{i-1} of the carried state;
+ *     - Key components, 2. Multi-Scale Retention: each head has its own decay
+ *       (the usual schedule is gamma_h = 1 - 2^(-5-h));
+ *     - Methods / Key components, 4. block: a GroupNorm follows retention.
+ *   jisaku.com RetNet glossary entry: the same definition, 0 < gamma < 1, and
+ *   the three computation modes (parallel, recurrent, chunkwise).
+ *
+ * Conventions shared by every entry point:
+ *   - Q, K are [B, H, N, dk] and V, O are [B, H, N, dv], contiguous row-major
+ *     device buffers of the element type `dtype` (RET_F32 or RET_BF16). O has
+ *     the input's element type; bf16 results are rounded to nearest even.
+ *   - A state S is fp32 [B, H, dk, dv], contiguous row-major, dv fastest.
+ *     A recurrent step updates the state first and then reads it out, so a
+ *     token sees itself with weight 1.
+ *   - gamma_host is a HOST array of H floats, each finite with 0 < gamma < 1.
+ *     It is read during the call only and may be freed on return.
+ *   - gn (optional, NULL = none) asks for the per-head GroupNorm epilogue:
+ *     for each (b, h, n) the mean and biased variance over that head's dv
+ *     outputs, y = (o - mean) / sqrt(var + eps) * weight[h*dv + c] + bias[h*dv + c].
+ *     weight and bias are device fp32 [H*dv] and may each be NULL (identity).
+ *   - stream is a hipStream_t (NULL = the default stream). All work is
+ *     enqueued on it and the call returns without synchronising. RET_OK means
+ *     "validated and launched"; a fault inside a kernel surfaces on the next
+ *     synchronising HIP call of the caller.
+ *   - Ownership: the caller owns every buffer. The library allocates no
+ *     device memory and keeps no mutable global state; calls on different
+ *     streams do not interfere except through buffers the caller shares.
+ *   - O must not alias Q, K or V. No entry point throws; all report status.
+ *
+ * Status codes:
+ *   RET_OK (0), RET_ERR_INVALID_ARG (-1): a required pointer is NULL, a size
+ *   is <= 0, chunk <= 0, a gamma is not in (0, 1), dtype is unknown, or the
+ *   workspace is too small; RET_ERR_UNSUPPORTED (-2): valid arguments outside
+ *   what the kernels implement (for example H > RETENTION_MAX_HEADS or dk
+ *   above RETENTION_MAX_DK); RET_ERR_HIP (-3): the HIP runtime reported an
+ *   error for a launch. Invalid or unsupported arguments are detected before
+ *   any HIP call is made.
+ */
+#ifndef RETENTION_H
+#define RETENTION_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RETENTION_ABI_VERSION 1
+#define RETENTION_MAX_HEADS 256
+#define RETENTION_MAX_DK 256
+#define RETENTION_MAX_DV 1024
+
+enum retention_dtype { RET_F32 = 0, RET_BF16 = 1 };
+
+enum retention_status {
+  RET_OK = 0,
+  RET_ERR_INVALID_ARG = -1,
+  RET_ERR_UNSUPPORTED = -2,
+  RET_ERR_HIP = -3
+};
+
+typedef struct retention_gn_t {
+  float eps;            /* added to the variance; must be >= 0 and finite */
+  const float* weight;  /* device fp32 [H*dv], or NULL for 1 */
+  const float* bias;    /* device fp32 [H*dv], or NULL for 0 */
+} retention_gn_t;
+
+/* RETENTION_ABI_VERSION of the built library. */
+int retention_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. Never NULL. */
+const char* retention_status_string(int status);
+
+/*
+ * Parallel form ("RetNet - Retentive Network ...", Key Equations, parallel
+ * form; jisaku.com glossary, parallel mode): for every (b, h),
+ *   o_n = sum_{m <= n} gamma_h^(n-m) (q_n . k_m) v_m,
+ * then the optional GroupNorm. The N x N decay mask is never materialised.
+ */
+int retention_parallel(const void* q, const void* k, const void* v,
+                       const float* gamma_host, void* o,
+                       int B, int H, int N, int dk, int dv, int dtype,
+                       const retention_gn_t* gn, void* stream);
+
+/*
+ * Bytes of device workspace retention_chunkwise needs for these sizes
+ * (a pure function of its arguments; 0 for invalid sizes).
+ */
+size_t retention_chunkwise_workspace_bytes(int B, int H, int N, int dk, int dv,
+                                           int chunk, int dtype);
+
+/*
+ * Chunkwise recurrent form ("RetNet - Retentive Network ...", Key Equations,
+ * chunkwise recurrent form and Key components, 1. Retention; jisaku.com
+ * glossary, chunkwise mode). With chunk length C, chunk i covers rows
+ * [i*C, min(i*C + C, N)) of length L (the last chunk may be shorter); for
+ * local row j, xi_j = gamma^(j+1) and zeta_j = gamma^(L-1-j):
+ *   O_[i] = (Q_[i] K_[i]^T (*) D_L) V_[i] + diag(xi) Q_[i] R_{i-1}
+ *   R_i   = gamma^L R_{i-1} + K_[i]^T diag(zeta) V_[i]
+ * with R_{-1} = state_in (NULL: zeros). state_out (NULL: not written)
+ * receives R of the last chunk and may alias state_in. The result equals the
+ * parallel and recurrent forms up to rounding. workspace must hold at least
+ * retention_chunkwise_workspace_bytes(...) bytes (it may be NULL when that is
+ * 0); its contents on entry do not matter and are clobbered.
+ */
+int retention_chunkwise(const void* q, const void* k, const void* v,
+                        const float* gamma_host, void* o,
+                        int B, int H, int N, int dk, int dv, int chunk, int dtype,
+                        const float* state_in, float* state_out,
+                        const retention_gn_t* gn,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One recurrent decode step ("RetNet - Retentive Network ...", Key
+ * Equations, recurrent form; jisaku.com glossary, recurrent mode):
+ *   state <- gamma_h * state + k^T v   (in place, fp32 [B, H, dk, dv])
+ *   o      = q . state                 (then the optional GroupNorm)
+ * q, k are [B, H, dk] (one token), v and o are [B, H, dv], of type dtype.
+ * state is required.
+ */
+int retention_recurrent_step(const void* q, const void* k, const void* v,
+                             const float* gamma_host, float* state, void* o,
+                             int B, int H, int dk, int dv, int dtype,
+                             const retention_gn_t* gn, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RETENTION_H */

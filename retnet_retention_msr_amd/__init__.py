@@ -1,0 +1,184 @@
+"""Multi-Scale Retention on MI355X: a thin torch binding of libretention.so.
+
+The functions here only marshal arguments: they check tensors, allocate
+outputs and workspace with torch, and call the C ABI (include/retention.h) on
+the current HIP stream. Every step of the computation runs in the library's
+HIP kernels; there is no other code path. The operator follows "RetNet -
+Retentive Network - A Successor to Transformer for LLMs" (Key Equations:
+parallel, recurrent and chunkwise recurrent forms; Key components, 2.
+Multi-Scale Retention) and the jisaku.com RetNet glossary entry.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Sequence, Union
+
+import torch
+
+from . import _lib
+
+__all__ = [
+    "GroupNorm",
+    "parallel",
+    "chunkwise",
+    "recurrent_step",
+    "chunkwise_workspace_bytes",
+    "RetentionError",
+]
+
+
+class RetentionError(RuntimeError):
+    """A non-zero status from the C ABI."""
+
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {_lib.status_string(code)} ({code})")
+        self.code = code
+
+
+@dataclass
+class GroupNorm:
+    """Per-head GroupNorm epilogue: eps and optional fp32 [H*dv] weight/bias on the device."""
+
+    eps: float = 1e-5
+    weight: Optional[torch.Tensor] = None
+    bias: Optional[torch.Tensor] = None
+
+
+GammaLike = Union[torch.Tensor, Sequence[float]]
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return _lib.RET_F32
+    if t.dtype == torch.bfloat16:
+        return _lib.RET_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _gamma_array(gamma: GammaLike, H: int):
+    g = torch.as_tensor(gamma, dtype=torch.float32).detach().to("cpu").contiguous()
+    if g.numel() != H:
+        raise ValueError(f"gamma has {g.numel()} entries, expected H={H}")
+    arr = (ctypes.c_float * H)(*g.tolist())
+    return arr
+
+
+def _gn_struct(gn: Optional[GroupNorm], H: int, dv: int, device):
+    if gn is None:
+        return None, ()
+    keep = []
+    ptrs = []
+    for t in (gn.weight, gn.bias):
+        if t is None:
+            ptrs.append(None)
+            continue
+        if t.device != device or t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != H * dv:
+            raise ValueError("GroupNorm weight/bias must be contiguous float32 [H*dv] on the input's device")
+        keep.append(t)
+        ptrs.append(t.data_ptr())
+    s = _lib.GnStruct(float(gn.eps), ptrs[0], ptrs[1])
+    return ctypes.byref(s), (s, keep)
+
+
+def _check_qkv(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("expected q, k [B,H,N,dk] and v [B,H,N,dv]")
+    B, H, N, dk = q.shape
+    return B, H, N, dk, v.shape[3], _dtype_code(q)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def parallel(q, k, v, gamma: GammaLike, gn: Optional[GroupNorm] = None, out=None):
+    """Parallel form O = (Q K^T * D) V per head (optionally GroupNorm-ed)."""
+    lib = _lib.load()
+    B, H, N, dk, dv, dt = _check_qkv(q, k, v)
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    g = _gamma_array(gamma, H)
+    gn_p, _keep = _gn_struct(gn, H, dv, q.device)
+    rc = lib.retention_parallel(q.data_ptr(), k.data_ptr(), v.data_ptr(), g, out.data_ptr(), B, H, N, dk, dv, dt,
+                                gn_p, _stream(q))
+    if rc != 0:
+        raise RetentionError("retention_parallel", rc)
+    return out
+
+
+def chunkwise_workspace_bytes(B, H, N, dk, dv, chunk, dtype=torch.bfloat16) -> int:
+    code = _lib.RET_BF16 if dtype == torch.bfloat16 else _lib.RET_F32
+    return int(_lib.load().retention_chunkwise_workspace_bytes(B, H, N, dk, dv, int(chunk), code))
+
+
+def chunkwise(q, k, v, gamma: GammaLike, chunk: int, state_in=None, state_out: Union[bool, torch.Tensor] = False,
+              gn: Optional[GroupNorm] = None, out=None, workspace=None):
+    """Chunkwise recurrent form. Returns (o, state_out or None).
+
+    ``state_out``: False (not produced), True (allocate), or an fp32
+    [B,H,dk,dv] tensor to fill (it may be ``state_in`` itself).
+    """
+    lib = _lib.load()
+    B, H, N, dk, dv, dt = _check_qkv(q, k, v)
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    for name, s in (("state_in", state_in), ("state_out", state_out)):
+        if isinstance(s, torch.Tensor):
+            if s.dtype != torch.float32 or not s.is_contiguous() or tuple(s.shape) != (B, H, dk, dv):
+                raise ValueError(f"{name} must be contiguous float32 [B,H,dk,dv]")
+    if state_out is True:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    elif state_out is False:
+        state_out = None
+    nbytes = int(lib.retention_chunkwise_workspace_bytes(B, H, N, dk, dv, int(chunk), dt))
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    g = _gamma_array(gamma, H)
+    gn_p, _keep = _gn_struct(gn, H, dv, q.device)
+    rc = lib.retention_chunkwise(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), g, out.data_ptr(), B, H, N, dk, dv, int(chunk), dt,
+        state_in.data_ptr() if state_in is not None else None,
+        state_out.data_ptr() if state_out is not None else None,
+        gn_p, ws_ptr, ws_bytes, _stream(q))
+    if rc != 0:
+        raise RetentionError("retention_chunkwise", rc)
+    return out, state_out
+
+
+def recurrent_step(q, k, v, gamma: GammaLike, state, gn: Optional[GroupNorm] = None, out=None):
+    """One decode step: state <- gamma*state + k^T v (in place), returns o = q.state.
+
+    q, k are [B,H,dk] (or [B,H,1,dk]); v is [B,H,dv] (or [B,H,1,dv]).
+    """
+    lib = _lib.load()
+    for name, t in (("q", q), ("k", k), ("v", v), ("state", state)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if state.dtype != torch.float32 or state.dim() != 4:
+        raise ValueError("state must be float32 [B,H,dk,dv]")
+    B, H, dk, dv = state.shape
+    if q.numel() != B * H * dk or k.numel() != B * H * dk or v.numel() != B * H * dv:
+        raise ValueError("q, k must hold B*H*dk and v B*H*dv elements")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    g = _gamma_array(gamma, H)
+    gn_p, _keep = _gn_struct(gn, H, dv, q.device)
+    rc = lib.retention_recurrent_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), g, state.data_ptr(),
+                                      out.data_ptr(), B, H, dk, dv, dt, gn_p, _stream(q))
+    if rc != 0:
+        raise RetentionError("retention_recurrent_step", rc)
+    return out

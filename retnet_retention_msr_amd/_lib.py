@@ -1,0 +1,68 @@
+"""ctypes declarations of the C ABI in include/retention.h."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libretention.so")
+
+RET_F32 = 0
+RET_BF16 = 1
+RET_OK = 0
+RET_ERR_INVALID_ARG = -1
+RET_ERR_UNSUPPORTED = -2
+RET_ERR_HIP = -3
+
+# Every symbol include/retention.h declares.
+EXPORTED = (
+    "retention_abi_version",
+    "retention_status_string",
+    "retention_parallel",
+    "retention_chunkwise_workspace_bytes",
+    "retention_chunkwise",
+    "retention_recurrent_step",
+)
+
+
+class GnStruct(ctypes.Structure):
+    """retention_gn_t: eps, device weight pointer, device bias pointer."""
+
+    _fields_ = [("eps", ctypes.c_float), ("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load():
+    """Load libretention.so from the package directory (built in-tree)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m retnet_retention_msr_amd.build` "
+            "(there is no fallback path)"
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f_p, gn_p = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(GnStruct)
+    lib.retention_abi_version.argtypes = []
+    lib.retention_abi_version.restype = i
+    lib.retention_status_string.argtypes = [i]
+    lib.retention_status_string.restype = ctypes.c_char_p
+    lib.retention_parallel.argtypes = [vp, vp, vp, f_p, vp, i, i, i, i, i, i, gn_p, vp]
+    lib.retention_parallel.restype = i
+    lib.retention_chunkwise_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.retention_chunkwise_workspace_bytes.restype = ctypes.c_size_t
+    lib.retention_chunkwise.argtypes = [vp, vp, vp, f_p, vp, i, i, i, i, i, i, i, vp, vp, gn_p, vp,
+                                        ctypes.c_size_t, vp]
+    lib.retention_chunkwise.restype = i
+    lib.retention_recurrent_step.argtypes = [vp, vp, vp, f_p, vp, vp, i, i, i, i, i, gn_p, vp]
+    lib.retention_recurrent_step.restype = i
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load().retention_status_string(int(code)).decode()

@@ -1,0 +1,271 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Tolerances are those fixed for the operator: max|err| <= 1e-4 * max|o| for
+fp32 inputs and <= 2e-2 * max|o| for bf16 inputs, checked per (b, h) head
+slice against that slice's own max|o_ref| (stricter than one global max,
+because short-memory heads have much smaller outputs than long-memory ones).
+Both sides see identical inputs: bf16 tensors are widened exactly for the
+oracle. Inputs come from the seeded generators in
+retnet_retention_msr_amd.synthetic.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import retnet_retention_msr_amd as ret
+from oracle import retention_oracle as orc
+from retnet_retention_msr_amd import synthetic
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+DEV = "cuda:0"
+
+
+def _np(t):
+    return t.detach().to("cpu").double().numpy()
+
+
+def _check(got, ref, tol, what=""):
+    """Per-head check: max |got - ref| <= tol * max|ref| over each [b, h] slice."""
+    got = _np(got) if isinstance(got, torch.Tensor) else np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), what
+    B, H = ref.shape[:2]
+    for b in range(B):
+        for h in range(H):
+            scale = float(np.max(np.abs(ref[b, h])))
+            err = float(np.max(np.abs(got[b, h] - ref[b, h])))
+            assert err <= tol * max(scale, 1e-30), f"{what} b={b} h={h}: err {err:.3e} > {tol} * {scale:.3e}"
+
+
+def _inputs(B, H, N, dk, dv, dtype, seed, with_state=False):
+    q, k, v = synthetic.make_qkv(B, H, N, dk, dv, dtype=dtype, seed=seed)
+    g = synthetic.head_gammas(H)
+    S0 = synthetic.make_state(B, H, dk, dv, seed=seed + 1, std=0.5) if with_state else None
+    return q, k, v, g, S0
+
+
+def _dev(*ts):
+    return [None if t is None else t.to(DEV) for t in ts]
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Single-head fp32 case: B=1, H=1, N=64, d=16, gamma = 1 - 2^-5, chunk 16
+# ---------------------------------------------------------------------------
+
+
+def test_fp32_single_head_three_forms():
+    _announce("fp32 single head: parallel, chunkwise, recurrent steps")
+    q, k, v = synthetic.make_qkv(1, 1, 64, 16, 16, dtype=torch.float32, seed=1001, qk_var=1.0)
+    g = torch.tensor([1 - 2.0 ** -5], dtype=torch.float32)
+    ref, Sref = orc.recurrent(q, k, v, g)
+    qd, kd, vd = _dev(q, k, v)
+    _check(ret.parallel(qd, kd, vd, g), ref, 1e-4, "parallel")
+    o, S = ret.chunkwise(qd, kd, vd, g, 16, state_out=True)
+    _check(o, ref, 1e-4, "chunkwise")
+    _check(S, Sref, 1e-4, "chunkwise state")
+    state = torch.zeros(1, 1, 16, 16, device=DEV)
+    outs = [ret.recurrent_step(qd[:, :, n].contiguous(), kd[:, :, n].contiguous(), vd[:, :, n].contiguous(), g, state)
+            for n in range(64)]
+    _check(torch.stack(outs, dim=2), ref, 1e-4, "recurrent steps")
+    _check(state, Sref, 1e-4, "recurrent state")
+
+
+def test_fp32_closed_form_all_ones():
+    _announce("fp32 d=1 all-ones closed form")
+    N = 64
+    gamma = 1 - 2.0 ** -5
+    ones = torch.ones(1, 1, N, 1, device=DEV)
+    g = torch.tensor([gamma])
+    n = np.arange(N)
+    expect = ((1 - gamma ** (n + 1)) / (1 - gamma))[None, None, :, None]
+    _check(ret.parallel(ones, ones, ones, g), expect, 1e-4, "parallel")
+    _check(ret.chunkwise(ones, ones, ones, g, 16)[0], expect, 1e-4, "chunkwise")
+    state = torch.zeros(1, 1, 1, 1, device=DEV)
+    o = [ret.recurrent_step(ones[:, :, i].contiguous(), ones[:, :, i].contiguous(), ones[:, :, i].contiguous(), g,
+                            state) for i in range(N)]
+    _check(torch.stack(o, dim=2), expect, 1e-4, "recurrent")
+
+
+@pytest.mark.parametrize("N,C", [(61, 16), (100, 7), (33, 64)])
+def test_fp32_chunkwise_with_state_ragged(N, C):
+    _announce(f"fp32 chunkwise with state N={N} C={C}")
+    q, k, v, g, S0 = _inputs(2, 4, N, 24, 40, torch.float32, seed=N + C, with_state=True)
+    ref, Sref = orc.chunkwise(q, k, v, g, C, state_in=S0)
+    qd, kd, vd, S0d = _dev(q, k, v, S0)
+    o, S = ret.chunkwise(qd, kd, vd, g, C, state_in=S0d, state_out=True)
+    _check(o, ref, 1e-4, "o")
+    _check(S, Sref, 1e-4, "state")
+
+
+# ---------------------------------------------------------------------------
+# bf16 on the MFMA kernels: small sizes spanning several tiles and a ragged tail
+# ---------------------------------------------------------------------------
+
+BF16_SHAPES = [
+    # B, H, N, dk, dv, chunk
+    (2, 3, 200, 64, 128, 64),
+    (1, 2, 200, 64, 128, 128),
+    (1, 2, 130, 256, 512, 64),
+    (2, 2, 190, 96, 256, 128),
+    (1, 3, 300, 32, 128, 192),
+]
+
+
+@pytest.mark.parametrize("B,H,N,dk,dv,C", BF16_SHAPES)
+@pytest.mark.parametrize("with_state", [False, True])
+def test_bf16_chunkwise_matches_oracle(B, H, N, dk, dv, C, with_state):
+    _announce(f"bf16 chunkwise {B}x{H}x{N} dk={dk} dv={dv} C={C} state={with_state}")
+    q, k, v, g, S0 = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=N * 7 + dk + C, with_state=with_state)
+    ref, Sref = orc.chunkwise(q, k, v, g, C, state_in=S0)
+    qd, kd, vd, S0d = _dev(q, k, v, S0)
+    o, S = ret.chunkwise(qd, kd, vd, g, C, state_in=S0d, state_out=True)
+    _check(o, ref, 2e-2, "o")
+    _check(S, Sref, 2e-2, "state")
+
+
+@pytest.mark.parametrize("B,H,N,dk,dv,C", BF16_SHAPES[:4])
+def test_bf16_parallel_matches_oracle(B, H, N, dk, dv, C):
+    _announce(f"bf16 parallel {B}x{H}x{N} dk={dk} dv={dv}")
+    q, k, v, g, _ = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=N * 3 + dk)
+    ref = orc.parallel(q, k, v, g)
+    qd, kd, vd = _dev(q, k, v)
+    _check(ret.parallel(qd, kd, vd, g), ref, 2e-2, "parallel")
+
+
+@pytest.mark.parametrize("affine", [False, True])
+@pytest.mark.parametrize("form", ["parallel", "chunkwise"])
+def test_bf16_groupnorm_epilogue(affine, form):
+    _announce(f"bf16 GroupNorm {form} affine={affine}")
+    B, H, N, dk, dv, C = 2, 3, 200, 64, 256, 64
+    q, k, v, g, S0 = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=77, with_state=(form == "chunkwise"))
+    w, bvec = synthetic.make_gn_affine(H, dv, seed=78) if affine else (None, None)
+    if form == "parallel":
+        raw = orc.parallel(q, k, v, g)
+    else:
+        raw = orc.chunkwise(q, k, v, g, C, state_in=S0)[0]
+    ref = orc.group_norm(raw, eps=1e-5, weight=w, bias=bvec)
+    qd, kd, vd, S0d, wd, bd = _dev(q, k, v, S0, w, bvec)
+    gn = ret.GroupNorm(1e-5, wd, bd)
+    if form == "parallel":
+        o = ret.parallel(qd, kd, vd, g, gn=gn)
+    else:
+        o = ret.chunkwise(qd, kd, vd, g, C, state_in=S0d, gn=gn)[0]
+    _check(o, ref, 2e-2, "gn")
+
+
+def test_bf16_generic_fallback_shapes():
+    """bf16 sizes outside the MFMA kernels (dv=64, chunk not a multiple of 64) use the generic kernels."""
+    _announce("bf16 generic fallback")
+    q, k, v, g, S0 = _inputs(1, 2, 150, 48, 64, torch.bfloat16, seed=5, with_state=True)
+    ref, Sref = orc.chunkwise(q, k, v, g, 50, state_in=S0)
+    qd, kd, vd, S0d = _dev(q, k, v, S0)
+    o, S = ret.chunkwise(qd, kd, vd, g, 50, state_in=S0d, state_out=True)
+    _check(o, ref, 2e-2, "o")
+    _check(S, Sref, 2e-2, "state")
+    q, k, v, g, _ = _inputs(1, 2, 150, 64, 128, torch.bfloat16, seed=6)
+    ref, _ = orc.chunkwise(q, k, v, g, 40)
+    qd, kd, vd = _dev(q, k, v)
+    _check(ret.chunkwise(qd, kd, vd, g, 40)[0], ref, 2e-2, "o chunk 40")
+
+
+def test_bf16_segmented_walk_and_aliased_state():
+    """Few heads, many chunks: the state walk is cut into segments; state_out aliases state_in."""
+    _announce("bf16 segmented walk")
+    B, H, N, dk, dv, C = 1, 2, 1024 + 40, 64, 128, 64
+    q, k, v, g, S0 = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=11, with_state=True)
+    ref, Sref = orc.chunkwise(q, k, v, g, C, state_in=S0)
+    qd, kd, vd, Sd = _dev(q, k, v, S0)
+    o, S = ret.chunkwise(qd, kd, vd, g, C, state_in=Sd, state_out=Sd)
+    assert S is Sd
+    _check(o, ref, 2e-2, "o")
+    _check(Sd, Sref, 2e-2, "state")
+
+
+# ---------------------------------------------------------------------------
+# Decode step
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("gn_on", [False, True])
+@pytest.mark.parametrize("dv", [128, 100])
+def test_decode_steps_match_oracle(dtype, gn_on, dv):
+    _announce(f"decode dtype={dtype} gn={gn_on} dv={dv}")
+    B, H, dk, steps = 2, 3, 64, 5
+    q, k, v = synthetic.make_qkv(B, H, steps, dk, dv, dtype=dtype, seed=21, qk_var=1.0)
+    g = synthetic.head_gammas(H)
+    S = synthetic.make_state(B, H, dk, dv, seed=22)
+    w, bvec = synthetic.make_gn_affine(H, dv, seed=23)
+    Sd = S.to(DEV)
+    qd, kd, vd, wd, bd = _dev(q, k, v, w, bvec)
+    Sref = S.double().numpy()
+    tol = TOL[dtype]
+    for n in range(steps):
+        o_ref, Sref = orc.recurrent_step(q[:, :, n], k[:, :, n], v[:, :, n], g, Sref)
+        if gn_on:
+            o_ref = orc.group_norm(o_ref[:, :, None, :], 1e-5, w, bvec)[:, :, 0]
+        gn = ret.GroupNorm(1e-5, wd, bd) if gn_on else None
+        o = ret.recurrent_step(qd[:, :, n].contiguous(), kd[:, :, n].contiguous(), vd[:, :, n].contiguous(), g, Sd,
+                               gn=gn)
+        _check(o, o_ref, tol, f"o step {n}")
+    _check(Sd, Sref, 1e-5, "state")
+
+
+# ---------------------------------------------------------------------------
+# Agreement between the GPU forms, the prefill seam, determinism
+# ---------------------------------------------------------------------------
+
+
+def test_gpu_forms_agree_bf16():
+    _announce("bf16 GPU forms agree")
+    B, H, N, dk, dv = 1, 4, 192, 64, 128
+    q, k, v, g, _ = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=31)
+    qd, kd, vd = _dev(q, k, v)
+    o_par = ret.parallel(qd, kd, vd, g)
+    o_chk, _ = ret.chunkwise(qd, kd, vd, g, 64)
+    state = torch.zeros(B, H, dk, dv, device=DEV)
+    o_rec = torch.stack([ret.recurrent_step(qd[:, :, n].contiguous(), kd[:, :, n].contiguous(),
+                                            vd[:, :, n].contiguous(), g, state) for n in range(N)], dim=2)
+    ref = _np(o_rec)
+    _check(o_par, ref, 2e-2, "parallel vs recurrent")
+    _check(o_chk, ref, 2e-2, "chunkwise vs recurrent")
+    _check(o_chk, _np(o_par), 2e-2, "chunkwise vs parallel")
+
+
+def test_prefill_seam_bf16():
+    _announce("bf16 prefill seam")
+    B, H, N, dk, dv, C, N1 = 1, 3, 320, 64, 128, 64, 128
+    q, k, v, g, _ = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=41)
+    qd, kd, vd = _dev(q, k, v)
+    o_all, S_all = ret.chunkwise(qd, kd, vd, g, C, state_out=True)
+    o1, S1 = ret.chunkwise(qd[:, :, :N1].contiguous(), kd[:, :, :N1].contiguous(), vd[:, :, :N1].contiguous(), g, C,
+                           state_out=True)
+    o2, S2 = ret.chunkwise(qd[:, :, N1:].contiguous(), kd[:, :, N1:].contiguous(), vd[:, :, N1:].contiguous(), g, C,
+                           state_in=S1, state_out=True)
+    _check(torch.cat([o1, o2], dim=2), _np(o_all), 2e-2, "seam o")
+    _check(S2, _np(S_all), 2e-2, "seam state")
+
+
+def test_bitwise_reproducible():
+    _announce("bitwise reproducibility")
+    q, k, v, g, S0 = _inputs(2, 4, 256, 128, 256, torch.bfloat16, seed=51, with_state=True)
+    qd, kd, vd, S0d = _dev(q, k, v, S0)
+    gn = ret.GroupNorm(1e-5)
+    a, Sa = ret.chunkwise(qd, kd, vd, g, 64, state_in=S0d, state_out=True, gn=gn)
+    b, Sb = ret.chunkwise(qd, kd, vd, g, 64, state_in=S0d, state_out=True, gn=gn)
+    assert torch.equal(a, b) and torch.equal(Sa, Sb)
+
+
+def test_invalid_gamma_raises():
+    q, k, v, g, _ = _inputs(1, 2, 64, 32, 128, torch.bfloat16, seed=61)
+    qd, kd, vd = _dev(q, k, v)
+    with pytest.raises(ret.RetentionError):
+        ret.parallel(qd, kd, vd, [0.5, 1.0])
