@@ -102,6 +102,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-batch-rows", type=int, default=8)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (reference for HBM byte counters)")
+    ap.add_argument("--skip-decode", action="store_true")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -118,6 +121,13 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(f"[bench] generating inputs B={B} H={H} N={N} dk={DK} dv={DV}", file=sys.stderr, flush=True)
     q, k, v = synthetic.make_qkv(B, H, N, DK, DV, dtype=torch.bfloat16, seed=SEED)
     gamma = synthetic.head_gammas(H)
@@ -148,7 +158,9 @@ def main():
     flops = algorithmic_flops(B, H, N, CHUNK)
     achieved = flops / (ms * 1e-3)
 
-    # Decode: 1024 single-token steps from the prefill's state.
+    # Decode: single-token steps from the prefill's state.
+    if args.skip_decode:
+        args.decode_steps = 0
     print(f"[bench] timing {args.decode_steps} decode steps", file=sys.stderr, flush=True)
     gen = torch.Generator().manual_seed(DECODE_SEED)
     T = args.decode_steps
@@ -166,7 +178,7 @@ def main():
         ret.recurrent_step(dq[i], dk_[i], dvv[i], gamma, dstate, out=dout)
     d1.record(stream)
     torch.cuda.synchronize()
-    us_step = d0.elapsed_time(d1) * 1e3 / T
+    us_step = d0.elapsed_time(d1) * 1e3 / T if T else float("nan")
     dbytes = decode_bytes(B, H)
     dgbps = dbytes / (us_step * 1e-6) / 1e9
 

@@ -10,23 +10,33 @@
 // Two kernels:
 //  * state walk: one workgroup per (head, 32*MT-row k-tile, 128-column v-tile,
 //    sequence segment) keeps its tile of R in MFMA accumulators (fp32) and
-//    walks the chunks in order. Before each chunk it stores R as bf16 in a
-//    [v][k] layout (k fastest), which is exactly the B-operand layout of the
-//    read-out; then it applies the carry and accumulates K^T (zeta V) with K
-//    and zeta*V staged transposed in LDS. Long sequences with few heads are cut
-//    into chunk-aligned segments: a first launch computes each segment's local
-//    end state from zero, the second starts every segment from the sum of the
-//    earlier segments' end states, each decayed to its start.
-//  * output: one workgroup per (head, 64-row query block) with the full dv row.
-//    It reads out the stored chunk state, then loops over the 64-row key
-//    blocks of its chunk up to the diagonal: S^T = K Q^T on the MFMAs, the
-//    decay gamma^(n-m) (zero above the diagonal) applied to the fp32 scores
-//    in registers, scores rounded to bf16 into LDS, then O += A V. The per-head
-//    GroupNorm and the bf16 store close it. The N x N mask never exists in
-//    memory; with one chunk spanning the sequence this is the parallel form.
+//    walks the chunks in order. Before each chunk it stores R as bf16 ([k][v],
+//    v fastest, like V); then it applies the carry and accumulates
+//    K^T (zeta V) over 64-row key blocks. Long sequences with few heads are
+//    cut into chunk-aligned segments: a first launch computes each segment's
+//    end state (segment 0 from state_in, the others from zero), the second
+//    starts every segment from the earlier segments' end states, each decayed
+//    to its start, and writes the chunk states.
+//  * output: one workgroup per (head, 64-row query block) with the full dv
+//    row. It reads out the stored chunk state in 64-row slices (O = Q R), scales
+//    the rows by gamma^(j+1), then loops over the 64-row key blocks of its chunk
+//    up to the diagonal: S^T = K Q^T, the decay gamma^(n-m) (zero above the
+//    diagonal) applied to the fp32 scores in registers, scores rounded to bf16
+//    through LDS, then O += A V. The per-head GroupNorm and the bf16 store close
+//    it. The N x N mask never exists in memory; with one chunk spanning the
+//    sequence this is the parallel form.
+//
+// Data movement: every tile (K, V, state slice) is copied row-major into LDS
+// with 16-byte accesses; the next tile's global loads are issued into registers
+// before the current tile's matrix work so their latency is hidden. Operands
+// that need a transposed view (V and the state as B operands, K^T as the walk's
+// A operand) are fetched with ds_read_b64_tr_b16, which hands each lane four
+// consecutive rows of one column. Workgroups that share K/V/state tiles get
+// consecutive logical indices and are placed on the same XCD (workgroups are
+// dispatched round-robin over the 8 XCDs), so the re-reads hit one L2.
 //
 // MFMA 32x32x16 operand layouts used throughout (lane l of 64):
-//   A[i][kk]: i = l % 32, kk = 8*(l/32) + 0..7   (16 contiguous bytes)
+//   A[i][kk]: i = l % 32, kk = 8*(l/32) + 0..7
 //   B[kk][j]: j = l % 32, kk = 8*(l/32) + 0..7
 //   D[i][j] : j = l % 32, i = 8*(r/4) + 4*(l/32) + r%4 for accumulator r = 0..15
 #include "kernels.h"
@@ -37,8 +47,11 @@ namespace {
 
 constexpr int kThreads = 256;  // four waves
 constexpr int kRows = 64;      // query / key block height
-constexpr int kPitchT = 72;    // LDS pitch (elements) of transposed tiles: 64 + 8 pad
-constexpr int kPitchQK = 264;  // LDS pitch of row-major Q/K tiles: 256 + 8 pad
+constexpr int kXcds = 8;
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef short shortx8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
@@ -48,88 +61,119 @@ __device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, con
 
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
-// Row-major copy of `nvalid` rows (of 64) x `ncols` columns into LDS [t][c]
-// with pitch P; rows past nvalid are zero.
-template <int P>
-__device__ __forceinline__ void stage_rows(uint16_t* dst, const uint16_t* src, int64_t stride, int nvalid,
-                                           int ncols) {
-  const int octets = ncols >> 3;
-  for (int i = threadIdx.x; i < kRows * octets; i += kThreads) {
-    const int t = i / octets, co = i - t * octets;
-    uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (t < nvalid) val = *reinterpret_cast<const uint4*>(src + t * stride + co * 8);
-    *reinterpret_cast<uint4*>(dst + t * P + co * 8) = val;
-  }
+// Transposed operand from a row-major LDS tile: lane l receives
+// tile[row0 + 8*(l/32) + i][col0 + l%32] for i = 0..7 (an MFMA A or B operand
+// whose contraction index runs down the tile's rows). Two ds_read_b64_tr_b16:
+// within each 16-lane group, lane j points at row (j/4) and columns 4*(j%4)..+3
+// of a 4 x 16 block; lane i then holds column i of that block's four rows.
+__device__ __forceinline__ bf16x8 ld_tr8(const uint16_t* tile, int pitch, int row0, int col0, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const uint16_t* p = tile + (row0 + 8 * (g >> 1) + (j >> 2)) * pitch + col0 + 16 * (g & 1) + 4 * (j & 3);
+  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p));
+  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p + 4 * pitch));
+  const shortx8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
 }
 
-// Transposed copy: dst[c][t] = src[t][c] (times row_scale(t) when kScale),
-// 4 rows x 8 columns per work item: four 16-byte loads, eight 8-byte LDS stores.
-template <bool kScale>
-__device__ __forceinline__ void stage_transposed(uint16_t* dst, const uint16_t* src, int64_t stride, int nvalid,
-                                                 int ncols, float scale_log2g, int scale_last) {
-  const int octets = ncols >> 3;
-  for (int i = threadIdx.x; i < (kRows / 4) * octets; i += kThreads) {
-    const int tq = i / octets, co = i - tq * octets;
-    uint16_t x[4][8];
+// Logical workgroup index such that consecutive logical indices share an XCD.
+__device__ __forceinline__ int xcd_logical_block(int b, int nblocks) {
+  const int full = (nblocks / kXcds) * kXcds;
+  if (b >= full) return b;
+  return (b % kXcds) * (full / kXcds) + b / kXcds;
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufferConfig = 0x00020000;  // raw buffer descriptor word 3 for gfx9-family loads
+constexpr int kOutOfRange = 0x40000000;     // an offset past any tile: the load returns zero
+
+// Buffer descriptor over `nbytes` bytes at `base`; loads past the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), nbytes, kBufferConfig);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_offset) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0);
+}
+
+// Register staging of one 64-row tile of a row-major bf16 matrix with NTHR
+// threads: thread t owns 16-byte pieces t, t+NTHR, ... (row = piece / (cols/8)).
+// Rows at or past `rows_valid` read as zero through the buffer range check.
+template <int MAXP, int NTHR>
+struct TileRegs {
+  u32x4 p[MAXP];
+
+  __device__ __forceinline__ void load(const uint16_t* src, int stride, int rows_valid, int cols) {
+    const int per_row = cols >> 3;
+    const int nbytes = rows_valid > 0 ? ((rows_valid - 1) * stride + cols) * 2 : 0;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src, nbytes);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = 4 * tq + j;
-      uint4 val = make_uint4(0u, 0u, 0u, 0u);
-      if (t < nvalid) val = *reinterpret_cast<const uint4*>(src + t * stride + co * 8);
-      const uint32_t w[4] = {val.x, val.y, val.z, val.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[j][2 * e] = static_cast<uint16_t>(w[e] & 0xffffu);
-        x[j][2 * e + 1] = static_cast<uint16_t>(w[e] >> 16);
-      }
-      if (kScale) {
-        // zeta_t = gamma^(L-1-t) for the chunk-local row t
-        const float z = (t < nvalid) ? exp2f(static_cast<float>(scale_last - t) * scale_log2g) : 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[j][e] = f32_to_bf16(bf16_to_f32(x[j][e]) * z);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint2 w;
-      w.x = static_cast<uint32_t>(x[0][e]) | (static_cast<uint32_t>(x[1][e]) << 16);
-      w.y = static_cast<uint32_t>(x[2][e]) | (static_cast<uint32_t>(x[3][e]) << 16);
-      *reinterpret_cast<uint2*>(dst + (co * 8 + e) * kPitchT + 4 * tq) = w;
+    for (int m = 0; m < MAXP; ++m) {
+      const int i = threadIdx.x + NTHR * m;
+      const int row = i / per_row, c8 = i - row * per_row;
+      const int off = row < kRows ? (row * stride + c8 * 8) * 2 : kOutOfRange;
+      p[m] = buffer_load16(r, off);
     }
   }
-}
+
+  // Store into LDS [row][col] with the given pitch (elements). With kScale,
+  // row t is multiplied by gamma^(last - t) (the in-chunk decay zeta).
+  template <bool kScale>
+  __device__ __forceinline__ void store(uint16_t* dst, int pitch, int cols, float log2g = 0.f, int last = 0) const {
+    const int per_row = cols >> 3;
+#pragma unroll
+    for (int m = 0; m < MAXP; ++m) {
+      const int i = threadIdx.x + NTHR * m;
+      const int row = i / per_row, c8 = i - row * per_row;
+      if (row < kRows) {
+        u32x4 v = p[m];
+        if (kScale) {
+          const float z = exp2f(static_cast<float>(last - row) * log2g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v[e] = pack_bf16x2(bf16_to_f32(static_cast<uint16_t>(v[e] & 0xffffu)) * z,
+                               bf16_to_f32(static_cast<uint16_t>(v[e] >> 16)) * z);
+        }
+        *reinterpret_cast<u32x4*>(dst + row * pitch + c8 * 8) = v;
+      }
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------
 // State walk
 // ---------------------------------------------------------------------------
-constexpr int kWalkVT = 128;  // v columns per workgroup: 32 per wave
+constexpr int kWalkVT = 128;   // v columns per workgroup: 32 per wave
+constexpr int kWalkPitch = 160;  // LDS pitch of the K and V tiles (320 B: rows 64 B apart mod 256)
 
 struct WalkArgs {
   const uint16_t* k;
   const uint16_t* v;
   const float* state_in;
   float* state_out;
-  uint16_t* chunk_states;  // [B*H][nchunks][dv][dk]
+  uint16_t* chunk_states;  // [B*H][nchunks][dk][dv]
   float* seg_states;       // [B*H][nseg][dk][dv]
   int H, N, dk, dv, chunk, nchunks, nseg, chunks_per_seg;
   int nkt, nvt;
-  int mode;  // 0: local end state of segments 0..nseg-2; 1: write chunk states from the true start
+  int mode;  // 0: end state of segments 0..nseg-2; 1: write chunk states from the true start
 };
 
 template <int MT>
 __global__ void __launch_bounds__(kThreads) mfma_state_walk_kernel(WalkArgs a, HeadDecay decay) {
   constexpr int KT = 32 * MT;
-  __shared__ __attribute__((aligned(16))) uint16_t sKt[KT * kPitchT];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[kWalkVT * kPitchT];
+  constexpr int PIECES = (kRows * KT / 8 + kThreads - 1) / kThreads;
+  constexpr int VPIECES = kRows * kWalkVT / 8 / kThreads;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kRows * kWalkPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[kRows * kWalkPitch];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  int idx = blockIdx.x;
+  const int nseg_launch = (a.mode == 0) ? a.nseg - 1 : a.nseg;
+  const int nblocks = gridDim.x;
+  int idx = xcd_logical_block(blockIdx.x, nblocks);
   const int vt = idx % a.nvt;
   idx /= a.nvt;
   const int kt = idx % a.nkt;
   idx /= a.nkt;
-  const int nseg_launch = (a.mode == 0) ? a.nseg - 1 : a.nseg;
   const int seg = idx % nseg_launch;
   const int64_t bh = idx / nseg_launch;
   const int h = static_cast<int>(bh % a.H);
@@ -167,46 +211,65 @@ __global__ void __launch_bounds__(kThreads) mfma_state_walk_kernel(WalkArgs a, H
     }
   }
 
-  const uint16_t* kb = a.k + bh * static_cast<int64_t>(a.N) * a.dk;
-  const uint16_t* vb = a.v + bh * static_cast<int64_t>(a.N) * a.dv;
+  const uint16_t* kb = a.k + bh * static_cast<int64_t>(a.N) * a.dk + k0;
+  const uint16_t* vb = a.v + bh * static_cast<int64_t>(a.N) * a.dv + v0;
 
-  for (int c = c_begin; c < c_end; ++c) {
+  // Tiles are (chunk, 64-row block) pairs in sequence order.
+  TileRegs<PIECES, kThreads> rk;
+  TileRegs<VPIECES, kThreads> rv;
+  int c = c_begin, t0 = 0;
+  if (c < c_end) {
+    const int L = min(a.chunk, a.N - c * a.chunk);
+    rk.load(kb + static_cast<int64_t>(c * a.chunk) * a.dk, a.dk, min(kRows, L), KT);
+    rv.load(vb + static_cast<int64_t>(c * a.chunk) * a.dv, a.dv, min(kRows, L), kWalkVT);
+  }
+  while (c < c_end) {
     const int cs = c * a.chunk;
     const int L = min(a.chunk, a.N - cs);
-    if (a.mode == 1) {
-      // Store R_{c-1} as bf16 in [v][k] layout: 4 consecutive k per 8-byte store.
-      uint16_t* dst = a.chunk_states + ((bh * a.nchunks + c) * a.dv + vcol) * static_cast<int64_t>(a.dk) + k0;
+    if (t0 == 0) {
+      if (a.mode == 1) {
+        // Store R_{c-1} as bf16, [k][v] layout; 32 lanes cover 64 contiguous bytes of a row.
+        uint16_t* dst = a.chunk_states + ((bh * a.nchunks + c) * a.dk + k0) * static_cast<int64_t>(a.dv) + vcol;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          uint2 w;
-          w.x = pack_bf16x2(acc[mt][4 * g + 0], acc[mt][4 * g + 1]);
-          w.y = pack_bf16x2(acc[mt][4 * g + 2], acc[mt][4 * g + 3]);
-          *reinterpret_cast<uint2*>(dst + mt * 32 + 8 * g + 4 * (lane >> 5)) = w;
-        }
+          for (int r = 0; r < 16; ++r)
+            dst[static_cast<int64_t>(mt * 32 + acc_row(r, lane)) * a.dv] = f32_to_bf16(acc[mt][r]);
+      }
+      const float carry = exp2f(static_cast<float>(L) * lg);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] *= carry;
     }
-    const float carry = exp2f(static_cast<float>(L) * lg);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] *= carry;
+    __syncthreads();
+    rk.template store<false>(sK, kWalkPitch, KT);
+    rv.template store<true>(sV, kWalkPitch, kWalkVT, lg, L - 1 - t0);
+    __syncthreads();
 
-    for (int t0 = 0; t0 < L; t0 += kRows) {
-      const int nvalid = min(kRows, L - t0);
-      __syncthreads();
-      stage_transposed<false>(sKt, kb + static_cast<int64_t>(cs + t0) * a.dk + k0, a.dk, nvalid, KT, 0.f, 0);
-      stage_transposed<true>(sVt, vb + static_cast<int64_t>(cs + t0) * a.dv + v0, a.dv, nvalid, kWalkVT, lg,
-                             L - 1 - t0);
-      __syncthreads();
+    // Advance and prefetch the next tile while this one is multiplied.
+    int nc = c, nt0 = t0 + kRows;
+    if (nt0 >= L) {
+      nc = c + 1;
+      nt0 = 0;
+    }
+    if (nc < c_end) {
+      const int ncs = nc * a.chunk;
+      const int nL = min(a.chunk, a.N - ncs);
+      const int nvalid = min(kRows, nL - nt0);
+      rk.load(kb + static_cast<int64_t>(ncs + nt0) * a.dk, a.dk, nvalid, KT);
+      rv.load(vb + static_cast<int64_t>(ncs + nt0) * a.dv, a.dv, nvalid, kWalkVT);
+    }
+
 #pragma unroll
-      for (int s = 0; s < kRows / 16; ++s) {
-        const bf16x8 b = ld8(sVt + (wave * 32 + (lane & 31)) * kPitchT + s * 16 + 8 * (lane >> 5));
+    for (int s = 0; s < kRows / 16; ++s) {
+      const bf16x8 b = ld_tr8(sV, kWalkPitch, s * 16, wave * 32, lane);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const bf16x8 av = ld8(sKt + (mt * 32 + (lane & 31)) * kPitchT + s * 16 + 8 * (lane >> 5));
-          acc[mt] = mfma32(av, b, acc[mt]);
-        }
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 av = ld_tr8(sK, kWalkPitch, s * 16, mt * 32, lane);
+        acc[mt] = mfma32(av, b, acc[mt]);
       }
     }
+    c = nc;
+    t0 = nt0;
   }
 
   // Mode 0 stores the segment's end state. Mode 1 stores the final state: to
@@ -231,186 +294,296 @@ __global__ void __launch_bounds__(kThreads) mfma_state_walk_kernel(WalkArgs a, H
 // ---------------------------------------------------------------------------
 // Output
 // ---------------------------------------------------------------------------
+constexpr int kOutThreads = 512;  // eight waves, two per SIMD
+constexpr int kPitchQK = 264;     // sQ/sK pitch: 528 B, rows an odd number of 16-byte slots apart
+constexpr int kPitchP = 72;       // sP pitch: 144 B
+
 struct OutArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  const uint16_t* chunk_states;  // [B*H][nchunks][dv][dk] or null
+  const uint16_t* chunk_states;  // [B*H][nchunks][dk][dv] or null
   uint16_t* o;
   int state_for_chunk0;
   int H, N, dk, dv, chunk, nchunks, nqb;
 };
 
-template <int NT>
-__global__ void __launch_bounds__(kThreads) mfma_chunk_out_kernel(OutArgs a, HeadDecay decay, GnArgs gn) {
-  constexpr int DV = 128 * NT;   // dv handled by the workgroup
-  constexpr int WV = 32 * NT;    // columns per wave
+__device__ __forceinline__ floatx4 mfma16(const bf16x8& a, const bf16x8& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Waves form a (64/(32*MQ)) x VG grid over the 64 x DV output block: each wave
+// owns 32*MQ query rows and 32*NV value columns (VG * 32 * NV = DV).
+template <int MQ, int NV>
+__global__ void __launch_bounds__(kOutThreads) mfma_chunk_out_kernel(OutArgs a, HeadDecay decay, GnArgs gn) {
+  constexpr int QG = 2 / MQ;            // query-row groups
+  constexpr int VG = 8 / QG;            // value-column groups
+  constexpr int DV = VG * 32 * NV;      // dv handled by the workgroup
+  constexpr int PV = DV + 32;           // sV pitch: rows 64 B apart mod 256
+  constexpr int KP = kRows * 256 / 8 / kOutThreads;  // 16-byte pieces per thread of a K or Q tile (dk <= 256)
+  constexpr int VP = kRows * DV / 8 / kOutThreads;   // ... of a V tile or state slice
   __shared__ __attribute__((aligned(16))) uint16_t sQ[kRows * kPitchQK];
   __shared__ __attribute__((aligned(16))) uint16_t sK[kRows * kPitchQK];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[DV * kPitchT];
-  __shared__ __attribute__((aligned(16))) uint16_t sA[kRows * kPitchT];
-  __shared__ float s_stat[4][kRows];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[kRows * PV];
+  __shared__ __attribute__((aligned(16))) uint16_t sP[kRows * kPitchP];
+  __shared__ float s_stat[VG][kRows];
+  __shared__ float s_mean[kRows];
+  __shared__ float s_rstd[kRows];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lrow = lane & 31;
   const int lk = 8 * (lane >> 5);
-  const int64_t bh = blockIdx.x / a.nqb;
-  const int qb = blockIdx.x % a.nqb;
+  const int qg = wave / VG, vg = wave % VG;
+  const int qrow0 = qg * 32 * MQ;   // first query row (in the block) of this wave
+  const int vcol0 = vg * 32 * NV;   // first value column of this wave
+  const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int64_t bh = blk / a.nqb;
+  const int qb = blk % a.nqb;
   const int h = static_cast<int>(bh % a.H);
   const float lg = decay.log2g[h];
   const int q0 = qb * kRows;
   const int c = q0 / a.chunk;
   const int cs = c * a.chunk;
   const int dk = a.dk;
-  const uint16_t* qbase = a.q + bh * static_cast<int64_t>(a.N) * dk;
+  const int dk64 = (dk + 63) & ~63;  // Q columns padded with zeros to whole 64-row state slices
+  const int qvalid = min(kRows, a.N - q0);
+  const uint16_t* qbase = a.q + (bh * a.N + q0) * static_cast<int64_t>(dk);
   const uint16_t* kbase = a.k + bh * static_cast<int64_t>(a.N) * dk;
   const uint16_t* vbase = a.v + bh * static_cast<int64_t>(a.N) * DV;
+  const bool has_state = a.chunk_states && (c > 0 || a.state_for_chunk0);
+  const uint16_t* rbase = has_state ? a.chunk_states + (bh * a.nchunks + c) * static_cast<int64_t>(dk) * DV : nullptr;
+  const int nslices = has_state ? dk64 / kRows : 0;
+  const int tb_first = cs / kRows;
+  const int ntiles = nslices + (qb - tb_first + 1);
 
-  stage_rows<kPitchQK>(sQ, qbase + static_cast<int64_t>(q0) * dk, dk, min(kRows, a.N - q0), dk);
-  __syncthreads();
-
-  floatx16 acc[2][NT];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = floatx16{};
-
-  // Cross-chunk read-out: O = diag(gamma^(j+1)) Q R_{c-1}, R read as bf16 B operands.
-  if (a.chunk_states && (c > 0 || a.state_for_chunk0)) {
-    const uint16_t* Rt = a.chunk_states + (bh * a.nchunks + c) * static_cast<int64_t>(DV) * dk;
-    for (int s = 0; s < dk / 16; ++s) {
-      const bf16x8 a0 = ld8(sQ + lrow * kPitchQK + s * 16 + lk);
-      const bf16x8 a1 = ld8(sQ + (32 + lrow) * kPitchQK + s * 16 + lk);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int vcol = wave * WV + nt * 32 + lrow;
-        const bf16x8 b = ld8(Rt + static_cast<int64_t>(vcol) * dk + s * 16 + lk);
-        acc[0][nt] = mfma32(a0, b, acc[0][nt]);
-        acc[1][nt] = mfma32(a1, b, acc[1][nt]);
-      }
+  // Q tile into LDS (A operand of the read-out), zero beyond N and dk.
+  {
+    TileRegs<KP, kOutThreads> rq;
+    rq.load(qbase, dk, qvalid, dk);
+    rq.template store<false>(sQ, kPitchQK, dk);
+    // Columns dk..dk64 of sQ meet zero-filled state rows; clear them so they hold no stale values.
+    for (int i = threadIdx.x; i < kRows * (dk64 - dk); i += kOutThreads) {
+      const int row = i / (dk64 - dk);
+      sQ[row * kPitchQK + dk + (i - row * (dk64 - dk))] = 0;
     }
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = q0 + mt * 32 + acc_row(r, lane) - cs;  // chunk-local row
-        const float xi = exp2f(static_cast<float>(j + 1) * lg);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[mt][nt][r] *= xi;
-      }
   }
+  // S^T = K Q^T on 16x16x32 MFMAs: this wave's 16 query columns (qt16) and
+  // 32 key rows (two 16-row tiles); both operands are read from LDS.
+  const int qt16 = wave & 3, tg = wave >> 2;
+  const int l16 = lane & 15, lk16 = 8 * (lane >> 4);
 
-  // Intra-chunk causal part over key blocks cs/64 .. qb.
-  const int tt = wave >> 1, qt = wave & 1;  // this wave's 32x32 tile of S^T
-  for (int tb = cs / kRows; tb <= qb; ++tb) {
-    const int t0 = tb * kRows;
-    const int nvalid = min(kRows, a.N - t0);
-    __syncthreads();
-    stage_rows<kPitchQK>(sK, kbase + static_cast<int64_t>(t0) * dk, dk, nvalid, dk);
-    stage_transposed<false>(sVt, vbase + static_cast<int64_t>(t0) * DV, DV, nvalid, DV, 0.f, 0);
-    __syncthreads();
-
-    floatx16 sacc = floatx16{};
-    for (int s = 0; s < dk / 16; ++s) {
-      const bf16x8 ak = ld8(sK + (tt * 32 + lrow) * kPitchQK + s * 16 + lk);
-      const bf16x8 bq = ld8(sQ + (qt * 32 + lrow) * kPitchQK + s * 16 + lk);
-      sacc = mfma32(ak, bq, sacc);
-    }
-    // sacc[r] = S^T[t][q], t = tt*32 + acc_row(r), q = qt*32 + lrow. Apply gamma^(q-t), zero if t > q.
-    const int qa = q0 + qt * 32 + lrow;
+  floatx16 acc[MQ][NV];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+  for (int mt = 0; mt < MQ; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NV; ++nt) acc[mt][nt] = floatx16{};
+
+  TileRegs<KP, kOutThreads> rk;
+  TileRegs<VP, kOutThreads> rv;
+  auto prefetch = [&](int it) {
+    if (it < nslices) {
+      rv.load(rbase + static_cast<int64_t>(it * kRows) * DV, DV, min(kRows, dk - it * kRows), DV);
+    } else {
+      const int t0 = (tb_first + it - nslices) * kRows;
+      const int nvalid = min(kRows, a.N - t0);
+      rk.load(kbase + static_cast<int64_t>(t0) * dk, dk, nvalid, dk);
+      rv.load(vbase + static_cast<int64_t>(t0) * DV, DV, nvalid, DV);
+    }
+  };
+  prefetch(0);
+
+  for (int it = 0; it < ntiles; ++it) {
+    const bool is_slice = it < nslices;
+    __syncthreads();  // previous tile's readers are done with sK / sV / sP
+    if (!is_slice) rk.template store<false>(sK, kPitchQK, dk);
+    rv.template store<false>(sV, PV, DV);
+    __syncthreads();
+    if (it + 1 < ntiles) prefetch(it + 1);
+
+    if (is_slice) {
+      // Cross-chunk read-out: O += Q[:, 64 state rows] R[64 rows, :].
+      const int kcol = it * kRows;
+#pragma unroll 2
+      for (int s = 0; s < kRows / 16; ++s) {
+        bf16x8 av[MQ];
+#pragma unroll
+        for (int mt = 0; mt < MQ; ++mt) av[mt] = ld8(sQ + (qrow0 + mt * 32 + lrow) * kPitchQK + kcol + s * 16 + lk);
+#pragma unroll
+        for (int nt = 0; nt < NV; ++nt) {
+          const bf16x8 b = ld_tr8(sV, PV, s * 16, vcol0 + nt * 32, lane);
+#pragma unroll
+          for (int mt = 0; mt < MQ; ++mt) acc[mt][nt] = mfma32(av[mt], b, acc[mt][nt]);
+        }
+      }
+      if (it == nslices - 1) {
+        // Scale row j (chunk-local) by xi_j = gamma^(j+1).
+#pragma unroll
+        for (int mt = 0; mt < MQ; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = q0 + qrow0 + mt * 32 + acc_row(r, lane) - cs;
+            const float xi = exp2f(static_cast<float>(j + 1) * lg);
+#pragma unroll
+            for (int nt = 0; nt < NV; ++nt) acc[mt][nt][r] *= xi;
+          }
+      }
+      continue;
+    }
+
+    // Intra-chunk key block: S^T[t][q] for t in this wave's 32 rows, q in its 16 columns.
+    const int t0 = (tb_first + it - nslices) * kRows;
+    floatx4 sacc[2] = {floatx4{}, floatx4{}};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      if (s * 32 < dk) {
+        const bf16x8 bq = ld8(sQ + (qt16 * 16 + l16) * kPitchQK + s * 32 + lk16);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const bf16x8 ak = ld8(sK + (tg * 32 + u * 16 + l16) * kPitchQK + s * 32 + lk16);
+          sacc[u] = mfma16(ak, bq, sacc[u]);
+        }
+      }
+    }
+    // sacc[u][r] = S^T[t][q], t = tg*32 + 16u + 4*(lane/16) + r, q = qt16*16 + l16.
+    // Apply gamma^(q-t), zero above the diagonal, and store A[q][t] as bf16.
+    const int qa = q0 + qt16 * 16 + l16;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tl = tg * 32 + u * 16 + 4 * (lane >> 4);
       float x[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = t0 + tt * 32 + 8 * g + 4 * (lane >> 5) + e;
-        const int d = qa - t;
-        x[e] = (d >= 0) ? sacc[4 * g + e] * exp2f(static_cast<float>(d) * lg) : 0.f;
+      for (int r = 0; r < 4; ++r) {
+        const int d = qa - (t0 + tl + r);
+        x[r] = (d >= 0) ? sacc[u][r] * exp2f(static_cast<float>(d) * lg) : 0.f;
       }
       uint2 w;
       w.x = pack_bf16x2(x[0], x[1]);
       w.y = pack_bf16x2(x[2], x[3]);
-      *reinterpret_cast<uint2*>(sA + (qt * 32 + lrow) * kPitchT + tt * 32 + 8 * g + 4 * (lane >> 5)) = w;
+      *reinterpret_cast<uint2*>(sP + (qt16 * 16 + l16) * kPitchP + tl) = w;
     }
     __syncthreads();
-#pragma unroll
+#pragma unroll 2
     for (int s = 0; s < kRows / 16; ++s) {
-      const bf16x8 a0 = ld8(sA + lrow * kPitchT + s * 16 + lk);
-      const bf16x8 a1 = ld8(sA + (32 + lrow) * kPitchT + s * 16 + lk);
+      bf16x8 ap[MQ];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const bf16x8 b = ld8(sVt + (wave * WV + nt * 32 + lrow) * kPitchT + s * 16 + lk);
-        acc[0][nt] = mfma32(a0, b, acc[0][nt]);
-        acc[1][nt] = mfma32(a1, b, acc[1][nt]);
+      for (int mt = 0; mt < MQ; ++mt) ap[mt] = ld8(sP + (qrow0 + mt * 32 + lrow) * kPitchP + s * 16 + lk);
+#pragma unroll
+      for (int nt = 0; nt < NV; ++nt) {
+        const bf16x8 b = ld_tr8(sV, PV, s * 16, vcol0 + nt * 32, lane);
+#pragma unroll
+        for (int mt = 0; mt < MQ; ++mt) acc[mt][nt] = mfma32(ap[mt], b, acc[mt][nt]);
       }
     }
   }
 
-  // Epilogue: optional per-head GroupNorm over the DV columns of each row, then bf16 store.
+  // Epilogue: optional per-head GroupNorm over the DV columns of each row, then
+  // the bf16 store.
   if (gn.enabled) {
-    float mean[2][16], rstd[2][16];
+    // Row statistics: each lane reduces its 16 row slots over the 32 lanes that
+    // share them with a reduce-scatter butterfly (16 exchanges instead of 80);
+    // lane l then holds the wave's partial for slot (l%32)/2. One thread per row
+    // combines the value-column groups through LDS.
+    const int slot = (lane & 31) >> 1;
+    auto reduce_rows = [&](const float (&x)[16]) {
+      float w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool hi = lane & 16;
+        const float mine = hi ? x[i + 8] : x[i], other = hi ? x[i] : x[i + 8];
+        w[i] = mine + __shfl_xor(other, 16, 64);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool hi = lane & 8;
+        const float mine = hi ? w[i + 4] : w[i], other = hi ? w[i] : w[i + 4];
+        w[i] = mine + __shfl_xor(other, 8, 64);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const bool hi = lane & 4;
+        const float mine = hi ? w[i + 2] : w[i], other = hi ? w[i] : w[i + 2];
+        w[i] = mine + __shfl_xor(other, 4, 64);
+      }
+      {
+        const bool hi = lane & 2;
+        const float mine = hi ? w[1] : w[0], other = hi ? w[0] : w[1];
+        w[0] = mine + __shfl_xor(other, 2, 64);
+      }
+      return w[0] + __shfl_xor(w[0], 1, 64);
+    };
+    float x[16];
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
-      float part[2][16];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MQ; ++mt) {
+        float mean_r[16];
+        if (pass == 1) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mean_r[r] = s_mean[qrow0 + mt * 32 + acc_row(r, lane)];
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float s = 0.f;
+          float t = 0.f;
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const float d = pass == 0 ? acc[mt][nt][r] : acc[mt][nt][r] - mean[mt][r];
-            s += pass == 0 ? d : d * d;
+          for (int nt = 0; nt < NV; ++nt) {
+            const float d = pass == 0 ? acc[mt][nt][r] : acc[mt][nt][r] - mean_r[r];
+            t += pass == 0 ? d : d * d;
           }
-#pragma unroll
-          for (int off = 1; off < 32; off <<= 1) s += __shfl_xor(s, off, 64);
-          part[mt][r] = s;
+          x[r] = t;
         }
-      __syncthreads();
-      if (lrow == 0) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s_stat[wave][mt * 32 + acc_row(r, lane)] = part[mt][r];
+        const float tot = reduce_rows(x);
+        if ((lane & 1) == 0) s_stat[vg][qrow0 + mt * 32 + acc_row(slot, lane)] = tot;
       }
       __syncthreads();
+      if (threadIdx.x < kRows) {
+        float t = 0.f;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+        for (int g = 0; g < VG; ++g) t += s_stat[g][threadIdx.x];
+        t /= DV;
+        if (pass == 0) s_mean[threadIdx.x] = t;
+        else s_rstd[threadIdx.x] = 1.0f / sqrtf(t + gn.eps);
+      }
+      __syncthreads();
+    }
+    float w[NV], bb[NV];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = mt * 32 + acc_row(r, lane);
-          const float tot = (s_stat[0][row] + s_stat[1][row] + s_stat[2][row] + s_stat[3][row]) / DV;
-          if (pass == 0) mean[mt][r] = tot;
-          else rstd[mt][r] = 1.0f / sqrtf(tot + gn.eps);
-        }
+    for (int nt = 0; nt < NV; ++nt) {
+      const int vcol = vcol0 + nt * 32 + lrow;
+      w[nt] = gn.weight ? gn.weight[h * DV + vcol] : 1.f;
+      bb[nt] = gn.bias ? gn.bias[h * DV + vcol] : 0.f;
     }
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int vcol = wave * WV + nt * 32 + lrow;
-      const float w = gn.weight ? gn.weight[h * DV + vcol] : 1.f;
-      const float bb = gn.bias ? gn.bias[h * DV + vcol] : 0.f;
+    for (int mt = 0; mt < MQ; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int r = 0; r < 16; ++r) {
+        const int row = qrow0 + mt * 32 + acc_row(r, lane);
+        const float mean = s_mean[row], rstd = s_rstd[row];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[mt][nt][r] = (acc[mt][nt][r] - mean[mt][r]) * rstd[mt][r] * w + bb;
-    }
+        for (int nt = 0; nt < NV; ++nt) acc[mt][nt][r] = (acc[mt][nt][r] - mean) * rstd * w[nt] + bb[nt];
+      }
   }
 
-  uint16_t* obase = a.o + (bh * a.N + q0) * static_cast<int64_t>(DV);
+  // Store: stage the bf16 tile in LDS (the V buffer is free), then write each
+  // row with 16-byte stores.
+  __syncthreads();
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MQ; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = mt * 32 + acc_row(r, lane);
-      if (q0 + row < a.N) {
+      const int row = qrow0 + mt * 32 + acc_row(r, lane);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int vcol = wave * WV + nt * 32 + lrow;
-          obase[static_cast<int64_t>(row) * DV + vcol] = f32_to_bf16(acc[mt][nt][r]);
-        }
-      }
+      for (int nt = 0; nt < NV; ++nt) sV[row * PV + vcol0 + nt * 32 + lrow] = f32_to_bf16(acc[mt][nt][r]);
     }
+  __syncthreads();
+  uint16_t* obase = a.o + (bh * a.N + q0) * static_cast<int64_t>(DV);
+  constexpr int per_row = DV / 8;
+  for (int i = threadIdx.x; i < kRows * per_row; i += kOutThreads) {
+    const int row = i / per_row, c8 = i - row * per_row;
+    if (row < qvalid)
+      *reinterpret_cast<u32x4*>(obase + static_cast<int64_t>(row) * DV + c8 * 8) =
+          *reinterpret_cast<const u32x4*>(sV + row * PV + c8 * 8);
+  }
 }
 
 }  // namespace
@@ -418,6 +591,10 @@ __global__ void __launch_bounds__(kThreads) mfma_chunk_out_kernel(OutArgs a, Hea
 bool mfma_supports(int dk, int dv) {
   return dk % 32 == 0 && dk >= 32 && dk <= 256 && (dv == 128 || dv == 256 || dv == 512);
 }
+
+int walk_k_tiles(int dk) { return (dk % 64 == 0) ? 2 : 1; }
+
+int walk_tiles_per_head(int dk, int dv) { return (dk / (32 * walk_k_tiles(dk))) * (dv / kWalkVT); }
 
 hipError_t launch_mfma_state_walk(const uint16_t* k, const uint16_t* v, const float* state_in, float* state_out,
                                   uint16_t* chunk_states, float* seg_states, int chunks_per_seg, const Dims& d,
@@ -452,20 +629,15 @@ hipError_t launch_mfma_state_walk(const uint16_t* k, const uint16_t* v, const fl
     if (e != hipSuccess) return e;
   }
   if (a.nseg > 1 && state_out) {
-    // Final state sits in segment slot nseg-1 of every head: copy it out.
-    const int64_t dkdv = static_cast<int64_t>(d.dk) * d.dv;
-    for (int64_t bh = 0; bh < static_cast<int64_t>(d.B) * d.H; ++bh) {
-      const hipError_t e = hipMemcpyAsync(state_out + bh * dkdv, seg_states + (bh * a.nseg + a.nseg - 1) * dkdv,
-                                          dkdv * sizeof(float), hipMemcpyDeviceToDevice, stream);
-      if (e != hipSuccess) return e;
-    }
+    // The final state of every head sits in its segment slot nseg-1: one strided copy.
+    const size_t row = static_cast<size_t>(d.dk) * d.dv * sizeof(float);
+    const hipError_t e = hipMemcpy2DAsync(state_out, row, seg_states + static_cast<size_t>(a.nseg - 1) * d.dk * d.dv,
+                                          row * a.nseg, row, static_cast<size_t>(d.B) * d.H,
+                                          hipMemcpyDeviceToDevice, stream);
+    if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
-
-int walk_k_tiles(int dk) { return (dk % 128 == 0) ? 4 : ((dk % 64 == 0) ? 2 : 1); }
-
-int walk_tiles_per_head(int dk, int dv) { return (dk / (32 * walk_k_tiles(dk))) * (dv / kWalkVT); }
 
 hipError_t launch_mfma_chunk_out(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const uint16_t* chunk_states, bool state_for_chunk0, uint16_t* o, const Dims& d,
@@ -486,9 +658,9 @@ hipError_t launch_mfma_chunk_out(const uint16_t* q, const uint16_t* k, const uin
   a.nqb = (d.N + kRows - 1) / kRows;
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(d.B) * d.H * a.nqb));
   switch (d.dv) {
-    case 128: mfma_chunk_out_kernel<1><<<grid, kThreads, 0, stream>>>(a, decay, gn); break;
-    case 256: mfma_chunk_out_kernel<2><<<grid, kThreads, 0, stream>>>(a, decay, gn); break;
-    default: mfma_chunk_out_kernel<4><<<grid, kThreads, 0, stream>>>(a, decay, gn); break;
+    case 128: mfma_chunk_out_kernel<1, 1><<<grid, kOutThreads, 0, stream>>>(a, decay, gn); break;
+    case 256: mfma_chunk_out_kernel<1, 2><<<grid, kOutThreads, 0, stream>>>(a, decay, gn); break;
+    default: mfma_chunk_out_kernel<1, 4><<<grid, kOutThreads, 0, stream>>>(a, decay, gn); break;
   }
   return hipGetLastError();
 }
