@@ -1,0 +1,142 @@
+"""GPU parity at the full workload sizes (sampled where the oracle would be slow).
+
+Shapes are those the operator is benchmarked on: a 1.3B-shaped forward (B=2,
+H=8, N=2048, dk=256, dv=512, chunk 256), the 6.7B-shaped chunkwise prefill with
+GroupNorm (B=8, H=16, N=8192, chunk 512; the launch bench.py times), the decode
+step on an fp32 [8,16,256,512] state, and a 64k-token sequence (B=1, H=16,
+N=65536) at chunk sizes 64..512. Where the full oracle is too slow, outputs are
+compared on sampled rows (chunk boundaries, first/last rows, random rows)
+computed one by one from the definition, and the final state is compared on
+sampled heads against its closed form. Inputs are the seeded synthetic
+generators'; every oracle input is generated here, never read back from the
+GPU. Tolerance: 2e-2 * max|o| per (b, h) slice for bf16 inputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import retnet_retention_msr_amd as ret
+from oracle import retention_oracle as orc
+from retnet_retention_msr_amd import synthetic
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = 2e-2
+
+
+def _check(got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), what
+    for b in range(ref.shape[0]):
+        for h in range(ref.shape[1]):
+            scale = float(np.max(np.abs(ref[b, h])))
+            err = float(np.max(np.abs(got[b, h] - ref[b, h])))
+            assert err <= TOL * max(scale, 1e-30), f"{what} b={b} h={h}: err {err:.3e} > {TOL} * {scale:.3e}"
+
+
+def _rows(N, chunk, seed, n_random=6):
+    rng = np.random.default_rng(seed)
+    fixed = {0, 1, N - 1, N // 2, chunk - 1, chunk, min(N - 1, chunk + 1), min(N - 1, 2 * chunk - 1)}
+    fixed |= set(int(x) for x in rng.integers(0, N, n_random))
+    return sorted(r for r in fixed if 0 <= r < N)
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _f64(t):
+    return t.detach().to("cpu").double().numpy()
+
+
+def test_1p3b_shape_parallel_and_chunkwise_full():
+    _announce("B=2 H=8 N=2048 dk=256 dv=512 chunk 256: parallel and chunkwise, full oracle")
+    B, H, N, dk, dv, C = 2, 8, 2048, 256, 512, 256
+    q, k, v = synthetic.make_qkv(B, H, N, dk, dv, dtype=torch.bfloat16, seed=1002)
+    g = synthetic.head_gammas(H)
+    ref, Sref = orc.chunkwise(q, k, v, g, C)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o_par = ret.parallel(qd, kd, vd, g)
+    o_chk, S = ret.chunkwise(qd, kd, vd, g, C, state_out=True)
+    torch.cuda.synchronize()
+    _check(_f64(o_par), ref, "parallel")
+    _check(_f64(o_chk), ref, "chunkwise")
+    _check(_f64(S), Sref, "state")
+    # The GPU forms agree with each other within the same bound.
+    _check(_f64(o_chk), _f64(o_par), "chunkwise vs parallel")
+
+
+@pytest.fixture(scope="module")
+def prefill_6p7b():
+    B, H, N, dk, dv = 8, 16, 8192, 256, 512
+    q, k, v = synthetic.make_qkv(B, H, N, dk, dv, dtype=torch.bfloat16, seed=1003)
+    return q, k, v
+
+
+def test_6p7b_prefill_with_groupnorm_sampled(prefill_6p7b):
+    _announce("B=8 H=16 N=8192 chunk 512 + GroupNorm: sampled rows and states")
+    q, k, v = prefill_6p7b
+    B, H, N, dk = q.shape
+    dv, C = v.shape[-1], 512
+    g = synthetic.head_gammas(H)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out = torch.empty(B, H, N, dv, dtype=torch.bfloat16, device=DEV)
+    state = torch.empty(B, H, dk, dv, dtype=torch.float32, device=DEV)
+    ws = torch.empty(ret.chunkwise_workspace_bytes(B, H, N, dk, dv, C), dtype=torch.uint8, device=DEV)
+    ret.chunkwise(qd, kd, vd, g, C, state_out=state, gn=ret.GroupNorm(1e-5), out=out, workspace=ws)
+    torch.cuda.synchronize()
+    rows = _rows(N, C, seed=3)
+    for b in (0, B - 1):
+        qb, kb, vb = (_f64(t[b : b + 1]) for t in (q, k, v))
+        raw = orc.parallel_rows(qb, kb, vb, g, rows)
+        ref = orc.group_norm_rows(raw, eps=1e-5)
+        got = _f64(out[b : b + 1, :, rows])
+        _check(got, ref, f"o rows b={b}")
+        _check(_f64(state[b : b + 1]), orc.state_after(kb, vb, g), f"state b={b}")
+
+
+def test_decode_step_full_shape():
+    _announce("decode step on fp32 [8,16,256,512], 4 steps")
+    B, H, dk, dv = 8, 16, 256, 512
+    g = synthetic.head_gammas(H)
+    S = synthetic.make_state(B, H, dk, dv, seed=1004, std=4.0)
+    q, k, v = synthetic.make_qkv(B, H, 4, dk, dv, dtype=torch.bfloat16, seed=1005, qk_var=1.0)
+    Sd = S.to(DEV)
+    Sref = S.double().numpy()
+    for n in range(4):
+        o_ref, Sref = orc.recurrent_step(q[:, :, n], k[:, :, n], v[:, :, n], g, Sref)
+        o = ret.recurrent_step(q[:, :, n].contiguous().to(DEV), k[:, :, n].contiguous().to(DEV),
+                               v[:, :, n].contiguous().to(DEV), g, Sd)
+        torch.cuda.synchronize()
+        _check(_f64(o)[:, :, None, :], o_ref[:, :, None, :], f"o step {n}")
+    got = Sd.double().cpu().numpy()
+    err = np.abs(got - Sref).max() / np.abs(Sref).max()
+    assert err <= 1e-6, err
+
+
+@pytest.fixture(scope="module")
+def long_sequence():
+    B, H, N, dk, dv = 1, 16, 65536, 256, 512
+    q, k, v = synthetic.make_qkv(B, H, N, dk, dv, dtype=torch.bfloat16, seed=1005)
+    return q, k, v, (q.to(DEV), k.to(DEV), v.to(DEV)), (_f64(q), _f64(k), _f64(v))
+
+
+@pytest.mark.parametrize("C", [64, 128, 256, 512])
+def test_long_sequence_chunk_sweep_sampled(long_sequence, C):
+    _announce(f"B=1 H=16 N=65536 chunk {C}: sampled rows, states of heads 0 and 15")
+    q, k, v, (qd, kd, vd), (q64, k64, v64) = long_sequence
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    g = synthetic.head_gammas(H)
+    o, S = ret.chunkwise(qd, kd, vd, g, C, state_out=True)
+    torch.cuda.synchronize()
+    rows = _rows(N, C, seed=C, n_random=4)
+    ref = orc.parallel_rows(q64, k64, v64, g, rows)
+    _check(_f64(o[:, :, rows]), ref, "o rows")
+    for h in (0, H - 1):
+        Sh = orc.state_after(k64[:, h : h + 1], v64[:, h : h + 1], g[h : h + 1])
+        _check(_f64(S[:, h : h + 1]), Sh, f"state h={h}")
