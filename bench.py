@@ -48,6 +48,11 @@ def algorithmic_flops(B, H, N, chunk, dk=DK, dv=DV):
     return float(per) * B * H * N
 
 
+def output_flops(B, H, N, chunk, dk=DK, dv=DV):
+    """The output stage's share: intra-chunk causal half plus the cross-chunk read-out."""
+    return float((chunk + 1) * (dk + dv) + 2 * dk * dv) * B * H * N
+
+
 def decode_bytes(B, H, dk=DK, dv=DV):
     """fp32 state read + written, bf16 q, k, v in and o out."""
     return 2 * B * H * dk * dv * 4 + B * H * (2 * dk + 2 * dv) * 2
@@ -137,26 +142,37 @@ def main():
     ws = torch.empty(ret.chunkwise_workspace_bytes(B, H, N, DK, DV, CHUNK), dtype=torch.uint8, device=dev)
     gn = ret.GroupNorm(1e-5)
 
-    def step():
-        ret.chunkwise(qd, kd, vd, gamma, CHUNK, state_out=state, gn=gn, out=out, workspace=ws)
+    def step(events=None):
+        # One chunkwise forward as its two stages (the same work retention_chunkwise
+        # launches); optional events bracket each stage on the current stream.
+        if events is not None:
+            events[0].record(stream)
+        ret.chunk_states(kd, vd, gamma, CHUNK, ws, state_out=state)
+        if events is not None:
+            events[1].record(stream)
+        ret.chunk_output(qd, kd, vd, gamma, CHUNK, ws, gn=gn, out=out)
+        if events is not None:
+            events[2].record(stream)
 
+    stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} prefill steps", file=sys.stderr, flush=True)
     t_wall = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
+    for i in range(args.steps):
+        step(ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = ev[0][0].elapsed_time(ev[-1][2]) / args.steps
+    walk_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    out_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
     tokens_per_s = B * N / (ms * 1e-3)
     flops = algorithmic_flops(B, H, N, CHUNK)
     achieved = flops / (ms * 1e-3)
+    flops_out = output_flops(B, H, N, CHUNK)
+    flops_walk = flops - flops_out
 
     # Decode: single-token steps from the prefill's state.
     if args.skip_decode:
@@ -207,13 +223,28 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
+            "achieved": flops_out / (out_ms * 1e-3) / 1e12,
+            "peak": PEAK_BF16 / 1e12,
+            "unit": "TFLOP/s",
+            "frac": flops_out / (out_ms * 1e-3) / PEAK_BF16,
+            "traffic": None,
+            "kernel": "mfma_chunk_out_kernel (retention_chunk_output: intra-chunk products, read-out, GroupNorm)",
+            "algorithmic_flop_per_launch": flops_out,
+            "launch_ms": out_ms,
+        },
+        "step_roofline": {
+            "bound": "mfma",
             "achieved": achieved / 1e12,
             "peak": PEAK_BF16 / 1e12,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16,
-            "traffic": None,
-            "kernel": "retention_chunkwise call (state walk + query-block output kernels)",
             "algorithmic_flop_per_step": flops,
+        },
+        "state_walk": {
+            "kernel": "mfma_state_walk_kernel (retention_chunk_states: chunk-state carry)",
+            "launch_ms": walk_ms,
+            "algorithmic_flop_per_launch": flops_walk,
+            "achieved_tflops": flops_walk / (walk_ms * 1e-3) / 1e12,
         },
         "decode": {
             "steps": T,

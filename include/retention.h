@@ -122,6 +122,35 @@ int retention_chunkwise(const void* q, const void* k, const void* v,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The two stages of retention_chunkwise, for callers that want the chunk
+ * states themselves or time the stages separately. Same page and formulas as
+ * retention_chunkwise; R_{i-1} is the state carried into chunk i.
+ *
+ * retention_chunk_states: computes R_{i-1} for every chunk i (R_{-1} =
+ * state_in, or zeros when state_in is NULL) into the workspace, and the state
+ * after the last chunk into state_out (NULL: not written; it may alias
+ * state_in). Reads k and v only.
+ *
+ * retention_chunk_output: computes O from q, k, v and the chunk states that
+ * retention_chunk_states left in the workspace for the same B, H, N, dk, dv,
+ * chunk and dtype; has_state_in must be non-zero exactly when that call had a
+ * state_in. Applies the optional GroupNorm.
+ *
+ * The workspace (at least retention_chunkwise_workspace_bytes(...) bytes) is
+ * opaque; its contents are only meaningful between these two calls.
+ */
+int retention_chunk_states(const void* k, const void* v, const float* gamma_host,
+                           int B, int H, int N, int dk, int dv, int chunk, int dtype,
+                           const float* state_in, float* state_out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+int retention_chunk_output(const void* q, const void* k, const void* v,
+                           const float* gamma_host, void* o,
+                           int B, int H, int N, int dk, int dv, int chunk, int dtype,
+                           int has_state_in, const retention_gn_t* gn,
+                           const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One recurrent decode step ("RetNet - Retentive Network ...", Key
  * Equations, recurrent form; jisaku.com glossary, recurrent mode):
  *   state <- gamma_h * state + k^T v   (in place, fp32 [B, H, dk, dv])

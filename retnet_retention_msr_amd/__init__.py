@@ -23,6 +23,8 @@ __all__ = [
     "GroupNorm",
     "parallel",
     "chunkwise",
+    "chunk_states",
+    "chunk_output",
     "recurrent_step",
     "chunkwise_workspace_bytes",
     "RetentionError",
@@ -154,6 +156,46 @@ def chunkwise(q, k, v, gamma: GammaLike, chunk: int, state_in=None, state_out: U
     if rc != 0:
         raise RetentionError("retention_chunkwise", rc)
     return out, state_out
+
+
+def chunk_states(k, v, gamma: GammaLike, chunk: int, workspace, state_in=None, state_out=None):
+    """First stage of the chunkwise form: the state carried into every chunk, kept in ``workspace``.
+
+    ``workspace`` is a device uint8 tensor of at least chunkwise_workspace_bytes(...)
+    bytes; ``state_out`` (optional fp32 [B,H,dk,dv]) receives the final state.
+    """
+    lib = _lib.load()
+    B, H, N, dk, dv, dt = _check_qkv(k, k, v)
+    for name, t in (("state_in", state_in), ("state_out", state_out)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (B, H, dk, dv)):
+            raise ValueError(f"{name} must be contiguous float32 [B,H,dk,dv]")
+    g = _gamma_array(gamma, H)
+    rc = lib.retention_chunk_states(
+        k.data_ptr(), v.data_ptr(), g, B, H, N, dk, dv, int(chunk), dt,
+        state_in.data_ptr() if state_in is not None else None,
+        state_out.data_ptr() if state_out is not None else None,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(k))
+    if rc != 0:
+        raise RetentionError("retention_chunk_states", rc)
+    return state_out
+
+
+def chunk_output(q, k, v, gamma: GammaLike, chunk: int, workspace, has_state_in: bool = False,
+                 gn: Optional[GroupNorm] = None, out=None):
+    """Second stage of the chunkwise form: O from q, k, v and the chunk states in ``workspace``."""
+    lib = _lib.load()
+    B, H, N, dk, dv, dt = _check_qkv(q, k, v)
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    g = _gamma_array(gamma, H)
+    gn_p, _keep = _gn_struct(gn, H, dv, q.device)
+    rc = lib.retention_chunk_output(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), g, out.data_ptr(), B, H, N, dk, dv, int(chunk), dt,
+        1 if has_state_in else 0, gn_p, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream(q))
+    if rc != 0:
+        raise RetentionError("retention_chunk_output", rc)
+    return out
 
 
 def recurrent_step(q, k, v, gamma: GammaLike, state, gn: Optional[GroupNorm] = None, out=None):

@@ -22,6 +22,8 @@ EXPORTED = (
     "retention_parallel",
     "retention_chunkwise_workspace_bytes",
     "retention_chunkwise",
+    "retention_chunk_states",
+    "retention_chunk_output",
     "retention_recurrent_step",
 )
 
@@ -58,6 +60,11 @@ def load():
     lib.retention_chunkwise.argtypes = [vp, vp, vp, f_p, vp, i, i, i, i, i, i, i, vp, vp, gn_p, vp,
                                         ctypes.c_size_t, vp]
     lib.retention_chunkwise.restype = i
+    lib.retention_chunk_states.argtypes = [vp, vp, f_p, i, i, i, i, i, i, i, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.retention_chunk_states.restype = i
+    lib.retention_chunk_output.argtypes = [vp, vp, vp, f_p, vp, i, i, i, i, i, i, i, i, gn_p, vp,
+                                           ctypes.c_size_t, vp]
+    lib.retention_chunk_output.restype = i
     lib.retention_recurrent_step.argtypes = [vp, vp, vp, f_p, vp, vp, i, i, i, i, i, gn_p, vp]
     lib.retention_recurrent_step.restype = i
     _lib = lib

@@ -99,6 +99,47 @@ ChunkPlan plan_chunkwise(int B, int H, int N, int dk, int dv, int chunk, int dty
   return p;
 }
 
+// Shared validation of the chunkwise entry points (no HIP calls).
+int check_chunkwise(const float* gamma_host, int B, int H, int N, int dk, int dv, int chunk, int dtype,
+                    const retention_gn_t* gn, const void* workspace, size_t workspace_bytes, GnArgs* g,
+                    ChunkPlan* plan, HeadDecay* decay) {
+  if (chunk <= 0) return RET_ERR_INVALID_ARG;
+  int st = check_sizes(B, H, N, dk, dv, dtype);
+  if (st != RET_OK) return st;
+  st = check_gamma(gamma_host, H, nullptr);
+  if (st != RET_OK) return st;
+  st = check_gn(gn, g);
+  if (st != RET_OK) return st;
+  *plan = plan_chunkwise(B, H, N, dk, dv, chunk, dtype);
+  if (plan->total > 0 && (!workspace || workspace_bytes < plan->total)) return RET_ERR_INVALID_ARG;
+  check_gamma(gamma_host, H, decay);
+  return RET_OK;
+}
+
+hipError_t launch_states(const ChunkPlan& p, const void* k, const void* v, const float* state_in, float* state_out,
+                         char* ws, const Dims& d, int chunk, int dtype, const HeadDecay& decay, hipStream_t s) {
+  if (p.mfma) {
+    uint16_t* states = reinterpret_cast<uint16_t*>(ws);
+    float* segs = p.seg_bytes ? reinterpret_cast<float*>(ws + p.states_bytes) : nullptr;
+    return ret::launch_mfma_state_walk(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), state_in,
+                                       state_out, states, segs, p.chunks_per_seg, d, chunk, decay, s);
+  }
+  return ret::launch_generic_state_walk(dtype, k, v, state_in, state_out, reinterpret_cast<float*>(ws), d, chunk,
+                                        decay, s);
+}
+
+hipError_t launch_output(const ChunkPlan& p, const void* q, const void* k, const void* v, void* o, const char* ws,
+                         bool state0, const Dims& d, int chunk, int dtype, const HeadDecay& decay, const GnArgs& g,
+                         hipStream_t s) {
+  if (p.mfma) {
+    return ret::launch_mfma_chunk_out(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                      static_cast<const uint16_t*>(v), reinterpret_cast<const uint16_t*>(ws), state0,
+                                      static_cast<uint16_t*>(o), d, chunk, decay, g, s);
+  }
+  return ret::launch_generic_chunk_out(dtype, q, k, v, reinterpret_cast<const float*>(ws), state0, o, d, chunk,
+                                       decay, g, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -147,40 +188,47 @@ int retention_chunkwise(const void* q, const void* k, const void* v, const float
                         int N, int dk, int dv, int chunk, int dtype, const float* state_in, float* state_out,
                         const retention_gn_t* gn, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o) return RET_ERR_INVALID_ARG;
-  if (chunk <= 0) return RET_ERR_INVALID_ARG;
-  int st = check_sizes(B, H, N, dk, dv, dtype);
-  if (st != RET_OK) return st;
-  st = check_gamma(gamma_host, H, nullptr);
-  if (st != RET_OK) return st;
   GnArgs g;
-  st = check_gn(gn, &g);
-  if (st != RET_OK) return st;
-  const ChunkPlan p = plan_chunkwise(B, H, N, dk, dv, chunk, dtype);
-  if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return RET_ERR_INVALID_ARG;
-
+  ChunkPlan p;
   HeadDecay decay;
-  check_gamma(gamma_host, H, &decay);
+  const int st = check_chunkwise(gamma_host, B, H, N, dk, dv, chunk, dtype, gn, workspace, workspace_bytes, &g, &p,
+                                 &decay);
+  if (st != RET_OK) return st;
   const Dims d{B, H, N, dk, dv};
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  const bool state0 = state_in != nullptr;
-  if (p.mfma) {
-    uint16_t* states = reinterpret_cast<uint16_t*>(ws);
-    float* segs = p.seg_bytes ? reinterpret_cast<float*>(ws + p.states_bytes) : nullptr;
-    hipError_t e = ret::launch_mfma_state_walk(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                                               state_in, state_out, states, segs, p.chunks_per_seg, d, chunk, decay,
-                                               s);
-    if (e != hipSuccess) return RET_ERR_HIP;
-    e = ret::launch_mfma_chunk_out(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                                   static_cast<const uint16_t*>(v), states, state0, static_cast<uint16_t*>(o), d,
-                                   chunk, decay, g, s);
-    return status_of(e);
-  }
-  float* states = reinterpret_cast<float*>(ws);
-  hipError_t e = ret::launch_generic_state_walk(dtype, k, v, state_in, state_out, states, d, chunk, decay, s);
-  if (e != hipSuccess) return RET_ERR_HIP;
-  e = ret::launch_generic_chunk_out(dtype, q, k, v, states, state0, o, d, chunk, decay, g, s);
-  return status_of(e);
+  if (launch_states(p, k, v, state_in, state_out, ws, d, chunk, dtype, decay, s) != hipSuccess) return RET_ERR_HIP;
+  return status_of(launch_output(p, q, k, v, o, ws, state_in != nullptr, d, chunk, dtype, decay, g, s));
+}
+
+int retention_chunk_states(const void* k, const void* v, const float* gamma_host, int B, int H, int N, int dk,
+                           int dv, int chunk, int dtype, const float* state_in, float* state_out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!k || !v) return RET_ERR_INVALID_ARG;
+  GnArgs g;
+  ChunkPlan p;
+  HeadDecay decay;
+  const int st = check_chunkwise(gamma_host, B, H, N, dk, dv, chunk, dtype, nullptr, workspace, workspace_bytes, &g,
+                                 &p, &decay);
+  if (st != RET_OK) return st;
+  const Dims d{B, H, N, dk, dv};
+  return status_of(launch_states(p, k, v, state_in, state_out, static_cast<char*>(workspace), d, chunk, dtype, decay,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+int retention_chunk_output(const void* q, const void* k, const void* v, const float* gamma_host, void* o, int B,
+                           int H, int N, int dk, int dv, int chunk, int dtype, int has_state_in,
+                           const retention_gn_t* gn, const void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o) return RET_ERR_INVALID_ARG;
+  GnArgs g;
+  ChunkPlan p;
+  HeadDecay decay;
+  const int st = check_chunkwise(gamma_host, B, H, N, dk, dv, chunk, dtype, gn, workspace, workspace_bytes, &g, &p,
+                                 &decay);
+  if (st != RET_OK) return st;
+  const Dims d{B, H, N, dk, dv};
+  return status_of(launch_output(p, q, k, v, o, static_cast<const char*>(workspace), has_state_in != 0, d, chunk,
+                                 dtype, decay, g, static_cast<hipStream_t>(stream)));
 }
 
 int retention_recurrent_step(const void* q, const void* k, const void* v, const float* gamma_host, float* state,

@@ -96,48 +96,54 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byt
 }
 
 // Register staging of one 64-row tile of a row-major bf16 matrix with NTHR
-// threads: thread t owns 16-byte pieces t, t+NTHR, ... (row = piece / (cols/8)).
-// Rows at or past `rows_valid` read as zero through the buffer range check.
-template <int MAXP, int NTHR>
+// threads: thread t owns 16-byte pieces t, t+NTHR, ... of a tile COLS wide
+// (row = piece / (COLS/8)); COLS is a compile-time width so the piece layout
+// costs shifts only. Rows at or past `rows_valid`, and columns at or past
+// `cols_valid`, read as zero (buffer range check / out-of-range offset).
+template <int MAXP, int NTHR, int COLS>
 struct TileRegs {
+  static constexpr int kPerRow = COLS / 8;
   u32x4 p[MAXP];
 
-  __device__ __forceinline__ void load(const uint16_t* src, int stride, int rows_valid, int cols) {
-    const int per_row = cols >> 3;
-    const int nbytes = rows_valid > 0 ? ((rows_valid - 1) * stride + cols) * 2 : 0;
+  __device__ __forceinline__ static int row_of(int m) { return (static_cast<int>(threadIdx.x) + NTHR * m) / kPerRow; }
+  __device__ __forceinline__ static int col_of(int m) { return ((static_cast<int>(threadIdx.x) + NTHR * m) % kPerRow) * 8; }
+
+  __device__ __forceinline__ void load(const uint16_t* src, int stride, int rows_valid, int cols_valid) {
+    const int nbytes = rows_valid > 0 ? ((rows_valid - 1) * stride + cols_valid) * 2 : 0;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(src, nbytes);
 #pragma unroll
     for (int m = 0; m < MAXP; ++m) {
-      const int i = threadIdx.x + NTHR * m;
-      const int row = i / per_row, c8 = i - row * per_row;
-      const int off = row < kRows ? (row * stride + c8 * 8) * 2 : kOutOfRange;
+      const int row = row_of(m), col = col_of(m);
+      const int off = (row < kRows && col < cols_valid) ? (row * stride + col) * 2 : kOutOfRange;
       p[m] = buffer_load16(r, off);
     }
   }
 
-  // Store into LDS [row][col] with the given pitch (elements). With kScale,
-  // row t is multiplied by gamma^(last - t) (the in-chunk decay zeta).
-  template <bool kScale>
-  __device__ __forceinline__ void store(uint16_t* dst, int pitch, int cols, float log2g = 0.f, int last = 0) const {
-    const int per_row = cols >> 3;
+  // Store into LDS [row][col] with the given pitch (elements).
+  __device__ __forceinline__ void store(uint16_t* dst, int pitch) const {
+#pragma unroll
+    for (int m = 0; m < MAXP; ++m)
+      if (row_of(m) < kRows) *reinterpret_cast<u32x4*>(dst + row_of(m) * pitch + col_of(m)) = p[m];
+  }
+
+  // Store with row r multiplied by scale[m] (one factor per owned piece's row).
+  __device__ __forceinline__ void store_scaled(uint16_t* dst, int pitch, const float (&scale)[MAXP]) const {
 #pragma unroll
     for (int m = 0; m < MAXP; ++m) {
-      const int i = threadIdx.x + NTHR * m;
-      const int row = i / per_row, c8 = i - row * per_row;
-      if (row < kRows) {
+      if (row_of(m) < kRows) {
         u32x4 v = p[m];
-        if (kScale) {
-          const float z = exp2f(static_cast<float>(last - row) * log2g);
+        const float z = scale[m];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            v[e] = pack_bf16x2(bf16_to_f32(static_cast<uint16_t>(v[e] & 0xffffu)) * z,
-                               bf16_to_f32(static_cast<uint16_t>(v[e] >> 16)) * z);
-        }
-        *reinterpret_cast<u32x4*>(dst + row * pitch + c8 * 8) = v;
+        for (int e = 0; e < 4; ++e)
+          v[e] = pack_bf16x2(__uint_as_float(v[e] << 16) * z, __uint_as_float(v[e] & 0xffff0000u) * z);
+        *reinterpret_cast<u32x4*>(dst + row_of(m) * pitch + col_of(m)) = v;
       }
     }
   }
 };
+
+// gamma^e through the hardware exp2 (results below the normal range flush to 0).
+__device__ __forceinline__ float gpow(float log2g, float e) { return __builtin_amdgcn_exp2f(e * log2g); }
 
 // ---------------------------------------------------------------------------
 // State walk
@@ -201,7 +207,7 @@ __global__ void __launch_bounds__(kThreads) mfma_state_walk_kernel(WalkArgs a, H
     const int p = c_begin * a.chunk;
     for (int s = 0; s < seg; ++s) {
       const int end_s = (s + 1) * a.chunks_per_seg * a.chunk;
-      const float f = exp2f(static_cast<float>(p - end_s) * lg);
+      const float f = gpow(lg, static_cast<float>(p - end_s));
       const float* U = a.seg_states + (bh * a.nseg + s) * dkdv;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -215,8 +221,13 @@ __global__ void __launch_bounds__(kThreads) mfma_state_walk_kernel(WalkArgs a, H
   const uint16_t* vb = a.v + bh * static_cast<int64_t>(a.N) * a.dv + v0;
 
   // Tiles are (chunk, 64-row block) pairs in sequence order.
-  TileRegs<PIECES, kThreads> rk;
-  TileRegs<VPIECES, kThreads> rv;
+  TileRegs<PIECES, kThreads, KT> rk;
+  TileRegs<VPIECES, kThreads, kWalkVT> rv;
+  // zeta_t = gamma^(L-1-t) = gamma^(L-1-t0) * gamma^(-r) for row r of a tile at t0;
+  // the gamma^(-r) factors of this thread's rows are fixed (r <= 63, so <= 7.4).
+  float zrow[PIECES];
+#pragma unroll
+  for (int m = 0; m < PIECES; ++m) zrow[m] = gpow(lg, -static_cast<float>(rk.row_of(m)));
   int c = c_begin, t0 = 0;
   if (c < c_end) {
     const int L = min(a.chunk, a.N - c * a.chunk);
@@ -236,13 +247,19 @@ __global__ void __launch_bounds__(kThreads) mfma_state_walk_kernel(WalkArgs a, H
           for (int r = 0; r < 16; ++r)
             dst[static_cast<int64_t>(mt * 32 + acc_row(r, lane)) * a.dv] = f32_to_bf16(acc[mt][r]);
       }
-      const float carry = exp2f(static_cast<float>(L) * lg);
+      const float carry = gpow(lg, static_cast<float>(L));
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] *= carry;
     }
     __syncthreads();
-    rk.template store<false>(sK, kWalkPitch, KT);
-    rv.template store<true>(sV, kWalkPitch, kWalkVT, lg, L - 1 - t0);
+    {
+      const float z0 = gpow(lg, static_cast<float>(L - 1 - t0));
+      float z[PIECES];
+#pragma unroll
+      for (int m = 0; m < PIECES; ++m) z[m] = z0 * zrow[m];
+      rk.store_scaled(sK, kWalkPitch, z);
+    }
+    rv.store(sV, kWalkPitch);
     __syncthreads();
 
     // Advance and prefetch the next tile while this one is multiplied.
@@ -294,7 +311,6 @@ __global__ void __launch_bounds__(kThreads) mfma_state_walk_kernel(WalkArgs a, H
 // ---------------------------------------------------------------------------
 // Output
 // ---------------------------------------------------------------------------
-constexpr int kOutThreads = 512;  // eight waves, two per SIMD
 constexpr int kPitchQK = 264;     // sQ/sK pitch: 528 B, rows an odd number of 16-byte slots apart
 constexpr int kPitchP = 72;       // sP pitch: 144 B
 
@@ -312,12 +328,17 @@ __device__ __forceinline__ floatx4 mfma16(const bf16x8& a, const bf16x8& b, cons
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Waves form a (64/(32*MQ)) x VG grid over the 64 x DV output block: each wave
-// owns 32*MQ query rows and 32*NV value columns (VG * 32 * NV = DV).
-template <int MQ, int NV>
-__global__ void __launch_bounds__(kOutThreads) mfma_chunk_out_kernel(OutArgs a, HeadDecay decay, GnArgs gn) {
+// WAVES waves form a (64/(32*MQ)) x VG grid over the 64 x DV output block:
+// each wave owns 32*MQ query rows and 32*NV value columns (VG * 32 * NV = DV).
+// With four waves (one per SIMD) each wave owns all 64 rows of a 32*NV column
+// slab, accumulates in AGPRs and computes one 32x32 tile of S^T, so every LDS
+// operand is read by fewer waves.
+// With eight waves S^T is split into 16x16 tiles with both operands in LDS.
+template <int WAVES, int MQ, int NV>
+__global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, HeadDecay decay, GnArgs gn) {
+  constexpr int kOutThreads = 64 * WAVES;
   constexpr int QG = 2 / MQ;            // query-row groups
-  constexpr int VG = 8 / QG;            // value-column groups
+  constexpr int VG = WAVES / QG;        // value-column groups
   constexpr int DV = VG * 32 * NV;      // dv handled by the workgroup
   constexpr int PV = DV + 32;           // sV pitch: rows 64 B apart mod 256
   constexpr int KP = kRows * 256 / 8 / kOutThreads;  // 16-byte pieces per thread of a K or Q tile (dk <= 256)
@@ -346,7 +367,7 @@ __global__ void __launch_bounds__(kOutThreads) mfma_chunk_out_kernel(OutArgs a, 
   const int c = q0 / a.chunk;
   const int cs = c * a.chunk;
   const int dk = a.dk;
-  const int dk64 = (dk + 63) & ~63;  // Q columns padded with zeros to whole 64-row state slices
+  const int dk64 = (dk + 63) & ~63;  // state rows read in whole 64-row slices (zero past dk)
   const int qvalid = min(kRows, a.N - q0);
   const uint16_t* qbase = a.q + (bh * a.N + q0) * static_cast<int64_t>(dk);
   const uint16_t* kbase = a.k + bh * static_cast<int64_t>(a.N) * dk;
@@ -359,19 +380,25 @@ __global__ void __launch_bounds__(kOutThreads) mfma_chunk_out_kernel(OutArgs a, 
 
   // Q tile into LDS (A operand of the read-out), zero beyond N and dk.
   {
-    TileRegs<KP, kOutThreads> rq;
+    // Columns dk..255 are written as zeros (they meet zero-filled state rows).
+    TileRegs<KP, kOutThreads, 256> rq;
     rq.load(qbase, dk, qvalid, dk);
-    rq.template store<false>(sQ, kPitchQK, dk);
-    // Columns dk..dk64 of sQ meet zero-filled state rows; clear them so they hold no stale values.
-    for (int i = threadIdx.x; i < kRows * (dk64 - dk); i += kOutThreads) {
-      const int row = i / (dk64 - dk);
-      sQ[row * kPitchQK + dk + (i - row * (dk64 - dk))] = 0;
-    }
+    rq.store(sQ, kPitchQK);
   }
-  // S^T = K Q^T on 16x16x32 MFMAs: this wave's 16 query columns (qt16) and
-  // 32 key rows (two 16-row tiles); both operands are read from LDS.
+  // S^T = K Q^T. Eight waves: 16x16x32 MFMAs, this wave's 16 query columns
+  // (qt16) and 32 key rows (two 16-row tiles), both operands from LDS. Four
+  // waves: one 32x32 tile (key rows tt*32.., query columns qt*32..) per wave,
+  // operands from LDS.
   const int qt16 = wave & 3, tg = wave >> 2;
   const int l16 = lane & 15, lk16 = 8 * (lane >> 4);
+  const int tt = wave >> 1, qt = wave & 1;
+  constexpr int NBT = WAVES == 8 ? 8 : 16;
+  float bt[NBT];  // gamma^(-(t - t0)) for this lane's key rows of a block (t - t0 <= 63)
+#pragma unroll
+  for (int i = 0; i < NBT; ++i) {
+    const int tl = WAVES == 8 ? tg * 32 + (i >> 2) * 16 + 4 * (lane >> 4) + (i & 3) : tt * 32 + acc_row(i, lane);
+    bt[i] = gpow(lg, -static_cast<float>(tl));
+  }
 
   floatx16 acc[MQ][NV];
 #pragma unroll
@@ -379,8 +406,8 @@ __global__ void __launch_bounds__(kOutThreads) mfma_chunk_out_kernel(OutArgs a, 
 #pragma unroll
     for (int nt = 0; nt < NV; ++nt) acc[mt][nt] = floatx16{};
 
-  TileRegs<KP, kOutThreads> rk;
-  TileRegs<VP, kOutThreads> rv;
+  TileRegs<KP, kOutThreads, 256> rk;
+  TileRegs<VP, kOutThreads, DV> rv;
   auto prefetch = [&](int it) {
     if (it < nslices) {
       rv.load(rbase + static_cast<int64_t>(it * kRows) * DV, DV, min(kRows, dk - it * kRows), DV);
@@ -396,8 +423,8 @@ __global__ void __launch_bounds__(kOutThreads) mfma_chunk_out_kernel(OutArgs a, 
   for (int it = 0; it < ntiles; ++it) {
     const bool is_slice = it < nslices;
     __syncthreads();  // previous tile's readers are done with sK / sV / sP
-    if (!is_slice) rk.template store<false>(sK, kPitchQK, dk);
-    rv.template store<false>(sV, PV, DV);
+    if (!is_slice) rk.store(sK, kPitchQK);
+    rv.store(sV, PV);
     __syncthreads();
     if (it + 1 < ntiles) prefetch(it + 1);
 
@@ -423,7 +450,7 @@ __global__ void __launch_bounds__(kOutThreads) mfma_chunk_out_kernel(OutArgs a, 
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int j = q0 + qrow0 + mt * 32 + acc_row(r, lane) - cs;
-            const float xi = exp2f(static_cast<float>(j + 1) * lg);
+            const float xi = gpow(lg, static_cast<float>(j + 1));
 #pragma unroll
             for (int nt = 0; nt < NV; ++nt) acc[mt][nt][r] *= xi;
           }
@@ -431,36 +458,67 @@ __global__ void __launch_bounds__(kOutThreads) mfma_chunk_out_kernel(OutArgs a, 
       continue;
     }
 
-    // Intra-chunk key block: S^T[t][q] for t in this wave's 32 rows, q in its 16 columns.
+    // Intra-chunk key block starting at t0: S^T[t][q], decay gamma^(q-t) (zero above
+    // the diagonal) applied in registers, A[q][t] stored to LDS as bf16.
+    // gamma^(q-t) = gamma^(q-t0) * gamma^(-(t-t0)); the second factor is fixed per lane.
     const int t0 = (tb_first + it - nslices) * kRows;
-    floatx4 sacc[2] = {floatx4{}, floatx4{}};
+    if constexpr (WAVES == 8) {
+      floatx4 sacc[2] = {floatx4{}, floatx4{}};
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      if (s * 32 < dk) {
-        const bf16x8 bq = ld8(sQ + (qt16 * 16 + l16) * kPitchQK + s * 32 + lk16);
+      for (int s = 0; s < 8; ++s) {
+        if (s * 32 < dk) {
+          const bf16x8 bq = ld8(sQ + (qt16 * 16 + l16) * kPitchQK + s * 32 + lk16);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const bf16x8 ak = ld8(sK + (tg * 32 + u * 16 + l16) * kPitchQK + s * 32 + lk16);
-          sacc[u] = mfma16(ak, bq, sacc[u]);
+          for (int u = 0; u < 2; ++u) {
+            const bf16x8 ak = ld8(sK + (tg * 32 + u * 16 + l16) * kPitchQK + s * 32 + lk16);
+            sacc[u] = mfma16(ak, bq, sacc[u]);
+          }
         }
       }
-    }
-    // sacc[u][r] = S^T[t][q], t = tg*32 + 16u + 4*(lane/16) + r, q = qt16*16 + l16.
-    // Apply gamma^(q-t), zero above the diagonal, and store A[q][t] as bf16.
-    const int qa = q0 + qt16 * 16 + l16;
+      // sacc[u][r] = S^T[t][q], t = tg*32 + 16u + 4*(lane/16) + r, q = qt16*16 + l16.
+      const int qa = q0 + qt16 * 16 + l16;
+      const float aq = gpow(lg, static_cast<float>(qa - t0));
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int tl = tg * 32 + u * 16 + 4 * (lane >> 4);
-      float x[4];
+      for (int u = 0; u < 2; ++u) {
+        const int tl = tg * 32 + u * 16 + 4 * (lane >> 4);
+        float x[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int d = qa - (t0 + tl + r);
-        x[r] = (d >= 0) ? sacc[u][r] * exp2f(static_cast<float>(d) * lg) : 0.f;
+        for (int r = 0; r < 4; ++r) {
+          const int d = qa - (t0 + tl + r);
+          x[r] = (d >= 0) ? sacc[u][r] * (aq * bt[u * 4 + r]) : 0.f;
+        }
+        uint2 w;
+        w.x = pack_bf16x2(x[0], x[1]);
+        w.y = pack_bf16x2(x[2], x[3]);
+        *reinterpret_cast<uint2*>(sP + (qt16 * 16 + l16) * kPitchP + tl) = w;
       }
-      uint2 w;
-      w.x = pack_bf16x2(x[0], x[1]);
-      w.y = pack_bf16x2(x[2], x[3]);
-      *reinterpret_cast<uint2*>(sP + (qt16 * 16 + l16) * kPitchP + tl) = w;
+    } else {
+      floatx16 sacc = floatx16{};
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        if (s * 16 < dk) {
+          const bf16x8 ak = ld8(sK + (tt * 32 + lrow) * kPitchQK + s * 16 + lk);
+          const bf16x8 bq = ld8(sQ + (qt * 32 + lrow) * kPitchQK + s * 16 + lk);
+          sacc = mfma32(ak, bq, sacc);
+        }
+      }
+      // sacc[r] = S^T[t][q], t = tt*32 + acc_row(r), q = qt*32 + lrow.
+      const int qa = q0 + qt * 32 + lrow;
+      const float aq = gpow(lg, static_cast<float>(qa - t0));
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const int d = qa - (t0 + tt * 32 + acc_row(r, lane));
+          x[e] = (d >= 0) ? sacc[r] * (aq * bt[r]) : 0.f;
+        }
+        uint2 w;
+        w.x = pack_bf16x2(x[0], x[1]);
+        w.y = pack_bf16x2(x[2], x[3]);
+        *reinterpret_cast<uint2*>(sP + (qt * 32 + lrow) * kPitchP + tt * 32 + 8 * g + 4 * (lane >> 5)) = w;
+      }
     }
     __syncthreads();
 #pragma unroll 2
@@ -622,8 +680,7 @@ hipError_t launch_mfma_state_walk(const uint16_t* k, const uint16_t* v, const fl
     a.mode = mode;
     const int64_t nblocks = per_seg * (mode == 0 ? a.nseg - 1 : a.nseg);
     const dim3 grid(static_cast<unsigned>(nblocks));
-    if (MT == 4) mfma_state_walk_kernel<4><<<grid, kThreads, 0, stream>>>(a, decay);
-    else if (MT == 2) mfma_state_walk_kernel<2><<<grid, kThreads, 0, stream>>>(a, decay);
+    if (MT == 2) mfma_state_walk_kernel<2><<<grid, kThreads, 0, stream>>>(a, decay);
     else mfma_state_walk_kernel<1><<<grid, kThreads, 0, stream>>>(a, decay);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -658,9 +715,9 @@ hipError_t launch_mfma_chunk_out(const uint16_t* q, const uint16_t* k, const uin
   a.nqb = (d.N + kRows - 1) / kRows;
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(d.B) * d.H * a.nqb));
   switch (d.dv) {
-    case 128: mfma_chunk_out_kernel<1, 1><<<grid, kOutThreads, 0, stream>>>(a, decay, gn); break;
-    case 256: mfma_chunk_out_kernel<1, 2><<<grid, kOutThreads, 0, stream>>>(a, decay, gn); break;
-    default: mfma_chunk_out_kernel<1, 4><<<grid, kOutThreads, 0, stream>>>(a, decay, gn); break;
+    case 128: mfma_chunk_out_kernel<8, 1, 1><<<grid, 512, 0, stream>>>(a, decay, gn); break;
+    case 256: mfma_chunk_out_kernel<8, 1, 2><<<grid, 512, 0, stream>>>(a, decay, gn); break;
+    default: mfma_chunk_out_kernel<8, 1, 4><<<grid, 512, 0, stream>>>(a, decay, gn); break;
   }
   return hipGetLastError();
 }

@@ -135,3 +135,22 @@ def test_workspace_bytes(lib):
     # Invalid sizes give 0.
     assert ws(0, 16, 8192, 256, 512, 512, 1) == 0
     assert ws(1, 16, 8192, 256, 512, 0, 1) == 0
+
+
+def test_chunk_stage_entry_points_validate(lib):
+    g = _gamma([0.9, 0.8])
+    need = lib.retention_chunkwise_workspace_bytes(1, 2, 256, 64, 128, 64, 1)
+    # states: null k, bad chunk, short workspace, bad gamma
+    assert lib.retention_chunk_states(None, FAKE, g, 1, 2, 256, 64, 128, 64, 1, None, None, FAKE, need, None) == -1
+    assert lib.retention_chunk_states(FAKE, FAKE, g, 1, 2, 256, 64, 128, 0, 1, None, None, FAKE, need, None) == -1
+    assert lib.retention_chunk_states(FAKE, FAKE, g, 1, 2, 256, 64, 128, 64, 1, None, None, FAKE, need - 1,
+                                      None) == -1
+    assert lib.retention_chunk_states(FAKE, FAKE, _gamma([0.9, 1.0]), 1, 2, 256, 64, 128, 64, 1, None, None, FAKE,
+                                      need, None) == -1
+    # output: null o, unknown dtype, missing workspace
+    assert lib.retention_chunk_output(FAKE, FAKE, FAKE, g, None, 1, 2, 256, 64, 128, 64, 1, 0, None, FAKE, need,
+                                      None) == -1
+    assert lib.retention_chunk_output(FAKE, FAKE, FAKE, g, FAKE, 1, 2, 256, 64, 128, 64, 3, 0, None, FAKE, need,
+                                      None) == -1
+    assert lib.retention_chunk_output(FAKE, FAKE, FAKE, g, FAKE, 1, 2, 256, 64, 128, 64, 1, 0, None, None, 0,
+                                      None) == -1

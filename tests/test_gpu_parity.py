@@ -269,3 +269,19 @@ def test_invalid_gamma_raises():
     qd, kd, vd = _dev(q, k, v)
     with pytest.raises(ret.RetentionError):
         ret.parallel(qd, kd, vd, [0.5, 1.0])
+
+
+@pytest.mark.parametrize("dtype,dk,dv,C", [(torch.bfloat16, 64, 128, 64), (torch.float32, 24, 40, 16)])
+def test_stage_entry_points_equal_chunkwise(dtype, dk, dv, C):
+    """retention_chunk_states + retention_chunk_output reproduce retention_chunkwise bit for bit."""
+    _announce(f"stage entry points {dtype} dk={dk} dv={dv} C={C}")
+    B, H, N = 2, 3, 200
+    q, k, v, g, S0 = _inputs(B, H, N, dk, dv, dtype, seed=71, with_state=True)
+    qd, kd, vd, S0d = _dev(q, k, v, S0)
+    gn = ret.GroupNorm(1e-5)
+    o_ref, S_ref = ret.chunkwise(qd, kd, vd, g, C, state_in=S0d, state_out=True, gn=gn)
+    ws = torch.empty(ret.chunkwise_workspace_bytes(B, H, N, dk, dv, C, dtype), dtype=torch.uint8, device=DEV)
+    S = torch.empty_like(S_ref)
+    ret.chunk_states(kd, vd, g, C, ws, state_in=S0d, state_out=S)
+    o = ret.chunk_output(qd, kd, vd, g, C, ws, has_state_in=True, gn=gn)
+    assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
