@@ -27,6 +27,8 @@ HIP_FLAGS = [
     "-Wall",
     # Keep the compiler from forming packed-fp32 VALU ops.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: avoids copying state tiles between VGPRs and AGPRs.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

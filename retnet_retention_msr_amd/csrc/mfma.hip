@@ -168,7 +168,8 @@ __global__ void __launch_bounds__(kThreads) mfma_state_walk_kernel(WalkArgs a, H
   constexpr int KT = 32 * MT;
   constexpr int PIECES = (kRows * KT / 8 + kThreads - 1) / kThreads;
   constexpr int VPIECES = kRows * kWalkVT / 8 / kThreads;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kRows * kWalkPitch];
+  constexpr int kPitchWK = KT <= 128 ? kWalkPitch : KT + 32;  // K tile pitch: rows 64 B apart mod 256
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kRows * kPitchWK];
   __shared__ __attribute__((aligned(16))) uint16_t sV[kRows * kWalkPitch];
 
   const int lane = threadIdx.x & 63;
@@ -224,10 +225,16 @@ __global__ void __launch_bounds__(kThreads) mfma_state_walk_kernel(WalkArgs a, H
   TileRegs<PIECES, kThreads, KT> rk;
   TileRegs<VPIECES, kThreads, kWalkVT> rv;
   // zeta_t = gamma^(L-1-t) = gamma^(L-1-t0) * gamma^(-r) for row r of a tile at t0;
-  // the gamma^(-r) factors of this thread's rows are fixed (r <= 63, so <= 7.4).
-  float zrow[PIECES];
+  // it scales whichever of the K and V tiles is smaller. The gamma^(-r) factors
+  // of this thread's rows are fixed (r <= 63, so <= 7.4).
+  constexpr bool kScaleK = KT < kWalkVT;
+  constexpr int ZP = kScaleK ? PIECES : VPIECES;
+  float zrow[ZP];
 #pragma unroll
-  for (int m = 0; m < PIECES; ++m) zrow[m] = gpow(lg, -static_cast<float>(rk.row_of(m)));
+  for (int m = 0; m < ZP; ++m) {
+    const int row = kScaleK ? TileRegs<PIECES, kThreads, KT>::row_of(m) : TileRegs<VPIECES, kThreads, kWalkVT>::row_of(m);
+    zrow[m] = gpow(lg, -static_cast<float>(row));
+  }
   int c = c_begin, t0 = 0;
   if (c < c_end) {
     const int L = min(a.chunk, a.N - c * a.chunk);
@@ -254,12 +261,17 @@ __global__ void __launch_bounds__(kThreads) mfma_state_walk_kernel(WalkArgs a, H
     __syncthreads();
     {
       const float z0 = gpow(lg, static_cast<float>(L - 1 - t0));
-      float z[PIECES];
+      float z[ZP];
 #pragma unroll
-      for (int m = 0; m < PIECES; ++m) z[m] = z0 * zrow[m];
-      rk.store_scaled(sK, kWalkPitch, z);
+      for (int m = 0; m < ZP; ++m) z[m] = z0 * zrow[m];
+      if constexpr (kScaleK) {
+        rk.store_scaled(sK, kPitchWK, z);
+        rv.store(sV, kWalkPitch);
+      } else {
+        rk.store(sK, kPitchWK);
+        rv.store_scaled(sV, kWalkPitch, z);
+      }
     }
-    rv.store(sV, kWalkPitch);
     __syncthreads();
 
     // Advance and prefetch the next tile while this one is multiplied.
@@ -281,7 +293,7 @@ __global__ void __launch_bounds__(kThreads) mfma_state_walk_kernel(WalkArgs a, H
       const bf16x8 b = ld_tr8(sV, kWalkPitch, s * 16, wave * 32, lane);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8 av = ld_tr8(sK, kWalkPitch, s * 16, mt * 32, lane);
+        const bf16x8 av = ld_tr8(sK, kPitchWK, s * 16, mt * 32, lane);
         acc[mt] = mfma32(av, b, acc[mt]);
       }
     }
@@ -680,7 +692,8 @@ hipError_t launch_mfma_state_walk(const uint16_t* k, const uint16_t* v, const fl
     a.mode = mode;
     const int64_t nblocks = per_seg * (mode == 0 ? a.nseg - 1 : a.nseg);
     const dim3 grid(static_cast<unsigned>(nblocks));
-    if (MT == 2) mfma_state_walk_kernel<2><<<grid, kThreads, 0, stream>>>(a, decay);
+    if (false) {}
+    else if (MT == 2) mfma_state_walk_kernel<2><<<grid, kThreads, 0, stream>>>(a, decay);
     else mfma_state_walk_kernel<1><<<grid, kThreads, 0, stream>>>(a, decay);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
