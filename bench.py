@@ -58,6 +58,43 @@ def decode_bytes(B, H, dk=DK, dv=DV):
     return 2 * B * H * dk * dv * 4 + B * H * (2 * dk + 2 * dv) * 2
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_6p7b_prefill_and_decode.md")
+CSRC = os.path.join(ROOT, "retnet_retention_msr_amd", "csrc")
+
+
+def _source_hash(names):
+    import hashlib
+
+    m = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            m.update(f.read())
+    return m.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary.
+
+    A figure is used only while the kernel source it was measured on is
+    unchanged (hash of the kernel file and common.h); otherwise it is None.
+    """
+    current = {
+        "chunk_out": _source_hash(["mfma.hip", "common.h"]),
+        "state_walk": _source_hash(["mfma.hip", "common.h"]),
+        "decode_step": _source_hash(["decode.hip", "common.h"]),
+    }
+    out = {k: None for k in current}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                parts = line.split()
+                if len(parts) == 4 and parts[0] == "traffic" and parts[1] in current and parts[2] == current[parts[1]]:
+                    out[parts[1]] = float(parts[3])
+    except OSError:
+        pass
+    return out
+
+
 def _cpu_threads():
     try:
         import threadpoolctl
@@ -203,6 +240,7 @@ def main():
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(q, k, v, gamma, args.cpu_batch_rows)
 
+    traffic = measured_traffic()
     line = {
         "metric": "chunkwise MSR tokens/s @B8 H16 N8k; decode-step µs; % of MFMA/HBM roofline",
         "value": tokens_per_s,
@@ -227,7 +265,7 @@ def main():
             "peak": PEAK_BF16 / 1e12,
             "unit": "TFLOP/s",
             "frac": flops_out / (out_ms * 1e-3) / PEAK_BF16,
-            "traffic": None,
+            "traffic": traffic["chunk_out"],
             "kernel": "mfma_chunk_out_kernel (retention_chunk_output: intra-chunk products, read-out, GroupNorm)",
             "algorithmic_flop_per_launch": flops_out,
             "launch_ms": out_ms,
@@ -245,6 +283,7 @@ def main():
             "launch_ms": walk_ms,
             "algorithmic_flop_per_launch": flops_walk,
             "achieved_tflops": flops_walk / (walk_ms * 1e-3) / 1e12,
+            "traffic": traffic["state_walk"],
         },
         "decode": {
             "steps": T,
@@ -255,7 +294,7 @@ def main():
                 "peak": PEAK_HBM / 1e9,
                 "unit": "GB/s",
                 "frac": dgbps * 1e9 / PEAK_HBM,
-                "traffic": None,
+                "traffic": traffic["decode_step"],
                 "algorithmic_bytes_per_step": dbytes,
             },
         },
