@@ -39,6 +39,8 @@
 //   A[i][kk]: i = l % 32, kk = 8*(l/32) + 0..7
 //   B[kk][j]: j = l % 32, kk = 8*(l/32) + 0..7
 //   D[i][j] : j = l % 32, i = 8*(r/4) + 4*(l/32) + r%4 for accumulator r = 0..15
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace ret {
@@ -57,6 +59,10 @@ __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) { return *reinterpret_c
 
 __device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, const floatx16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 mfma16(const bf16x8& a, const bf16x8& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
@@ -87,20 +93,29 @@ constexpr int kBufferConfig = 0x00020000;  // raw buffer descriptor word 3 for g
 constexpr int kOutOfRange = 0x40000000;     // an offset past any tile: the load returns zero
 
 // Buffer descriptor over `nbytes` bytes at `base`; loads past the end return zero.
+// `base` and `nbytes` must be the same in every lane of the wave: they are
+// read from the first active lane, so the descriptor lives in scalar
+// registers (otherwise the compiler wraps each load in a loop over the
+// distinct descriptors of the wave).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int nbytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), nbytes, kBufferConfig);
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+  void* u = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, static_cast<short>(0), __builtin_amdgcn_readfirstlane(nbytes),
+                                           kBufferConfig);
 }
 
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_offset) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0);
 }
 
-// Register staging of one 64-row tile of a row-major bf16 matrix with NTHR
+// Register staging of one ROWS-row tile of a row-major bf16 matrix with NTHR
 // threads: thread t owns 16-byte pieces t, t+NTHR, ... of a tile COLS wide
 // (row = piece / (COLS/8)); COLS is a compile-time width so the piece layout
 // costs shifts only. Rows at or past `rows_valid`, and columns at or past
 // `cols_valid`, read as zero (buffer range check / out-of-range offset).
-template <int MAXP, int NTHR, int COLS>
+template <int MAXP, int NTHR, int COLS, int ROWS = kRows>
 struct TileRegs {
   static constexpr int kPerRow = COLS / 8;
   u32x4 p[MAXP];
@@ -114,7 +129,7 @@ struct TileRegs {
 #pragma unroll
     for (int m = 0; m < MAXP; ++m) {
       const int row = row_of(m), col = col_of(m);
-      const int off = (row < kRows && col < cols_valid) ? (row * stride + col) * 2 : kOutOfRange;
+      const int off = (row < ROWS && col < cols_valid) ? (row * stride + col) * 2 : kOutOfRange;
       p[m] = buffer_load16(r, off);
     }
   }
@@ -123,14 +138,14 @@ struct TileRegs {
   __device__ __forceinline__ void store(uint16_t* dst, int pitch) const {
 #pragma unroll
     for (int m = 0; m < MAXP; ++m)
-      if (row_of(m) < kRows) *reinterpret_cast<u32x4*>(dst + row_of(m) * pitch + col_of(m)) = p[m];
+      if (row_of(m) < ROWS) *reinterpret_cast<u32x4*>(dst + row_of(m) * pitch + col_of(m)) = p[m];
   }
 
   // Store with row r multiplied by scale[m] (one factor per owned piece's row).
   __device__ __forceinline__ void store_scaled(uint16_t* dst, int pitch, const float (&scale)[MAXP]) const {
 #pragma unroll
     for (int m = 0; m < MAXP; ++m) {
-      if (row_of(m) < kRows) {
+      if (row_of(m) < ROWS) {
         u32x4 v = p[m];
         const float z = scale[m];
 #pragma unroll
@@ -323,8 +338,9 @@ __global__ void __launch_bounds__(kThreads) mfma_state_walk_kernel(WalkArgs a, H
 // ---------------------------------------------------------------------------
 // Output
 // ---------------------------------------------------------------------------
-constexpr int kPitchQK = 264;     // sQ/sK pitch: 528 B, rows an odd number of 16-byte slots apart
-constexpr int kPitchP = 72;       // sP pitch: 144 B
+constexpr int kTile = 32;      // rows of a staged tile: 32 keys of V, or 32 rows of the chunk state
+constexpr int kPitchQ = 264;   // sQ pitch: 528 B, rows an odd number of 16-byte slots apart
+constexpr int kPitchP = 40;    // sP pitch: 80 B, 16 consecutive rows fall on distinct banks
 
 struct OutArgs {
   const uint16_t* q;
@@ -336,40 +352,64 @@ struct OutArgs {
   int H, N, dk, dv, chunk, nchunks, nqb;
 };
 
-__device__ __forceinline__ floatx4 mfma16(const bf16x8& a, const bf16x8& b, const floatx4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+// One level of a reduce-scatter butterfly across lanes that differ in bit M:
+// x[0..2M) -> x[0..M), the lane keeping the half its bit M selects and adding
+// the partner's copy of it.
+template <int M>
+__device__ __forceinline__ void butterfly_level(float* x, int lane) {
+  const bool hi = lane & M;
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    const float mine = hi ? x[j + M] : x[j], other = hi ? x[j] : x[j + M];
+    x[j] = mine + __shfl_xor(other, M, 64);
+  }
 }
 
-// WAVES waves form a (64/(32*MQ)) x VG grid over the 64 x DV output block:
-// each wave owns 32*MQ query rows and 32*NV value columns (VG * 32 * NV = DV).
-// With four waves (one per SIMD) each wave owns all 64 rows of a 32*NV column
-// slab, accumulates in AGPRs and computes one 32x32 tile of S^T, so every LDS
-// operand is read by fewer waves.
-// With eight waves S^T is split into 16x16 tiles with both operands in LDS.
-template <int WAVES, int MQ, int NV>
+// Offset (elements) of 16-byte granule `g` of row `row` in a 32 x 256 K block
+// stored without padding: granules are XOR-swizzled with the row so that 16
+// rows read at the same column hit 16 different bank groups.
+__device__ __forceinline__ int k_swz(int row, int g) { return row * 256 + ((g ^ (row & 15)) << 3); }
+
+// One workgroup per (head, 64-row query block); wave w owns value columns
+// [32*NVT*w, 32*NVT*(w+1)) of all 64 rows (2 x NVT accumulator tiles).
+//
+// The block's work is a sequence of tiles, each a 32-row bf16 matrix X staged
+// in LDS and multiplied into O as O += A X: first the dk/32 slices of the
+// stored chunk state (A = the matching 32 columns of Q, the cross-chunk
+// read-out), then the 32-key blocks of the chunk up to the diagonal (A = the
+// decayed scores of that block, X = its V rows). X tiles are loaded into
+// registers two tiles ahead and written to LDS one tile ahead.
+//
+// Scores of a key block, S^T = K Q^T (32 keys x 64 queries), are formed one
+// tile ahead: wave (tt, qt) computes the 16 x 16 tile of keys 16*tt.. and
+// queries 16*qt.. on 16x16x32 MFMAs, K from LDS, its 16 query rows held in
+// registers for the whole block; it applies gamma^(n-m) (zero above the
+// diagonal) and writes the bf16 scores to sP for the next tile's product. The
+// block's K rows are loaded once by all threads, three tiles ahead into
+// registers and into LDS one tile before use. Every thread issues the same
+// global loads each tile (ranges past the data load zeros); one barrier per
+// tile.
+template <int NVT, int WAVES>
 __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, HeadDecay decay, GnArgs gn) {
-  constexpr int kOutThreads = 64 * WAVES;
-  constexpr int QG = 2 / MQ;            // query-row groups
-  constexpr int VG = WAVES / QG;        // value-column groups
-  constexpr int DV = VG * 32 * NV;      // dv handled by the workgroup
-  constexpr int PV = DV + 32;           // sV pitch: rows 64 B apart mod 256
-  constexpr int KP = kRows * 256 / 8 / kOutThreads;  // 16-byte pieces per thread of a K or Q tile (dk <= 256)
-  constexpr int VP = kRows * DV / 8 / kOutThreads;   // ... of a V tile or state slice
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[kRows * kPitchQK];
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kRows * kPitchQK];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kRows * PV];
-  __shared__ __attribute__((aligned(16))) uint16_t sP[kRows * kPitchP];
-  __shared__ float s_stat[VG][kRows];
-  __shared__ float s_mean[kRows];
-  __shared__ float s_rstd[kRows];
+  constexpr int NT = 64 * WAVES;
+  constexpr int DV = WAVES * 32 * NVT;
+  constexpr int PX = DV + 32;                  // sX pitch: rows 64 B apart mod 256
+  constexpr int XP = kTile * DV / 8 / NT;      // 16-byte pieces per thread of an X tile
+  constexpr int KP = kTile * 256 / 8 / NT;     // ... of a K block (dk <= 256)
+  constexpr int QP = kRows * 256 / 8 / NT;     // ... of the Q block
+  static_assert(XP >= 1 && KP >= 1 && QP >= 1, "layout");
+  constexpr int SW = 8 / WAVES;              // 16 x 16 score tiles per wave (8 per key block)
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[kRows * kPitchQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sX[2 * kTile * PX];  // two X buffers; 64 rows of O at the end
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kTile * 256];
+  __shared__ __attribute__((aligned(16))) uint16_t sP[2][kRows * kPitchP];
+  static_assert(sizeof(sK) >= (WAVES + 2) * kRows * sizeof(float), "GroupNorm statistics reuse sK");
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int lrow = lane & 31;
+  const int l32 = lane & 31;
   const int lk = 8 * (lane >> 5);
-  const int qg = wave / VG, vg = wave % VG;
-  const int qrow0 = qg * 32 * MQ;   // first query row (in the block) of this wave
-  const int vcol0 = vg * 32 * NV;   // first value column of this wave
+  const int vcol0 = wave * 32 * NVT;
   const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
   const int64_t bh = blk / a.nqb;
   const int qb = blk % a.nqb;
@@ -379,280 +419,247 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
   const int c = q0 / a.chunk;
   const int cs = c * a.chunk;
   const int dk = a.dk;
-  const int dk64 = (dk + 63) & ~63;  // state rows read in whole 64-row slices (zero past dk)
   const int qvalid = min(kRows, a.N - q0);
-  const uint16_t* qbase = a.q + (bh * a.N + q0) * static_cast<int64_t>(dk);
+  const int kend = min(q0 + kRows, a.N);
+  const int nkb = (kend - cs + kTile - 1) / kTile;  // 32-key blocks of the chunk up to the diagonal
+  const bool has_state = a.chunk_states && (c > 0 || a.state_for_chunk0);
+  const int ns = has_state ? dk / kTile : 0;          // state slices (dk is a multiple of 32)
+  const int ntiles = ns + nkb;
   const uint16_t* kbase = a.k + bh * static_cast<int64_t>(a.N) * dk;
   const uint16_t* vbase = a.v + bh * static_cast<int64_t>(a.N) * DV;
-  const bool has_state = a.chunk_states && (c > 0 || a.state_for_chunk0);
   const uint16_t* rbase = has_state ? a.chunk_states + (bh * a.nchunks + c) * static_cast<int64_t>(dk) * DV : nullptr;
-  const int nslices = has_state ? dk64 / kRows : 0;
-  const int tb_first = cs / kRows;
-  const int ntiles = nslices + (qb - tb_first + 1);
 
-  // Q tile into LDS (A operand of the read-out), zero beyond N and dk.
-  {
-    // Columns dk..255 are written as zeros (they meet zero-filled state rows).
-    TileRegs<KP, kOutThreads, 256> rq;
-    rq.load(qbase, dk, qvalid, dk);
-    rq.store(sQ, kPitchQK);
-  }
-  // S^T = K Q^T. Eight waves: 16x16x32 MFMAs, this wave's 16 query columns
-  // (qt16) and 32 key rows (two 16-row tiles), both operands from LDS. Four
-  // waves: one 32x32 tile (key rows tt*32.., query columns qt*32..) per wave,
-  // operands from LDS.
-  const int qt16 = wave & 3, tg = wave >> 2;
+  // Score tiles of this wave: u = wave + WAVES*j (j < SW) of the 8 16 x 16
+  // tiles of a key block, key tile tt = u/4 and query tile qt = u%4.
   const int l16 = lane & 15, lk16 = 8 * (lane >> 4);
-  const int tt = wave >> 1, qt = wave & 1;
-  constexpr int NBT = WAVES == 8 ? 8 : 16;
-  float bt[NBT];  // gamma^(-(t - t0)) for this lane's key rows of a block (t - t0 <= 63)
-#pragma unroll
-  for (int i = 0; i < NBT; ++i) {
-    const int tl = WAVES == 8 ? tg * 32 + (i >> 2) * 16 + 4 * (lane >> 4) + (i & 3) : tt * 32 + acc_row(i, lane);
-    bt[i] = gpow(lg, -static_cast<float>(tl));
-  }
 
-  floatx16 acc[MQ][NV];
-#pragma unroll
-  for (int mt = 0; mt < MQ; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NV; ++nt) acc[mt][nt] = floatx16{};
-
-  TileRegs<KP, kOutThreads, 256> rk;
-  TileRegs<VP, kOutThreads, DV> rv;
-  auto prefetch = [&](int it) {
-    if (it < nslices) {
-      rv.load(rbase + static_cast<int64_t>(it * kRows) * DV, DV, min(kRows, dk - it * kRows), DV);
+  TileRegs<XP, NT, DV, kTile> rx;
+  auto load_x = [&](int it) {
+    if (it < ns) {
+      rx.load(rbase + static_cast<int64_t>(it * kTile) * DV, DV, kTile, DV);
     } else {
-      const int t0 = (tb_first + it - nslices) * kRows;
-      const int nvalid = min(kRows, a.N - t0);
-      rk.load(kbase + static_cast<int64_t>(t0) * dk, dk, nvalid, dk);
-      rv.load(vbase + static_cast<int64_t>(t0) * DV, DV, nvalid, DV);
+      const int t0 = cs + (it - ns) * kTile;
+      rx.load(vbase + static_cast<int64_t>(t0) * DV, DV, it < ntiles ? min(kTile, a.N - t0) : 0, DV);
     }
   };
-  prefetch(0);
+  TileRegs<KP, NT, 256, kTile> rk;
+  auto load_k = [&](int kb) {
+    const bool ok = kb >= 0 && kb < nkb;
+    const int t0 = cs + (ok ? kb : 0) * kTile;
+    rk.load(kbase + static_cast<int64_t>(t0) * dk, dk, ok ? min(kTile, a.N - t0) : 0, dk);
+  };
+  auto store_k = [&](int kb) {
+    uint16_t* dst = sK[kb & 1];
+#pragma unroll
+    for (int m = 0; m < KP; ++m) {
+      const int row = rk.row_of(m);
+      *reinterpret_cast<u32x4*>(dst + k_swz(row, rk.col_of(m) >> 3)) = rk.p[m];
+    }
+  };
 
-  for (int it = 0; it < ntiles; ++it) {
-    const bool is_slice = it < nslices;
-    __syncthreads();  // previous tile's readers are done with sK / sV / sP
-    if (!is_slice) rk.store(sK, kPitchQK);
-    rv.store(sV, PV);
-    __syncthreads();
-    if (it + 1 < ntiles) prefetch(it + 1);
+  // Prologue: Q block into LDS (zero past N and dk), first X tile into LDS and
+  // the second into registers; the K block of the first scores into LDS and
+  // the next into registers.
+  const int i0 = min(0, ns - 1);
+  {
+    TileRegs<QP, NT, 256> rq;
+    rq.load(a.q + (bh * a.N + q0) * static_cast<int64_t>(dk), dk, qvalid, dk);
+    load_x(0);
+    load_k(i0 + 1 - ns);
+    rq.store(sQ, kPitchQ);
+    rx.store(sX, PX);
+    store_k(i0 + 1 - ns);
+  }
+  load_x(1);
+  load_k(i0 + 2 - ns);
+  __syncthreads();
+  // Query rows of this wave's score tiles as 16x16x32 B operands (zero past dk).
+  bf16x8 qf[SW][8];
+#pragma unroll
+  for (int j = 0; j < SW; ++j) {
+    const int qt = (wave + WAVES * j) & 3;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[j][s] = ld8(sQ + (qt * 16 + l16) * kPitchQ + 32 * s + lk16);
+  }
 
-    if (is_slice) {
-      // Cross-chunk read-out: O += Q[:, 64 state rows] R[64 rows, :].
-      const int kcol = it * kRows;
-#pragma unroll 2
-      for (int s = 0; s < kRows / 16; ++s) {
-        bf16x8 av[MQ];
+  floatx16 acc[2][NVT];
 #pragma unroll
-        for (int mt = 0; mt < MQ; ++mt) av[mt] = ld8(sQ + (qrow0 + mt * 32 + lrow) * kPitchQK + kcol + s * 16 + lk);
+  for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int nt = 0; nt < NV; ++nt) {
-          const bf16x8 b = ld_tr8(sV, PV, s * 16, vcol0 + nt * 32, lane);
+    for (int nt = 0; nt < NVT; ++nt) acc[qt][nt] = floatx16{};
+
+  // Scores of key block kb: this wave's 16 x 16 tiles of S^T = K Q^T, decayed
+  // and masked, as bf16 into sP.
+  auto scores = [&](int kb) {
+    if (kb < 0 || kb >= nkb) return;
+    const int t0 = cs + kb * kTile;
+    const uint16_t* kt = sK[kb & 1];
 #pragma unroll
-          for (int mt = 0; mt < MQ; ++mt) acc[mt][nt] = mfma32(av[mt], b, acc[mt][nt]);
+    for (int j = 0; j < SW; ++j) {
+      const int u = wave + WAVES * j;
+      const int qt = u & 3, tt = u >> 2;
+      floatx4 sacc = floatx4{};
+      if (t0 + tt * 16 <= q0 + qt * 16 + 15) {  // else every key follows every query of the tile
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const bf16x8 kfr = ld8(kt + k_swz(tt * 16 + l16, 4 * s + (lane >> 4)));
+          sacc = mfma16(kfr, qf[j][s], sacc);  // zero columns past dk
         }
       }
-      if (it == nslices - 1) {
-        // Scale row j (chunk-local) by xi_j = gamma^(j+1).
+      // sacc[r] = S^T[t][q]: t = tt*16 + 4*(lane/16) + r, q = qt*16 + lane%16.
+      const int ql = qt * 16 + l16;
+      const int tl = tt * 16 + 4 * (lane >> 4);
+      const int d0 = q0 + ql - (t0 + tl);
+      float x[4];
 #pragma unroll
-        for (int mt = 0; mt < MQ; ++mt)
+      for (int r = 0; r < 4; ++r) {
+        const int d = d0 - r;
+        x[r] = d >= 0 ? sacc[r] * gpow(lg, static_cast<float>(d)) : 0.f;
+      }
+      uint2 w;
+      w.x = pack_bf16x2(x[0], x[1]);
+      w.y = pack_bf16x2(x[2], x[3]);
+      *reinterpret_cast<uint2*>(sP[kb & 1] + ql * kPitchP + tl) = w;
+    }
+  };
+
+  // Tile i multiplies X_i and forms the scores of key block i+1-ns; with no
+  // state slice the first key block's scores are formed before the first tile.
+  for (int i = i0; i < 0; ++i) {
+    store_k(i + 2 - ns);
+    load_k(i + 3 - ns);
+    scores(i + 1 - ns);
+    __syncthreads();
+  }
+  for (int i = 0; i < ntiles; ++i) {
+    rx.store(sX + ((i + 1) & 1) * kTile * PX, PX);
+    store_k(i + 2 - ns);
+    load_x(i + 2);
+    load_k(i + 3 - ns);
+    scores(i + 1 - ns);
+
+    {
+      // O += A X over the tile's 32 rows.
+      const bool slice = i < ns;
+      const uint16_t* abase = slice ? sQ + i * kTile : sP[(i - ns) & 1];
+      const int apitch = slice ? kPitchQ : kPitchP;
+      const uint16_t* xb = sX + (i & 1) * kTile * PX;
+      auto multiply = [&](auto skip_tile0) {
+#pragma unroll
+        for (int s = 0; s < kTile / 16; ++s) {
+          bf16x8 av[2];
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) av[qt] = ld8(abase + (qt * 32 + l32) * apitch + 16 * s + lk);
+#pragma unroll
+          for (int nt = 0; nt < NVT; ++nt) {
+            const bf16x8 b = ld_tr8(xb, PX, 16 * s, vcol0 + 32 * nt, lane);
+            if constexpr (!decltype(skip_tile0)::value) acc[0][nt] = mfma32(av[0], b, acc[0][nt]);
+            acc[1][nt] = mfma32(av[1], b, acc[1][nt]);
+          }
+        }
+      };
+      // Keys of this block all follow query tile 0: its scores are zero.
+      if (!slice && cs + (i - ns) * kTile > q0 + 31) multiply(std::true_type{});
+      else multiply(std::false_type{});
+      if (i == ns - 1) {
+        // Scale chunk-local row j by xi_j = gamma^(j+1).
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int j = q0 + qrow0 + mt * 32 + acc_row(r, lane) - cs;
+            const int j = q0 + qt * 32 + acc_row(r, lane) - cs;
             const float xi = gpow(lg, static_cast<float>(j + 1));
 #pragma unroll
-            for (int nt = 0; nt < NV; ++nt) acc[mt][nt][r] *= xi;
+            for (int nt = 0; nt < NVT; ++nt) acc[qt][nt][r] *= xi;
           }
-      }
-      continue;
-    }
-
-    // Intra-chunk key block starting at t0: S^T[t][q], decay gamma^(q-t) (zero above
-    // the diagonal) applied in registers, A[q][t] stored to LDS as bf16.
-    // gamma^(q-t) = gamma^(q-t0) * gamma^(-(t-t0)); the second factor is fixed per lane.
-    const int t0 = (tb_first + it - nslices) * kRows;
-    if constexpr (WAVES == 8) {
-      floatx4 sacc[2] = {floatx4{}, floatx4{}};
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        if (s * 32 < dk) {
-          const bf16x8 bq = ld8(sQ + (qt16 * 16 + l16) * kPitchQK + s * 32 + lk16);
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const bf16x8 ak = ld8(sK + (tg * 32 + u * 16 + l16) * kPitchQK + s * 32 + lk16);
-            sacc[u] = mfma16(ak, bq, sacc[u]);
-          }
-        }
-      }
-      // sacc[u][r] = S^T[t][q], t = tg*32 + 16u + 4*(lane/16) + r, q = qt16*16 + l16.
-      const int qa = q0 + qt16 * 16 + l16;
-      const float aq = gpow(lg, static_cast<float>(qa - t0));
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int tl = tg * 32 + u * 16 + 4 * (lane >> 4);
-        float x[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int d = qa - (t0 + tl + r);
-          x[r] = (d >= 0) ? sacc[u][r] * (aq * bt[u * 4 + r]) : 0.f;
-        }
-        uint2 w;
-        w.x = pack_bf16x2(x[0], x[1]);
-        w.y = pack_bf16x2(x[2], x[3]);
-        *reinterpret_cast<uint2*>(sP + (qt16 * 16 + l16) * kPitchP + tl) = w;
-      }
-    } else {
-      floatx16 sacc = floatx16{};
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        if (s * 16 < dk) {
-          const bf16x8 ak = ld8(sK + (tt * 32 + lrow) * kPitchQK + s * 16 + lk);
-          const bf16x8 bq = ld8(sQ + (qt * 32 + lrow) * kPitchQK + s * 16 + lk);
-          sacc = mfma32(ak, bq, sacc);
-        }
-      }
-      // sacc[r] = S^T[t][q], t = tt*32 + acc_row(r), q = qt*32 + lrow.
-      const int qa = q0 + qt * 32 + lrow;
-      const float aq = gpow(lg, static_cast<float>(qa - t0));
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float x[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          const int d = qa - (t0 + tt * 32 + acc_row(r, lane));
-          x[e] = (d >= 0) ? sacc[r] * (aq * bt[r]) : 0.f;
-        }
-        uint2 w;
-        w.x = pack_bf16x2(x[0], x[1]);
-        w.y = pack_bf16x2(x[2], x[3]);
-        *reinterpret_cast<uint2*>(sP + (qt * 32 + lrow) * kPitchP + tt * 32 + 8 * g + 4 * (lane >> 5)) = w;
       }
     }
     __syncthreads();
-#pragma unroll 2
-    for (int s = 0; s < kRows / 16; ++s) {
-      bf16x8 ap[MQ];
-#pragma unroll
-      for (int mt = 0; mt < MQ; ++mt) ap[mt] = ld8(sP + (qrow0 + mt * 32 + lrow) * kPitchP + s * 16 + lk);
-#pragma unroll
-      for (int nt = 0; nt < NV; ++nt) {
-        const bf16x8 b = ld_tr8(sV, PV, s * 16, vcol0 + nt * 32, lane);
-#pragma unroll
-        for (int mt = 0; mt < MQ; ++mt) acc[mt][nt] = mfma32(ap[mt], b, acc[mt][nt]);
-      }
-    }
   }
 
   // Epilogue: optional per-head GroupNorm over the DV columns of each row, then
   // the bf16 store.
   if (gn.enabled) {
-    // Row statistics: each lane reduces its 16 row slots over the 32 lanes that
-    // share them with a reduce-scatter butterfly (16 exchanges instead of 80);
-    // lane l then holds the wave's partial for slot (l%32)/2. One thread per row
-    // combines the value-column groups through LDS.
-    const int slot = (lane & 31) >> 1;
-    auto reduce_rows = [&](const float (&x)[16]) {
-      float w[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bool hi = lane & 16;
-        const float mine = hi ? x[i + 8] : x[i], other = hi ? x[i] : x[i + 8];
-        w[i] = mine + __shfl_xor(other, 16, 64);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool hi = lane & 8;
-        const float mine = hi ? w[i + 4] : w[i], other = hi ? w[i] : w[i + 4];
-        w[i] = mine + __shfl_xor(other, 8, 64);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const bool hi = lane & 4;
-        const float mine = hi ? w[i + 2] : w[i], other = hi ? w[i] : w[i + 2];
-        w[i] = mine + __shfl_xor(other, 4, 64);
-      }
-      {
-        const bool hi = lane & 2;
-        const float mine = hi ? w[1] : w[0], other = hi ? w[0] : w[1];
-        w[0] = mine + __shfl_xor(other, 2, 64);
-      }
-      return w[0] + __shfl_xor(w[0], 1, 64);
+    float* s_stat = reinterpret_cast<float*>(&sK[0][0]);  // [WAVES][64], then mean[64], rstd[64]
+    float* s_mean = s_stat + WAVES * kRows;
+    float* s_rstd = s_mean + kRows;
+    // Each lane holds 32 row slots (query tile qt, accumulator r). A
+    // reduce-scatter butterfly over the 32 lanes sharing them leaves lane l
+    // with the wave's sum for slot l%32; one thread per row then adds the waves.
+    auto reduce_rows = [&](float (&x)[32]) {
+      butterfly_level<16>(x, lane);
+      butterfly_level<8>(x, lane);
+      butterfly_level<4>(x, lane);
+      butterfly_level<2>(x, lane);
+      butterfly_level<1>(x, lane);
+      return x[0];
     };
-    float x[16];
+    const int my_slot = lane & 31;
+    const int my_row = (my_slot >> 4) * 32 + acc_row(my_slot & 15, lane);
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
+      float x[32];
 #pragma unroll
-      for (int mt = 0; mt < MQ; ++mt) {
-        float mean_r[16];
-        if (pass == 1) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mean_r[r] = s_mean[qrow0 + mt * 32 + acc_row(r, lane)];
-        }
+      for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
+          const float mean = pass == 0 ? 0.f : s_mean[qt * 32 + acc_row(r, lane)];
           float t = 0.f;
 #pragma unroll
-          for (int nt = 0; nt < NV; ++nt) {
-            const float d = pass == 0 ? acc[mt][nt][r] : acc[mt][nt][r] - mean_r[r];
+          for (int nt = 0; nt < NVT; ++nt) {
+            const float d = acc[qt][nt][r] - mean;
             t += pass == 0 ? d : d * d;
           }
-          x[r] = t;
+          x[qt * 16 + r] = t;
         }
-        const float tot = reduce_rows(x);
-        if ((lane & 1) == 0) s_stat[vg][qrow0 + mt * 32 + acc_row(slot, lane)] = tot;
-      }
+      s_stat[wave * kRows + my_row] = reduce_rows(x);
       __syncthreads();
       if (threadIdx.x < kRows) {
         float t = 0.f;
 #pragma unroll
-        for (int g = 0; g < VG; ++g) t += s_stat[g][threadIdx.x];
+        for (int w = 0; w < WAVES; ++w) t += s_stat[w * kRows + threadIdx.x];
         t /= DV;
         if (pass == 0) s_mean[threadIdx.x] = t;
         else s_rstd[threadIdx.x] = 1.0f / sqrtf(t + gn.eps);
       }
       __syncthreads();
     }
-    float w[NV], bb[NV];
+    float w[NVT], bb[NVT];
 #pragma unroll
-    for (int nt = 0; nt < NV; ++nt) {
-      const int vcol = vcol0 + nt * 32 + lrow;
+    for (int nt = 0; nt < NVT; ++nt) {
+      const int vcol = vcol0 + nt * 32 + l32;
       w[nt] = gn.weight ? gn.weight[h * DV + vcol] : 1.f;
       bb[nt] = gn.bias ? gn.bias[h * DV + vcol] : 0.f;
     }
 #pragma unroll
-    for (int mt = 0; mt < MQ; ++mt)
+    for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = qrow0 + mt * 32 + acc_row(r, lane);
+        const int row = qt * 32 + acc_row(r, lane);
         const float mean = s_mean[row], rstd = s_rstd[row];
 #pragma unroll
-        for (int nt = 0; nt < NV; ++nt) acc[mt][nt][r] = (acc[mt][nt][r] - mean) * rstd * w[nt] + bb[nt];
+        for (int nt = 0; nt < NVT; ++nt) acc[qt][nt][r] = (acc[qt][nt][r] - mean) * rstd * w[nt] + bb[nt];
       }
   }
 
-  // Store: stage the bf16 tile in LDS (the V buffer is free), then write each
-  // row with 16-byte stores.
-  __syncthreads();
+  // Store: stage the bf16 block in LDS (the X buffers), then write each row
+  // with 16-byte stores.
 #pragma unroll
-  for (int mt = 0; mt < MQ; ++mt)
+  for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = qrow0 + mt * 32 + acc_row(r, lane);
+      const int row = qt * 32 + acc_row(r, lane);
 #pragma unroll
-      for (int nt = 0; nt < NV; ++nt) sV[row * PV + vcol0 + nt * 32 + lrow] = f32_to_bf16(acc[mt][nt][r]);
+      for (int nt = 0; nt < NVT; ++nt) sX[row * PX + vcol0 + nt * 32 + l32] = f32_to_bf16(acc[qt][nt][r]);
     }
   __syncthreads();
   uint16_t* obase = a.o + (bh * a.N + q0) * static_cast<int64_t>(DV);
   constexpr int per_row = DV / 8;
-  for (int i = threadIdx.x; i < kRows * per_row; i += kOutThreads) {
+  for (int i = threadIdx.x; i < kRows * per_row; i += NT) {
     const int row = i / per_row, c8 = i - row * per_row;
     if (row < qvalid)
       *reinterpret_cast<u32x4*>(obase + static_cast<int64_t>(row) * DV + c8 * 8) =
-          *reinterpret_cast<const u32x4*>(sV + row * PV + c8 * 8);
+          *reinterpret_cast<const u32x4*>(sX + row * PX + c8 * 8);
   }
 }
 
@@ -728,9 +735,9 @@ hipError_t launch_mfma_chunk_out(const uint16_t* q, const uint16_t* k, const uin
   a.nqb = (d.N + kRows - 1) / kRows;
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(d.B) * d.H * a.nqb));
   switch (d.dv) {
-    case 128: mfma_chunk_out_kernel<8, 1, 1><<<grid, 512, 0, stream>>>(a, decay, gn); break;
-    case 256: mfma_chunk_out_kernel<8, 1, 2><<<grid, 512, 0, stream>>>(a, decay, gn); break;
-    default: mfma_chunk_out_kernel<8, 1, 4><<<grid, 512, 0, stream>>>(a, decay, gn); break;
+    case 128: mfma_chunk_out_kernel<1, 4><<<grid, 256, 0, stream>>>(a, decay, gn); break;
+    case 256: mfma_chunk_out_kernel<1, 8><<<grid, 512, 0, stream>>>(a, decay, gn); break;
+    default: mfma_chunk_out_kernel<2, 8><<<grid, 512, 0, stream>>>(a, decay, gn); break;
   }
   return hipGetLastError();
 }
