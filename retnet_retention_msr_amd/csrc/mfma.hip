@@ -134,6 +134,11 @@ struct TileRegs {
     }
   }
 
+  // Store piece m into LDS [row][col] with the given pitch (elements).
+  __device__ __forceinline__ void store_piece(uint16_t* dst, int pitch, int m) const {
+    if (row_of(m) < ROWS) *reinterpret_cast<u32x4*>(dst + row_of(m) * pitch + col_of(m)) = p[m];
+  }
+
   // Store into LDS [row][col] with the given pitch (elements).
   __device__ __forceinline__ void store(uint16_t* dst, int pitch) const {
 #pragma unroll
@@ -352,17 +357,38 @@ struct OutArgs {
   int H, N, dk, dv, chunk, nchunks, nqb;
 };
 
-// One level of a reduce-scatter butterfly across lanes that differ in bit M:
-// x[0..2M) -> x[0..M), the lane keeping the half its bit M selects and adding
-// the partner's copy of it.
-template <int M>
-__device__ __forceinline__ void butterfly_level(float* x, int lane) {
+// Reduce-scatter of 32 values over the 32 lanes of each half-wave, in VALU
+// lane exchanges only: afterwards lane l holds, for slot l%32, the sum over
+// the 32 lanes of its half. Each level pairs every lane with one whose bit
+// (16, 8, 4, 2, 1) differs and that shares the bits already processed; the
+// lane keeps the half of its slots its own bit selects and adds the partner's
+// copy of that half. Level 16 uses v_permlane16_swap (rows 1/3 exchanged with
+// rows 0/2); levels 8, 4, 2, 1 use DPP row rotate by 8, row half-mirror
+// (lane i <-> 7-i within eight), and quad permutes [2,3,0,1] and [1,0,3,2].
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+template <int M, int CTRL>
+__device__ __forceinline__ void rs_level(float* x, int lane) {
   const bool hi = lane & M;
 #pragma unroll
   for (int j = 0; j < M; ++j) {
     const float mine = hi ? x[j + M] : x[j], other = hi ? x[j] : x[j + M];
-    x[j] = mine + __shfl_xor(other, M, 64);
+    x[j] = mine + dpp_f<CTRL>(other);
   }
+}
+__device__ __forceinline__ float reduce_scatter32(float (&x)[32], int lane) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[j]), __float_as_uint(x[j + 16]), false, false);
+    x[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  rs_level<8, 0x128>(x, lane);  // row_ror:8
+  rs_level<4, 0x141>(x, lane);  // row_half_mirror
+  rs_level<2, 0x4E>(x, lane);   // quad_perm [2,3,0,1]
+  rs_level<1, 0xB1>(x, lane);   // quad_perm [1,0,3,2]
+  return x[0];
 }
 
 // Offset (elements) of 16-byte granule `g` of row `row` in a 32 x 256 K block
@@ -370,45 +396,83 @@ __device__ __forceinline__ void butterfly_level(float* x, int lane) {
 // rows read at the same column hit 16 different bank groups.
 __device__ __forceinline__ int k_swz(int row, int g) { return row * 256 + ((g ^ (row & 15)) << 3); }
 
+// Position of 16-byte granule `g` of row `row` in an unpadded X tile (V rows or
+// chunk-state rows): rows r..r+3 of a transposed read land in four different
+// 64-byte bank groups.
+__device__ __forceinline__ int x_pos(int row, int g) { return g ^ ((row & 3) << 2); }
+
+// Transposed MFMA operand (see ld_tr8) from an unpadded, swizzled X tile with
+// DV columns.
+template <int DV>
+__device__ __forceinline__ bf16x8 ld_tr8_x(const uint16_t* tile, int row0, int col0, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int row = row0 + 8 * (g >> 1) + (j >> 2);
+  const int col = col0 + 16 * (g & 1) + 4 * (j & 3);
+  const uint16_t* p = tile + row * DV + (x_pos(row, col >> 3) << 3) + (col & 7);
+  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p));
+  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p + 4 * DV));  // row+4: same swizzle
+  const shortx8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
+// lds_chunk + 16*l (the chunk address must be the same in every lane); the
+// global side is `byte_offset` into the descriptor's range (zeros past it).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds_chunk, int byte_offset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds_chunk), 16, byte_offset, 0, 0, 0);
+}
+
+// Wait until this wave's global loads (including the direct LDS copies) are done.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
 // One workgroup per (head, 64-row query block); wave w owns value columns
 // [32*NVT*w, 32*NVT*(w+1)) of all 64 rows (2 x NVT accumulator tiles).
 //
-// The block's work is a sequence of tiles, each a 32-row bf16 matrix X staged
-// in LDS and multiplied into O as O += A X: first the dk/32 slices of the
-// stored chunk state (A = the matching 32 columns of Q, the cross-chunk
-// read-out), then the 32-key blocks of the chunk up to the diagonal (A = the
-// decayed scores of that block, X = its V rows). X tiles are loaded into
-// registers two tiles ahead and written to LDS one tile ahead.
+// The block's work is a sequence of tiles, each a 32-row bf16 matrix X in
+// LDS multiplied into O as O += A X: first the dk/32 slices of the stored
+// chunk state (A = the matching 32 columns of Q, the cross-chunk read-out),
+// then the 32-key blocks of the chunk up to the diagonal (A = the decayed
+// scores of that block, X = its V rows).
 //
 // Scores of a key block, S^T = K Q^T (32 keys x 64 queries), are formed one
 // tile ahead: wave (tt, qt) computes the 16 x 16 tile of keys 16*tt.. and
 // queries 16*qt.. on 16x16x32 MFMAs, K from LDS, its 16 query rows held in
 // registers for the whole block; it applies gamma^(n-m) (zero above the
-// diagonal) and writes the bf16 scores to sP for the next tile's product. The
-// block's K rows are loaded once by all threads, three tiles ahead into
-// registers and into LDS one tile before use. Every thread issues the same
-// global loads each tile (ranges past the data load zeros); one barrier per
-// tile.
+// diagonal) and writes the bf16 scores to sP for the next tile's product.
+//
+// X tiles and K blocks travel straight from global memory into LDS (buffer
+// loads with an LDS destination) one tile ahead, into the other of two buffer
+// pairs; each tile ends with a wait for those copies and one barrier. The
+// buffers are distinct LDS arrays chosen at compile time per tile parity, so
+// the LDS reads of a tile never wait for the copies in flight.
 template <int NVT, int WAVES>
 __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, HeadDecay decay, GnArgs gn) {
   constexpr int NT = 64 * WAVES;
   constexpr int DV = WAVES * 32 * NVT;
-  constexpr int PX = DV + 32;                  // sX pitch: rows 64 B apart mod 256
-  constexpr int XP = kTile * DV / 8 / NT;      // 16-byte pieces per thread of an X tile
-  constexpr int KP = kTile * 256 / 8 / NT;     // ... of a K block (dk <= 256)
-  constexpr int QP = kRows * 256 / 8 / NT;     // ... of the Q block
-  static_assert(XP >= 1 && KP >= 1 && QP >= 1, "layout");
-  constexpr int SW = 8 / WAVES;              // 16 x 16 score tiles per wave (8 per key block)
+  constexpr int SW = 8 / WAVES;                    // 16 x 16 score tiles per wave (8 per key block)
+  constexpr int XCH = kTile * DV * 2 / 1024;       // 1-KiB chunks of an X tile
+  constexpr int KCH = kTile * 256 * 2 / 1024;      // ... of a K block (dk <= 256)
+  constexpr int XI = XCH / WAVES, KI = KCH / WAVES;  // chunks copied per wave
+  constexpr int GPR = DV / 8;                      // 16-byte granules per X row
+  constexpr int QP = kRows * 256 / 8 / NT;         // 16-byte pieces per thread of the Q block
+  static_assert(XI >= 1 && KI >= 1 && QP >= 1 && XCH % WAVES == 0 && KCH % WAVES == 0, "layout");
+  static_assert((GPR >= 16 && 64 % GPR == 0) || GPR % 64 == 0, "X rows");
   __shared__ __attribute__((aligned(16))) uint16_t sQ[kRows * kPitchQ];
-  __shared__ __attribute__((aligned(16))) uint16_t sX[2 * kTile * PX];  // two X buffers; 64 rows of O at the end
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kTile * 256];
-  __shared__ __attribute__((aligned(16))) uint16_t sP[2][kRows * kPitchP];
-  static_assert(sizeof(sK) >= (WAVES + 2) * kRows * sizeof(float), "GroupNorm statistics reuse sK");
+  __shared__ __attribute__((aligned(1024))) uint16_t sX0[kTile * DV];
+  __shared__ __attribute__((aligned(1024))) uint16_t sX1[kTile * DV];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK0[kTile * 256];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK1[kTile * 256];
+  __shared__ __attribute__((aligned(16))) uint16_t sP0[kRows * kPitchP];
+  __shared__ __attribute__((aligned(16))) uint16_t sP1[kRows * kPitchP];
+  static_assert(sizeof(sK0) >= (WAVES + 2) * kRows * sizeof(float), "GroupNorm statistics reuse sK0");
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int l32 = lane & 31;
   const int lk = 8 * (lane >> 5);
+  const int l16 = lane & 15, lk16 = 8 * (lane >> 4);
   const int vcol0 = wave * 32 * NVT;
   const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
   const int64_t bh = blk / a.nqb;
@@ -429,49 +493,57 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
   const uint16_t* vbase = a.v + bh * static_cast<int64_t>(a.N) * DV;
   const uint16_t* rbase = has_state ? a.chunk_states + (bh * a.nchunks + c) * static_cast<int64_t>(dk) * DV : nullptr;
 
-  // Score tiles of this wave: u = wave + WAVES*j (j < SW) of the 8 16 x 16
-  // tiles of a key block, key tile tt = u/4 and query tile qt = u%4.
-  const int l16 = lane & 15, lk16 = 8 * (lane >> 4);
-
-  TileRegs<XP, NT, DV, kTile> rx;
-  auto load_x = [&](int it) {
+  // Copy X tile `it` (zeros past the data) into `dst`.
+  auto copy_x = [&](int it, uint16_t* dst) {
+    const uint16_t* src;
+    int rows;
     if (it < ns) {
-      rx.load(rbase + static_cast<int64_t>(it * kTile) * DV, DV, kTile, DV);
+      src = rbase + static_cast<int64_t>(it * kTile) * DV;
+      rows = kTile;
     } else {
       const int t0 = cs + (it - ns) * kTile;
-      rx.load(vbase + static_cast<int64_t>(t0) * DV, DV, it < ntiles ? min(kTile, a.N - t0) : 0, DV);
+      src = vbase + static_cast<int64_t>(min(t0, a.N)) * DV;
+      rows = it < ntiles ? min(kTile, a.N - t0) : 0;
+    }
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src, rows * DV * 2);
+#pragma unroll
+    for (int m = 0; m < XI; ++m) {
+      const int chunk = wave + WAVES * m;
+      const int flat = chunk * 64 + lane;  // granule index in the tile
+      const int row = flat / GPR, pos = flat % GPR;
+      dma16(r, dst + chunk * 512, (row * GPR + x_pos(row, pos)) * 16);
     }
   };
-  TileRegs<KP, NT, 256, kTile> rk;
-  auto load_k = [&](int kb) {
+  // Copy K block kb (zeros outside the chunk's blocks, past N and past dk) into `dst`.
+  auto copy_k = [&](int kb, uint16_t* dst) {
     const bool ok = kb >= 0 && kb < nkb;
     const int t0 = cs + (ok ? kb : 0) * kTile;
-    rk.load(kbase + static_cast<int64_t>(t0) * dk, dk, ok ? min(kTile, a.N - t0) : 0, dk);
-  };
-  auto store_k = [&](int kb) {
-    uint16_t* dst = sK[kb & 1];
+    const int rows = ok ? min(kTile, a.N - t0) : 0;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(kbase + static_cast<int64_t>(t0) * dk, rows * dk * 2);
 #pragma unroll
-    for (int m = 0; m < KP; ++m) {
-      const int row = rk.row_of(m);
-      *reinterpret_cast<u32x4*>(dst + k_swz(row, rk.col_of(m) >> 3)) = rk.p[m];
+    for (int m = 0; m < KI; ++m) {
+      const int chunk = wave + WAVES * m;
+      const int row = 2 * chunk + (lane >> 5), pos = lane & 31;
+      const int g = pos ^ (row & 15);
+      dma16(r, dst + chunk * 512, g * 8 < dk ? (row * dk + g * 8) * 2 : kOutOfRange);
     }
   };
 
-  // Prologue: Q block into LDS (zero past N and dk), first X tile into LDS and
-  // the second into registers; the K block of the first scores into LDS and
-  // the next into registers.
+  // Prologue: Q block into LDS through registers (zero past N and dk); the K
+  // block of the first scores and, when the first step is a tile, X_0.
   const int i0 = min(0, ns - 1);
   {
     TileRegs<QP, NT, 256> rq;
     rq.load(a.q + (bh * a.N + q0) * static_cast<int64_t>(dk), dk, qvalid, dk);
-    load_x(0);
-    load_k(i0 + 1 - ns);
+    if (i0 == 0) {
+      copy_k(1 - ns, sK0);
+      copy_x(0, sX0);
+    } else {
+      copy_k(0, sK1);
+    }
     rq.store(sQ, kPitchQ);
-    rx.store(sX, PX);
-    store_k(i0 + 1 - ns);
   }
-  load_x(1);
-  load_k(i0 + 2 - ns);
+  wait_vmem();
   __syncthreads();
   // Query rows of this wave's score tiles as 16x16x32 B operands (zero past dk).
   bf16x8 qf[SW][8];
@@ -488,25 +560,30 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
 #pragma unroll
     for (int nt = 0; nt < NVT; ++nt) acc[qt][nt] = floatx16{};
 
-  // Scores of key block kb: this wave's 16 x 16 tiles of S^T = K Q^T, decayed
-  // and masked, as bf16 into sP.
-  auto scores = [&](int kb) {
-    if (kb < 0 || kb >= nkb) return;
+  // Scores of key block kb from K block `kt`: this wave's 16 x 16 tiles of
+  // S^T = K Q^T, decayed and masked, as bf16 into `pdst`. Blocks outside
+  // 0..nkb-1 (zero K rows) write zeros into a buffer nobody reads before it is
+  // rewritten. The dk sum runs in four accumulators so the MFMAs need not wait
+  // for each other.
+  auto score_reads = [&](const uint16_t* kt, bf16x8 (&kfr)[SW][8]) {
+#pragma unroll
+    for (int j = 0; j < SW; ++j) {
+      const int tt = (wave + WAVES * j) >> 2;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) kfr[j][s] = ld8(kt + k_swz(tt * 16 + l16, 4 * s + (lane >> 4)));
+    }
+  };
+  auto scores = [&](int kb, const bf16x8 (&kfr)[SW][8], uint16_t* pdst) {
     const int t0 = cs + kb * kTile;
-    const uint16_t* kt = sK[kb & 1];
 #pragma unroll
     for (int j = 0; j < SW; ++j) {
       const int u = wave + WAVES * j;
       const int qt = u & 3, tt = u >> 2;
-      floatx4 sacc = floatx4{};
-      if (t0 + tt * 16 <= q0 + qt * 16 + 15) {  // else every key follows every query of the tile
+      floatx4 sacc[4] = {};
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const bf16x8 kfr = ld8(kt + k_swz(tt * 16 + l16, 4 * s + (lane >> 4)));
-          sacc = mfma16(kfr, qf[j][s], sacc);  // zero columns past dk
-        }
-      }
-      // sacc[r] = S^T[t][q]: t = tt*16 + 4*(lane/16) + r, q = qt*16 + lane%16.
+      for (int s = 0; s < 8; ++s) sacc[s & 3] = mfma16(kfr[j][s], qf[j][s], sacc[s & 3]);  // zero past dk
+      const floatx4 sum = (sacc[0] + sacc[1]) + (sacc[2] + sacc[3]);
+      // sum[r] = S^T[t][q]: t = tt*16 + 4*(lane/16) + r, q = qt*16 + lane%16.
       const int ql = qt * 16 + l16;
       const int tl = tt * 16 + 4 * (lane >> 4);
       const int d0 = q0 + ql - (t0 + tl);
@@ -514,86 +591,102 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int d = d0 - r;
-        x[r] = d >= 0 ? sacc[r] * gpow(lg, static_cast<float>(d)) : 0.f;
+        const float e = gpow(lg, static_cast<float>(max(d, 0)));
+        x[r] = d >= 0 ? sum[r] * e : 0.f;
       }
       uint2 w;
       w.x = pack_bf16x2(x[0], x[1]);
       w.y = pack_bf16x2(x[2], x[3]);
-      *reinterpret_cast<uint2*>(sP[kb & 1] + ql * kPitchP + tl) = w;
+      *reinterpret_cast<uint2*>(pdst + ql * kPitchP + tl) = w;
     }
   };
 
-  // Tile i multiplies X_i and forms the scores of key block i+1-ns; with no
-  // state slice the first key block's scores are formed before the first tile.
-  for (int i = i0; i < 0; ++i) {
-    store_k(i + 2 - ns);
-    load_k(i + 3 - ns);
-    scores(i + 1 - ns);
-    __syncthreads();
-  }
-  for (int i = 0; i < ntiles; ++i) {
-    rx.store(sX + ((i + 1) & 1) * kTile * PX, PX);
-    store_k(i + 2 - ns);
-    load_x(i + 2);
-    load_k(i + 3 - ns);
-    scores(i + 1 - ns);
-
-    {
-      // O += A X over the tile's 32 rows.
-      const bool slice = i < ns;
-      const uint16_t* abase = slice ? sQ + i * kTile : sP[(i - ns) & 1];
-      const int apitch = slice ? kPitchQ : kPitchP;
-      const uint16_t* xb = sX + (i & 1) * kTile * PX;
-      auto multiply = [&](auto skip_tile0) {
+  // Step i (buffer parity PAR = i & 1): read the LDS operands of tile i and of
+  // the scores of key block i+1-ns; start the copies of X_{i+1} and of the K
+  // block of step i+1's scores into the other buffers (after the reads, so no
+  // read has to wait for them); O += A X_i; the scores; wait for the copies;
+  // barrier.
+  auto step = [&](int i, auto par_tag, auto slice_tag) {
+    constexpr int PAR = decltype(par_tag)::value;
+    constexpr bool kSlice = decltype(slice_tag)::value;
+    uint16_t* xcur = PAR ? sX1 : sX0;
+    uint16_t* xnext = PAR ? sX0 : sX1;
+    uint16_t* kcur = PAR ? sK1 : sK0;
+    uint16_t* knext = PAR ? sK0 : sK1;
+    uint16_t* pcur = PAR ? sP1 : sP0;
+    uint16_t* pnext = PAR ? sP0 : sP1;
+    bf16x8 av[2][2], bv[2][NVT];
+    if (i >= 0) {
+      const uint16_t* abase = kSlice ? sQ + i * kTile : pcur;
+      constexpr int apitch = kSlice ? kPitchQ : kPitchP;
 #pragma unroll
-        for (int s = 0; s < kTile / 16; ++s) {
-          bf16x8 av[2];
+      for (int s = 0; s < 2; ++s) {
 #pragma unroll
-          for (int qt = 0; qt < 2; ++qt) av[qt] = ld8(abase + (qt * 32 + l32) * apitch + 16 * s + lk);
+        for (int qt = 0; qt < 2; ++qt) av[s][qt] = ld8(abase + (qt * 32 + l32) * apitch + 16 * s + lk);
 #pragma unroll
-          for (int nt = 0; nt < NVT; ++nt) {
-            const bf16x8 b = ld_tr8(xb, PX, 16 * s, vcol0 + 32 * nt, lane);
-            if constexpr (!decltype(skip_tile0)::value) acc[0][nt] = mfma32(av[0], b, acc[0][nt]);
-            acc[1][nt] = mfma32(av[1], b, acc[1][nt]);
-          }
-        }
-      };
-      // Keys of this block all follow query tile 0: its scores are zero.
-      if (!slice && cs + (i - ns) * kTile > q0 + 31) multiply(std::true_type{});
-      else multiply(std::false_type{});
-      if (i == ns - 1) {
-        // Scale chunk-local row j by xi_j = gamma^(j+1).
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = q0 + qt * 32 + acc_row(r, lane) - cs;
-            const float xi = gpow(lg, static_cast<float>(j + 1));
-#pragma unroll
-            for (int nt = 0; nt < NVT; ++nt) acc[qt][nt][r] *= xi;
-          }
+        for (int nt = 0; nt < NVT; ++nt) bv[s][nt] = ld_tr8_x<DV>(xcur, 16 * s, vcol0 + 32 * nt, lane);
       }
     }
+    bf16x8 kfr[SW][8];
+    score_reads(kcur, kfr);
+    __builtin_amdgcn_sched_barrier(0);
+    copy_x(i + 1, xnext);
+    copy_k(i + 2 - ns, knext);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i >= 0) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int nt = 0; nt < NVT; ++nt) {
+          acc[0][nt] = mfma32(av[s][0], bv[s][nt], acc[0][nt]);
+          acc[1][nt] = mfma32(av[s][1], bv[s][nt], acc[1][nt]);
+        }
+    }
+    scores(i + 1 - ns, kfr, pnext);
+    wait_vmem();
     __syncthreads();
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  // Steps begin..end-1 as straight-line even/odd pairs (the buffer parity is
+  // a compile-time constant in each).
+  auto run = [&](int begin, int end, auto slice_tag) {
+    int i = begin;
+    if (i < end && (i & 1)) step(i++, P1{}, slice_tag);
+    for (; i + 1 < end; i += 2) {
+      step(i, P0{}, slice_tag);
+      step(i + 1, P1{}, slice_tag);
+    }
+    if (i < end) step(i, P0{}, slice_tag);
+  };
+
+  // With no state slice the first key block's scores are formed in a step of
+  // its own (i = -1) before the first tile.
+  if (i0 < 0) step(-1, P1{}, std::false_type{});
+  run(0, ns, std::true_type{});
+  if (ns > 0) {
+    // Scale chunk-local row j of the read-out by xi_j = gamma^(j+1).
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = q0 + qt * 32 + acc_row(r, lane) - cs;
+        const float xi = gpow(lg, static_cast<float>(j + 1));
+#pragma unroll
+        for (int nt = 0; nt < NVT; ++nt) acc[qt][nt][r] *= xi;
+      }
   }
+  run(ns, ntiles, std::false_type{});
 
   // Epilogue: optional per-head GroupNorm over the DV columns of each row, then
   // the bf16 store.
   if (gn.enabled) {
-    float* s_stat = reinterpret_cast<float*>(&sK[0][0]);  // [WAVES][64], then mean[64], rstd[64]
+    float* s_stat = reinterpret_cast<float*>(sK0);  // [WAVES][64], then mean[64], rstd[64]
     float* s_mean = s_stat + WAVES * kRows;
     float* s_rstd = s_mean + kRows;
-    // Each lane holds 32 row slots (query tile qt, accumulator r). A
-    // reduce-scatter butterfly over the 32 lanes sharing them leaves lane l
-    // with the wave's sum for slot l%32; one thread per row then adds the waves.
-    auto reduce_rows = [&](float (&x)[32]) {
-      butterfly_level<16>(x, lane);
-      butterfly_level<8>(x, lane);
-      butterfly_level<4>(x, lane);
-      butterfly_level<2>(x, lane);
-      butterfly_level<1>(x, lane);
-      return x[0];
-    };
+    // Each lane holds 32 row slots (query tile qt, accumulator r); a
+    // reduce-scatter over the 32 lanes sharing them leaves lane l with the
+    // wave's sum for slot l%32; one thread per row then adds the waves.
     const int my_slot = lane & 31;
     const int my_row = (my_slot >> 4) * 32 + acc_row(my_slot & 15, lane);
 #pragma unroll
@@ -612,7 +705,7 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
           }
           x[qt * 16 + r] = t;
         }
-      s_stat[wave * kRows + my_row] = reduce_rows(x);
+      s_stat[wave * kRows + my_row] = reduce_scatter32(x, lane);
       __syncthreads();
       if (threadIdx.x < kRows) {
         float t = 0.f;
@@ -642,24 +735,27 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
       }
   }
 
-  // Store: stage the bf16 block in LDS (the X buffers), then write each row
-  // with 16-byte stores.
+  // Store: stage the bf16 block in LDS (rows 0-31 in sX0, 32-63 in sX1), then
+  // write each row with 16-byte stores.
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
+  for (int qt = 0; qt < 2; ++qt) {
+    uint16_t* stage = qt ? sX1 : sX0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = qt * 32 + acc_row(r, lane);
+      const int row = acc_row(r, lane);
 #pragma unroll
-      for (int nt = 0; nt < NVT; ++nt) sX[row * PX + vcol0 + nt * 32 + l32] = f32_to_bf16(acc[qt][nt][r]);
+      for (int nt = 0; nt < NVT; ++nt) stage[row * DV + vcol0 + nt * 32 + l32] = f32_to_bf16(acc[qt][nt][r]);
     }
+  }
   __syncthreads();
   uint16_t* obase = a.o + (bh * a.N + q0) * static_cast<int64_t>(DV);
   constexpr int per_row = DV / 8;
   for (int i = threadIdx.x; i < kRows * per_row; i += NT) {
     const int row = i / per_row, c8 = i - row * per_row;
+    const uint16_t* stage = row < kTile ? sX0 : sX1;
     if (row < qvalid)
       *reinterpret_cast<u32x4*>(obase + static_cast<int64_t>(row) * DV + c8 * 8) =
-          *reinterpret_cast<const u32x4*>(sX + row * PX + c8 * 8);
+          *reinterpret_cast<const u32x4*>(stage + (row & (kTile - 1)) * DV + c8 * 8);
   }
 }
 
