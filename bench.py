@@ -11,11 +11,17 @@ Also timed: the recurrent decode step from the prefill's final state
 (fp32 [8,16,256,512]), 1024 single-token steps back to back.
 
 Prints ONE JSON line. `value` is prefill tokens/s (B*N tokens per step).
-`roofline` is that of the chunkwise call's dominant work on the matrix cores:
-algorithmic flops (918,272 per token-head at chunk 512) over the measured
-time, against the 2.5 PFLOP/s dense bf16 peak. `decode` carries the decode
-step's latency and its HBM roofline (134,610,944 algorithmic bytes per step
-against 8 TB/s). `cpu_baseline` is the fp64 CPU oracle on a bounded sample.
+`roofline` is that of the dominant kernel, the output stage: its arithmetic
+intensity (algorithmic flops over algorithmic HBM bytes, about 185 flop/B) is
+below MI355X's ridge point (2.5 PFLOP/s / 8 TB/s = 312.5 flop/B), so its
+binding roof is HBM: achieved = algorithmic bytes per launch (Q, K, V, the
+bf16 chunk states it reads, O) over the launch time measured with HIP events,
+against 8 TB/s. The same object also gives the matrix-core view (algorithmic
+flops over time against the 2.5 PFLOP/s dense bf16 peak). `step_roofline`
+does the same for the whole step (both stages), `state_walk` for the first
+stage. `decode` carries the decode step's latency and its HBM roofline
+(134,610,944 algorithmic bytes per step against 8 TB/s). `cpu_baseline` is
+the fp64 CPU oracle on a bounded sample.
 """
 
 from __future__ import annotations
@@ -51,6 +57,22 @@ def algorithmic_flops(B, H, N, chunk, dk=DK, dv=DV):
 def output_flops(B, H, N, chunk, dk=DK, dv=DV):
     """The output stage's share: intra-chunk causal half plus the cross-chunk read-out."""
     return float((chunk + 1) * (dk + dv) + 2 * dk * dv) * B * H * N
+
+
+def output_bytes(B, H, N, chunk, dk=DK, dv=DV, state_in=False):
+    """HBM bytes the output stage must move: bf16 Q, K, V and O, plus the bf16
+    state carried into every chunk that has one (all but the first without
+    state_in)."""
+    nchunks = -(-N // chunk)
+    states = nchunks if state_in else nchunks - 1
+    return float(B * H * N * (2 * dk + 2 * dv) * 2 + B * H * states * dk * dv * 2)
+
+
+def walk_bytes(B, H, N, chunk, dk=DK, dv=DV):
+    """HBM bytes of the state stage: bf16 K and V read, the bf16 state of every
+    chunk written, the fp32 final state written."""
+    nchunks = -(-N // chunk)
+    return float(B * H * N * (dk + dv) * 2 + B * H * nchunks * dk * dv * 2 + B * H * dk * dv * 4)
 
 
 def decode_bytes(B, H, dk=DK, dv=DV):
@@ -210,6 +232,8 @@ def main():
     achieved = flops / (ms * 1e-3)
     flops_out = output_flops(B, H, N, CHUNK)
     flops_walk = flops - flops_out
+    bytes_out = output_bytes(B, H, N, CHUNK)
+    bytes_walk = walk_bytes(B, H, N, CHUNK)
 
     # Decode: single-token steps from the prefill's state.
     if args.skip_decode:
@@ -260,29 +284,41 @@ def main():
             "gamma": "1 - 2^(-5-h)", "parallelism": "single GPU",
         },
         "roofline": {
-            "bound": "mfma",
-            "achieved": flops_out / (out_ms * 1e-3) / 1e12,
-            "peak": PEAK_BF16 / 1e12,
-            "unit": "TFLOP/s",
-            "frac": flops_out / (out_ms * 1e-3) / PEAK_BF16,
+            "bound": "hbm",
+            "achieved": bytes_out / (out_ms * 1e-3) / 1e9,
+            "peak": PEAK_HBM / 1e9,
+            "unit": "GB/s",
+            "frac": bytes_out / (out_ms * 1e-3) / PEAK_HBM,
             "traffic": traffic["chunk_out"],
             "kernel": "mfma_chunk_out_kernel (retention_chunk_output: intra-chunk products, read-out, GroupNorm)",
+            "algorithmic_bytes_per_launch": bytes_out,
             "algorithmic_flop_per_launch": flops_out,
+            "arithmetic_intensity_flop_per_byte": flops_out / bytes_out,
+            "ridge_flop_per_byte": PEAK_BF16 / PEAK_HBM,
+            "mfma_tflops": flops_out / (out_ms * 1e-3) / 1e12,
+            "mfma_frac": flops_out / (out_ms * 1e-3) / PEAK_BF16,
             "launch_ms": out_ms,
         },
         "step_roofline": {
-            "bound": "mfma",
-            "achieved": achieved / 1e12,
-            "peak": PEAK_BF16 / 1e12,
-            "unit": "TFLOP/s",
-            "frac": achieved / PEAK_BF16,
+            "bound": "hbm",
+            "achieved": (bytes_out + bytes_walk) / (ms * 1e-3) / 1e9,
+            "peak": PEAK_HBM / 1e9,
+            "unit": "GB/s",
+            "frac": (bytes_out + bytes_walk) / (ms * 1e-3) / PEAK_HBM,
+            "algorithmic_bytes_per_step": bytes_out + bytes_walk,
             "algorithmic_flop_per_step": flops,
+            "mfma_tflops": achieved / 1e12,
+            "mfma_frac": achieved / PEAK_BF16,
         },
         "state_walk": {
             "kernel": "mfma_state_walk_kernel (retention_chunk_states: chunk-state carry)",
             "launch_ms": walk_ms,
+            "bound": "hbm",
+            "algorithmic_bytes_per_launch": bytes_walk,
+            "achieved_gbps": bytes_walk / (walk_ms * 1e-3) / 1e9,
+            "frac": bytes_walk / (walk_ms * 1e-3) / PEAK_HBM,
             "algorithmic_flop_per_launch": flops_walk,
-            "achieved_tflops": flops_walk / (walk_ms * 1e-3) / 1e12,
+            "mfma_tflops": flops_walk / (walk_ms * 1e-3) / 1e12,
             "traffic": traffic["state_walk"],
         },
         "decode": {

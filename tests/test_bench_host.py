@@ -37,3 +37,16 @@ def test_measured_traffic_is_keyed_by_kernel_source():
     assert set(t) == {"chunk_out", "state_walk", "decode_step"}
     for v in t.values():
         assert v is None or v > 0
+
+
+def test_output_and_walk_bytes():
+    # Output stage: bf16 Q, K (dk) and V, O (dv) per token-head, plus the bf16
+    # dk x dv state of every chunk but the first (no state_in).
+    per_tok = (2 * 256 + 2 * 512) * 2
+    states = 8 * 16 * 15 * 256 * 512 * 2
+    assert bench.output_bytes(8, 16, 8192, 512) == 8 * 16 * 8192 * per_tok + states
+    assert bench.output_bytes(8, 16, 8192, 512, state_in=True) == 8 * 16 * 8192 * per_tok + states * 16 // 15
+    # State stage: K, V read; the bf16 state of all 16 chunks and the fp32 final state written.
+    assert bench.walk_bytes(8, 16, 8192, 512) == 8 * 16 * 8192 * 768 * 2 + 8 * 16 * 16 * 256 * 512 * 2 + 8 * 16 * 256 * 512 * 4
+    # Both stages sit below the ridge point of 2.5 PFLOP/s over 8 TB/s.
+    assert bench.output_flops(8, 16, 8192, 512) / bench.output_bytes(8, 16, 8192, 512) < bench.PEAK_BF16 / bench.PEAK_HBM
