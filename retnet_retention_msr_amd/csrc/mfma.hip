@@ -162,6 +162,9 @@ struct TileRegs {
   }
 };
 
+// Wait until this wave's global loads (including the direct LDS copies) are done.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
 // gamma^e through the hardware exp2 (results below the normal range flush to 0).
 __device__ __forceinline__ float gpow(float log2g, float e) { return __builtin_amdgcn_exp2f(e * log2g); }
 
@@ -237,6 +240,11 @@ __global__ void __launch_bounds__(kThreads) mfma_state_walk_kernel(WalkArgs a, H
           acc[mt][r] = fmaf(f, U[static_cast<int64_t>(k0 + mt * 32 + acc_row(r, lane)) * a.dv + vcol], acc[mt][r]);
     }
   }
+
+  // The state came in through loads straight into the accumulators; finish
+  // them here so no later MFMA has to wait on the vector-memory counter for
+  // them (the compiler cannot tell that the first tile's wait covers them).
+  wait_vmem();
 
   const uint16_t* kb = a.k + bh * static_cast<int64_t>(a.N) * a.dk + k0;
   const uint16_t* vb = a.v + bh * static_cast<int64_t>(a.N) * a.dv + v0;
@@ -341,6 +349,240 @@ __global__ void __launch_bounds__(kThreads) mfma_state_walk_kernel(WalkArgs a, H
 }
 
 // ---------------------------------------------------------------------------
+// State walk, full-dk form (dk = 128 or 256)
+// ---------------------------------------------------------------------------
+// One workgroup of eight waves per (head, 128-column v tile, segment) owns the
+// whole dk x 128 slab of R: wave (kw, vw) keeps rows 32*MTW*kw.. and columns
+// 64*vw.. (MTW x 2 accumulator tiles), so each V row is read once and each K
+// row once per v tile. 64-key blocks are double-buffered in LDS (register
+// staging, zeta applied to V rows on the way), one barrier per block.
+constexpr int kWalk2Threads = 512;
+constexpr int kWalk2VT = 128;      // v columns per workgroup
+constexpr int kWalk2PV = 160;      // sV pitch: 320 B, rows 64 B apart mod 256
+constexpr int kWalk2PP = 36;       // store patch pitch: 72 B, 32 rows start on distinct bank pairs
+
+__device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, int byte_offset, const bf16x8& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_offset, 0, 0);
+}
+
+template <int MTW>
+__global__ void __launch_bounds__(kWalk2Threads) mfma_state_walk2_kernel(WalkArgs a, HeadDecay decay) {
+  constexpr int NT = kWalk2Threads;
+  constexpr int DK = 128 * MTW;
+  constexpr int PK = DK + 32;                  // sK pitch: rows 64 B apart mod 256
+  constexpr int KP = kRows * DK / 8 / NT;      // 16-byte pieces per thread of a K block
+  constexpr int VP = kRows * kWalk2VT / 8 / NT;  // ... of a V block
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kRows * PK];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kRows * kWalk2PV];
+  __shared__ __attribute__((aligned(16))) uint16_t sPatch[8][32 * kWalk2PP];  // per-wave store patch
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int kw = wave & 3, vw = wave >> 2;
+  const int nseg_launch = (a.mode == 0) ? a.nseg - 1 : a.nseg;
+  int idx = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int vt = idx % a.nvt;
+  idx /= a.nvt;
+  const int seg = idx % nseg_launch;
+  const int64_t bh = idx / nseg_launch;
+  const int h = static_cast<int>(bh % a.H);
+  const float lg = decay.log2g[h];
+  const int v0 = vt * kWalk2VT;
+  const int krow0 = kw * 32 * MTW;                 // this wave's first state row
+  const int vcol = v0 + vw * 64 + (lane & 31);     // state column of accumulator tile 0
+  const int c_begin = seg * a.chunks_per_seg;
+  const int c_end = min(a.nchunks, c_begin + a.chunks_per_seg);
+  const int64_t dkdv = static_cast<int64_t>(DK) * a.dv;
+
+  floatx16 acc[MTW][2];
+#pragma unroll
+  for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = floatx16{};
+
+  auto state_at = [&](const float* S, int mt, int nt, int r) -> float {
+    return S[static_cast<int64_t>(krow0 + mt * 32 + acc_row(r, lane)) * a.dv + vcol + 32 * nt];
+  };
+  if (seg == 0 && a.state_in) {
+    // Segment 0 starts from state_in (in both modes, so U_0 carries its decayed share).
+    const float* S0 = a.state_in + bh * dkdv;
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mt][nt][r] = state_at(S0, mt, nt, r);
+  } else if (a.mode == 1) {
+    // True state at a later segment's start p: sum over earlier segments s' of
+    // gamma^(p - end_s') U_s', where U_0 already includes state_in.
+    const int p = c_begin * a.chunk;
+    for (int s = 0; s < seg; ++s) {
+      const int end_s = (s + 1) * a.chunks_per_seg * a.chunk;
+      const float f = gpow(lg, static_cast<float>(p - end_s));
+      const float* U = a.seg_states + (bh * a.nseg + s) * dkdv;
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[mt][nt][r] = fmaf(f, state_at(U, mt, nt, r), acc[mt][nt][r]);
+    }
+  }
+
+  // The state came in through loads straight into the accumulators; finish
+  // them here so no later MFMA has to wait on the vector-memory counter for
+  // them (the compiler cannot tell that the first block's wait covers them).
+  wait_vmem();
+
+  const uint16_t* kb = a.k + bh * static_cast<int64_t>(a.N) * DK;
+  const uint16_t* vb = a.v + bh * static_cast<int64_t>(a.N) * a.dv + v0;
+  TileRegs<KP, NT, DK> rk;
+  TileRegs<VP, NT, kWalk2VT> rv;
+  // zeta_t = gamma^(L-1-t) = gamma^(L-1-t0) * gamma^(-r) for row r of a block
+  // at t0; the gamma^(-r) factors of this thread's V rows are fixed.
+  float zrow[VP];
+#pragma unroll
+  for (int m = 0; m < VP; ++m) zrow[m] = gpow(lg, -static_cast<float>(TileRegs<VP, NT, kWalk2VT>::row_of(m)));
+
+  // Blocks are (chunk, 64-row block) pairs in sequence order; `load` fetches
+  // block (c, t0) into registers, `put` stores it scaled into LDS buffer b.
+  auto load = [&](int c, int t0) {
+    const int cs = c * a.chunk;
+    const int L = min(a.chunk, a.N - cs);
+    const int nvalid = min(kRows, L - t0);
+    rk.load(kb + static_cast<int64_t>(cs + t0) * DK, DK, nvalid, DK);
+    rv.load(vb + static_cast<int64_t>(cs + t0) * a.dv, a.dv, nvalid, kWalk2VT);
+  };
+  auto put = [&](int c, int t0, int b) {
+    const int L = min(a.chunk, a.N - c * a.chunk);
+    const float z0 = gpow(lg, static_cast<float>(L - 1 - t0));
+    float z[VP];
+#pragma unroll
+    for (int m = 0; m < VP; ++m) z[m] = z0 * zrow[m];
+    rk.store(sK[b], PK);
+    rv.store_scaled(sV[b], kWalk2PV, z);
+  };
+  auto advance = [&](int& c, int& t0) {
+    t0 += kRows;
+    if (t0 >= min(a.chunk, a.N - c * a.chunk)) {
+      ++c;
+      t0 = 0;
+    }
+  };
+
+  int c = c_begin, t0 = 0;       // block being multiplied
+  int nc = c, nt0 = t0;          // block in the registers
+  if (c < c_end) {
+    load(c, t0);
+    put(c, t0, 0);
+    advance(nc, nt0);
+    if (nc < c_end) load(nc, nt0);
+  }
+  __syncthreads();
+  int buf = 0;
+  while (c < c_end) {
+    if (t0 == 0) {
+      const int L = min(a.chunk, a.N - c * a.chunk);
+      if (a.mode == 1) {
+        // Store R_{c-1} as bf16 ([k][v], v fastest). Each 32x32 accumulator tile
+        // goes through this wave's LDS patch, stored transposed (a lane's four
+        // consecutive rows of one column in one 8-byte write), and comes back
+        // with the transposed LDS read as eight consecutive v columns of one k
+        // row per lane: two 16-byte stores per lane and tile.
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(a.chunk_states + (bh * a.nchunks + c) * dkdv, static_cast<int>(dkdv * 2));
+        uint16_t* patch = sPatch[wave];
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              uint2 w;
+              w.x = pack_bf16x2(acc[mt][nt][4 * g], acc[mt][nt][4 * g + 1]);
+              w.y = pack_bf16x2(acc[mt][nt][4 * g + 2], acc[mt][nt][4 * g + 3]);
+              *reinterpret_cast<uint2*>(patch + (lane & 31) * kWalk2PP + 8 * g + 4 * (lane >> 5)) = w;
+            }
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const bf16x8 v8 = ld_tr8(patch, kWalk2PP, 16 * half, 0, lane);
+              const int row = krow0 + mt * 32 + (lane & 31);
+              const int col = v0 + vw * 64 + nt * 32 + 16 * half + 8 * (lane >> 5);
+              buffer_store16(rs, (row * a.dv + col) * 2, v8);
+            }
+          }
+      }
+      const float carry = gpow(lg, static_cast<float>(L));
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] *= carry;
+    }
+    // U += K^T (zeta V) over the block's 64 keys.
+    auto multiply = [&]() {
+      const uint16_t* kt = sK[buf];
+      const uint16_t* vt_ = sV[buf];
+#pragma unroll
+      for (int s = 0; s < kRows / 16; ++s) {
+        bf16x8 bv[2], av[MTW];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) bv[nt] = ld_tr8(vt_, kWalk2PV, s * 16, vw * 64 + 32 * nt, lane);
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt) av[mt] = ld_tr8(kt, PK, s * 16, krow0 + mt * 32, lane);
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32(av[mt], bv[nt], acc[mt][nt]);
+      }
+    };
+    // The next block goes into the other buffer (read one block ago), the
+    // one after into the registers.
+    auto stage = [&]() {
+      if (nc < c_end) {
+        put(nc, nt0, buf ^ 1);
+        int fc = nc, ft0 = nt0;
+        advance(fc, ft0);
+        if (fc < c_end) load(fc, ft0);
+      }
+    };
+    // The two waves on each SIMD take the two halves in opposite order, so
+    // one's matrix work overlaps the other's staging.
+    if (wave < 4) {
+      multiply();
+      stage();
+    } else {
+      stage();
+      multiply();
+    }
+    __syncthreads();
+    c = nc;
+    t0 = nt0;
+    advance(nc, nt0);
+    buf ^= 1;
+  }
+
+  // Mode 0 stores the segment's end state. Mode 1 stores the final state: to
+  // state_out when there is one segment, else into the spare last segment slot
+  // (the host copies it to state_out afterwards, so state_out may alias
+  // state_in while other segments still read it).
+  float* out = nullptr;
+  if (a.mode == 0) out = a.seg_states + (bh * a.nseg + seg) * dkdv;
+  else if (seg == a.nseg - 1) {
+    if (a.nseg > 1) out = a.seg_states + (bh * a.nseg + seg) * dkdv;
+    else if (a.state_out) out = a.state_out + bh * dkdv;
+  }
+  if (out) {
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          out[static_cast<int64_t>(krow0 + mt * 32 + acc_row(r, lane)) * a.dv + vcol + 32 * nt] = acc[mt][nt][r];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Output
 // ---------------------------------------------------------------------------
 constexpr int kTile = 32;      // rows of a staged tile: 32 keys of V, or 32 rows of the chunk state
@@ -424,8 +666,6 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds_ch
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds_chunk), 16, byte_offset, 0, 0, 0);
 }
 
-// Wait until this wave's global loads (including the direct LDS copies) are done.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // One workgroup per (head, 64-row query block); wave w owns value columns
 // [32*NVT*w, 32*NVT*(w+1)) of all 64 rows (2 x NVT accumulator tiles).
@@ -767,7 +1007,13 @@ bool mfma_supports(int dk, int dv) {
 
 int walk_k_tiles(int dk) { return (dk % 64 == 0) ? 2 : 1; }
 
-int walk_tiles_per_head(int dk, int dv) { return (dk / (32 * walk_k_tiles(dk))) * (dv / kWalkVT); }
+// The full-dk walk covers dk = 128 and 256 with one workgroup per 128 v columns.
+bool walk_full_dk(int dk) { return dk == 128 || dk == 256; }
+
+int walk_tiles_per_head(int dk, int dv) {
+  if (walk_full_dk(dk)) return dv / kWalk2VT;
+  return (dk / (32 * walk_k_tiles(dk))) * (dv / kWalkVT);
+}
 
 hipError_t launch_mfma_state_walk(const uint16_t* k, const uint16_t* v, const float* state_in, float* state_out,
                                   uint16_t* chunk_states, float* seg_states, int chunks_per_seg, const Dims& d,
@@ -787,15 +1033,17 @@ hipError_t launch_mfma_state_walk(const uint16_t* k, const uint16_t* v, const fl
   a.nchunks = (d.N + chunk - 1) / chunk;
   a.chunks_per_seg = chunks_per_seg;
   a.nseg = (a.nchunks + chunks_per_seg - 1) / chunks_per_seg;
+  const bool full = walk_full_dk(d.dk);
   const int MT = walk_k_tiles(d.dk);
-  a.nkt = d.dk / (32 * MT);
-  a.nvt = d.dv / kWalkVT;
+  a.nkt = full ? 1 : d.dk / (32 * MT);
+  a.nvt = d.dv / (full ? kWalk2VT : kWalkVT);
   const int64_t per_seg = static_cast<int64_t>(d.B) * d.H * a.nkt * a.nvt;
   for (int mode = (a.nseg > 1 ? 0 : 1); mode <= 1; ++mode) {
     a.mode = mode;
     const int64_t nblocks = per_seg * (mode == 0 ? a.nseg - 1 : a.nseg);
     const dim3 grid(static_cast<unsigned>(nblocks));
-    if (false) {}
+    if (full && d.dk == 256) mfma_state_walk2_kernel<2><<<grid, kWalk2Threads, 0, stream>>>(a, decay);
+    else if (full) mfma_state_walk2_kernel<1><<<grid, kWalk2Threads, 0, stream>>>(a, decay);
     else if (MT == 2) mfma_state_walk_kernel<2><<<grid, kThreads, 0, stream>>>(a, decay);
     else mfma_state_walk_kernel<1><<<grid, kThreads, 0, stream>>>(a, decay);
     const hipError_t e = hipGetLastError();
