@@ -130,6 +130,52 @@ def _cpu_threads():
     return len(os.sched_getaffinity(0)), "unknown"
 
 
+LONG_LENGTHS = (8192, 16384, 32768, 65536)
+LONG_CHUNKS = (64, 128, 256, 512)
+
+
+def long_sequence_sweep(ret, synthetic, dev, reps=5):
+    """Tokens/s of the chunkwise forward (GroupNorm, fp32 state out) for one
+    batch row of 16 heads as the sequence grows (chunk 512), and across chunk
+    sizes at 65,536 tokens. Each point: HIP events around `reps` calls after
+    one warm-up call."""
+    import torch
+
+    H_ = 16
+    gamma = synthetic.head_gammas(H_)
+    gn = ret.GroupNorm(1e-5)
+    q, k, v = synthetic.make_qkv(1, H_, max(LONG_LENGTHS), DK, DV, dtype=torch.bfloat16, seed=SEED + 7)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    del q, k, v
+
+    def run(n, chunk):
+        qs, ks, vs = qd[:, :, :n].contiguous(), kd[:, :, :n].contiguous(), vd[:, :, :n].contiguous()
+        out = torch.empty(1, H_, n, DV, dtype=torch.bfloat16, device=dev)
+        st = torch.empty(1, H_, DK, DV, dtype=torch.float32, device=dev)
+        ws = torch.empty(ret.chunkwise_workspace_bytes(1, H_, n, DK, DV, chunk), dtype=torch.uint8, device=dev)
+        f = lambda: ret.chunkwise(qs, ks, vs, gamma, chunk, state_out=st, gn=gn, out=out, workspace=ws)
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        return {"N": n, "chunk": chunk, "ms": ms, "tokens_per_s": n / (ms * 1e-3)}
+
+    by_length = [run(n, 512) for n in LONG_LENGTHS]
+    by_chunk = [run(max(LONG_LENGTHS), c) for c in LONG_CHUNKS]
+    tps = [r["tokens_per_s"] for r in by_length]
+    return {
+        "workload": "B=1 H=16 dk=256 dv=512 bf16, GroupNorm, fp32 state out",
+        "by_length_chunk512": by_length,
+        "by_chunk_N65536": by_chunk,
+        "flatness_min_over_max": min(tps) / max(tps),
+    }
+
+
 def cpu_baseline(q, k, v, gamma, n_batch_rows=2):
     """The fp64 oracle (as written, untuned) on batch rows 0..n_batch_rows-1 of the prefill."""
     import numpy as np
@@ -169,6 +215,7 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (reference for HBM byte counters)")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-long", action="store_true", help="skip the long-sequence flatness sweep")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -264,6 +311,11 @@ def main():
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(q, k, v, gamma, args.cpu_batch_rows)
 
+    long_seq = None
+    if not args.skip_long:
+        print("[bench] long-sequence sweep", file=sys.stderr, flush=True)
+        long_seq = long_sequence_sweep(ret, synthetic, dev)
+
     traffic = measured_traffic()
     line = {
         "metric": "chunkwise MSR tokens/s @B8 H16 N8k; decode-step µs; % of MFMA/HBM roofline",
@@ -334,6 +386,7 @@ def main():
                 "algorithmic_bytes_per_step": dbytes,
             },
         },
+        "long_sequence": long_seq,
         "cpu_baseline": cpu,
         "wall_s_timed": wall,
     }
