@@ -40,6 +40,9 @@
 //   B[kk][j]: j = l % 32, kk = 8*(l/32) + 0..7
 //   D[i][j] : j = l % 32, i = 8*(r/4) + 4*(l/32) + r%4 for accumulator r = 0..15
 #include <type_traits>
+#include <algorithm>
+#include <atomic>
+#include <cstdint>
 
 #include "kernels.h"
 
@@ -164,6 +167,17 @@ struct TileRegs {
 
 // Wait until this wave's global loads (including the direct LDS copies) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads it
+// does not wait for outstanding global loads and stores (or copies into LDS).
+// The empty asm statements keep the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // gamma^e through the hardware exp2 (results below the normal range flush to 0).
 __device__ __forceinline__ float gpow(float log2g, float e) { return __builtin_amdgcn_exp2f(e * log2g); }
@@ -586,7 +600,6 @@ __global__ void __launch_bounds__(kWalk2Threads) mfma_state_walk2_kernel(WalkArg
 // Output
 // ---------------------------------------------------------------------------
 constexpr int kTile = 32;      // rows of a staged tile: 32 keys of V, or 32 rows of the chunk state
-constexpr int kPitchQ = 264;   // sQ pitch: 528 B, rows an odd number of 16-byte slots apart
 constexpr int kPitchP = 40;    // sP pitch: 80 B, 16 consecutive rows fall on distinct banks
 
 struct OutArgs {
@@ -597,6 +610,7 @@ struct OutArgs {
   uint16_t* o;
   int state_for_chunk0;
   int H, N, dk, dv, chunk, nchunks, nqb;
+  int nblocks;                   // B * H * nqb query blocks
 };
 
 // Reduce-scatter of 32 values over the 32 lanes of each half-wave, in VALU
@@ -667,14 +681,21 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds_ch
 }
 
 
-// One workgroup per (head, 64-row query block); wave w owns value columns
-// [32*NVT*w, 32*NVT*(w+1)) of all 64 rows (2 x NVT accumulator tiles).
+// One workgroup per CU, looping over 64-row query blocks (head, rows q0..q0+63);
+// wave w owns value columns [32*NVT*w, 32*NVT*(w+1)) of all 64 rows (2 x NVT
+// accumulator tiles).
 //
-// The block's work is a sequence of tiles, each a 32-row bf16 matrix X in
-// LDS multiplied into O as O += A X: first the dk/32 slices of the stored
-// chunk state (A = the matching 32 columns of Q, the cross-chunk read-out),
-// then the 32-key blocks of the chunk up to the diagonal (A = the decayed
-// scores of that block, X = its V rows).
+// Block order: the blocks are split into one contiguous range per XCD (so the
+// eight query blocks of a chunk, which read the same K, V and state, meet in
+// one L2), and the workgroups of an XCD take the range in groups of their
+// count, each workgroup one block per group, rotated by one place per group so
+// every workgroup sees every position within a chunk (their work differs).
+//
+// A block's work is a sequence of tiles, each a 32-row bf16 matrix X in LDS
+// multiplied into O as O += A X: first the dk/32 slices of the stored chunk
+// state (A = the matching 32 columns of Q, the cross-chunk read-out), then the
+// 32-key blocks of the chunk up to the diagonal (A = the decayed scores of that
+// block, X = its V rows).
 //
 // Scores of a key block, S^T = K Q^T (32 keys x 64 queries), are formed one
 // tile ahead: wave (tt, qt) computes the 16 x 16 tile of keys 16*tt.. and
@@ -686,64 +707,87 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds_ch
 // loads with an LDS destination) one tile ahead, into the other of two buffer
 // pairs; each tile ends with a wait for those copies and one barrier. The
 // buffers are distinct LDS arrays chosen at compile time per tile parity, so
-// the LDS reads of a tile never wait for the copies in flight.
+// the LDS reads of a tile never wait for the copies in flight. The next
+// block's Q rows and first tiles are requested before the current block's
+// GroupNorm and store, which need no tile buffer.
 template <int NVT, int WAVES>
 __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, HeadDecay decay, GnArgs gn) {
-  constexpr int NT = 64 * WAVES;
   constexpr int DV = WAVES * 32 * NVT;
   constexpr int SW = 8 / WAVES;                    // 16 x 16 score tiles per wave (8 per key block)
   constexpr int XCH = kTile * DV * 2 / 1024;       // 1-KiB chunks of an X tile
   constexpr int KCH = kTile * 256 * 2 / 1024;      // ... of a K block (dk <= 256)
   constexpr int XI = XCH / WAVES, KI = KCH / WAVES;  // chunks copied per wave
   constexpr int GPR = DV / 8;                      // 16-byte granules per X row
-  constexpr int QP = kRows * 256 / 8 / NT;         // 16-byte pieces per thread of the Q block
-  static_assert(XI >= 1 && KI >= 1 && QP >= 1 && XCH % WAVES == 0 && KCH % WAVES == 0, "layout");
+  constexpr int QI = 2 * KCH / WAVES;              // 1-KiB chunks of the Q block copied per wave
+  constexpr int OSTORES = 2 * NVT * 8;             // 4-byte O stores per lane and block
+  static_assert(XI >= 1 && KI >= 1 && QI >= 1 && XCH % WAVES == 0 && KCH % WAVES == 0, "layout");
   static_assert((GPR >= 16 && 64 % GPR == 0) || GPR % 64 == 0, "X rows");
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[kRows * kPitchQ];
+  static_assert(OSTORES <= 48, "O stores must fit the vector-memory counter");
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ[kRows * 256];
   __shared__ __attribute__((aligned(1024))) uint16_t sX0[kTile * DV];
   __shared__ __attribute__((aligned(1024))) uint16_t sX1[kTile * DV];
   __shared__ __attribute__((aligned(1024))) uint16_t sK0[kTile * 256];
   __shared__ __attribute__((aligned(1024))) uint16_t sK1[kTile * 256];
   __shared__ __attribute__((aligned(16))) uint16_t sP0[kRows * kPitchP];
   __shared__ __attribute__((aligned(16))) uint16_t sP1[kRows * kPitchP];
-  static_assert(sizeof(sK0) >= (WAVES + 2) * kRows * sizeof(float), "GroupNorm statistics reuse sK0");
+  static_assert(sizeof(sP0) >= (WAVES + 2) * kRows * sizeof(float), "GroupNorm statistics reuse sP0");
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int l32 = lane & 31;
   const int lk = 8 * (lane >> 5);
-  const int l16 = lane & 15, lk16 = 8 * (lane >> 4);
+  const int l16 = lane & 15;
   const int vcol0 = wave * 32 * NVT;
-  const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int64_t bh = blk / a.nqb;
-  const int qb = blk % a.nqb;
-  const int h = static_cast<int>(bh % a.H);
-  const float lg = decay.log2g[h];
-  const int q0 = qb * kRows;
-  const int c = q0 / a.chunk;
-  const int cs = c * a.chunk;
   const int dk = a.dk;
-  const int qvalid = min(kRows, a.N - q0);
-  const int kend = min(q0 + kRows, a.N);
-  const int nkb = (kend - cs + kTile - 1) / kTile;  // 32-key blocks of the chunk up to the diagonal
-  const bool has_state = a.chunk_states && (c > 0 || a.state_for_chunk0);
-  const int ns = has_state ? dk / kTile : 0;          // state slices (dk is a multiple of 32)
-  const int ntiles = ns + nkb;
-  const uint16_t* kbase = a.k + bh * static_cast<int64_t>(a.N) * dk;
-  const uint16_t* vbase = a.v + bh * static_cast<int64_t>(a.N) * DV;
-  const uint16_t* rbase = has_state ? a.chunk_states + (bh * a.nchunks + c) * static_cast<int64_t>(dk) * DV : nullptr;
 
-  // Copy X tile `it` (zeros past the data) into `dst`.
-  auto copy_x = [&](int it, uint16_t* dst) {
+  // This workgroup's blocks.
+  const int nx = min(kXcds, static_cast<int>(gridDim.x));
+  const int xcd = blockIdx.x % nx, slot = blockIdx.x / nx;
+  const int nwg = (static_cast<int>(gridDim.x) - xcd + nx - 1) / nx;  // workgroups sharing this range
+  const int per = (a.nblocks + nx - 1) / nx;
+  const int lo = min(a.nblocks, xcd * per), hi = min(a.nblocks, lo + per);
+  auto block_of = [&](int it) __attribute__((always_inline)) {
+    const int L = lo + it * nwg + (slot + it) % nwg;
+    return L < hi ? L : -1;
+  };
+
+  // Geometry of one query block.
+  struct Blk {
+    int64_t bh;
+    int h, q0, cs, qvalid, nkb, ns, ntiles;
+    float lg;
+    const uint16_t *kbase, *vbase, *rbase;
+  };
+  auto setup = [&](int L, Blk& b) __attribute__((always_inline)) {
+    b.bh = L / a.nqb;
+    const int qb = L % a.nqb;
+    b.h = static_cast<int>(b.bh % a.H);
+    b.lg = decay.log2g[b.h];
+    b.q0 = qb * kRows;
+    const int c = b.q0 / a.chunk;
+    b.cs = c * a.chunk;
+    b.qvalid = min(kRows, a.N - b.q0);
+    const int kend = min(b.q0 + kRows, a.N);
+    b.nkb = (kend - b.cs + kTile - 1) / kTile;  // 32-key blocks of the chunk up to the diagonal
+    const bool has_state = a.chunk_states && (c > 0 || a.state_for_chunk0);
+    b.ns = has_state ? dk / kTile : 0;          // state slices (dk is a multiple of 32)
+    b.ntiles = b.ns + b.nkb;
+    b.kbase = a.k + b.bh * static_cast<int64_t>(a.N) * dk;
+    b.vbase = a.v + b.bh * static_cast<int64_t>(a.N) * DV;
+    b.rbase = has_state ? a.chunk_states + (b.bh * a.nchunks + c) * static_cast<int64_t>(dk) * DV : nullptr;
+  };
+
+  // Copy X tile `it` of block b (zeros past the data) into `dst`.
+  auto copy_x = [&](const Blk& b, int it, uint16_t* dst) __attribute__((always_inline)) {
     const uint16_t* src;
     int rows;
-    if (it < ns) {
-      src = rbase + static_cast<int64_t>(it * kTile) * DV;
+    if (it < b.ns) {
+      src = b.rbase + static_cast<int64_t>(it * kTile) * DV;
       rows = kTile;
     } else {
-      const int t0 = cs + (it - ns) * kTile;
-      src = vbase + static_cast<int64_t>(min(t0, a.N)) * DV;
-      rows = it < ntiles ? min(kTile, a.N - t0) : 0;
+      const int t0 = b.cs + (it - b.ns) * kTile;
+      src = b.vbase + static_cast<int64_t>(min(t0, a.N)) * DV;
+      rows = it < b.ntiles ? min(kTile, a.N - t0) : 0;
     }
     const __amdgpu_buffer_rsrc_t r = make_rsrc(src, rows * DV * 2);
 #pragma unroll
@@ -754,12 +798,12 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
       dma16(r, dst + chunk * 512, (row * GPR + x_pos(row, pos)) * 16);
     }
   };
-  // Copy K block kb (zeros outside the chunk's blocks, past N and past dk) into `dst`.
-  auto copy_k = [&](int kb, uint16_t* dst) {
-    const bool ok = kb >= 0 && kb < nkb;
-    const int t0 = cs + (ok ? kb : 0) * kTile;
+  // Copy K block kb of block b (zeros outside the chunk's blocks, past N and past dk) into `dst`.
+  auto copy_k = [&](const Blk& b, int kb, uint16_t* dst) __attribute__((always_inline)) {
+    const bool ok = kb >= 0 && kb < b.nkb;
+    const int t0 = b.cs + (ok ? kb : 0) * kTile;
     const int rows = ok ? min(kTile, a.N - t0) : 0;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(kbase + static_cast<int64_t>(t0) * dk, rows * dk * 2);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(b.kbase + static_cast<int64_t>(t0) * dk, rows * dk * 2);
 #pragma unroll
     for (int m = 0; m < KI; ++m) {
       const int chunk = wave + WAVES * m;
@@ -768,234 +812,282 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
       dma16(r, dst + chunk * 512, g * 8 < dk ? (row * dk + g * 8) * 2 : kOutOfRange);
     }
   };
-
-  // Prologue: Q block into LDS through registers (zero past N and dk); the K
-  // block of the first scores and, when the first step is a tile, X_0.
-  const int i0 = min(0, ns - 1);
-  {
-    TileRegs<QP, NT, 256> rq;
-    rq.load(a.q + (bh * a.N + q0) * static_cast<int64_t>(dk), dk, qvalid, dk);
-    if (i0 == 0) {
-      copy_k(1 - ns, sK0);
-      copy_x(0, sX0);
-    } else {
-      copy_k(0, sK1);
+  // Copy the Q rows of block b (zeros past N and past dk) into sQ, laid out as K blocks.
+  auto copy_q = [&](const Blk& b) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(a.q + (b.bh * a.N + b.q0) * static_cast<int64_t>(dk), b.qvalid * dk * 2);
+#pragma unroll
+    for (int m = 0; m < QI; ++m) {
+      const int chunk = wave + WAVES * m;
+      const int row = 2 * chunk + (lane >> 5), pos = lane & 31;
+      const int g = pos ^ (row & 15);
+      dma16(r, sQ + chunk * 512, g * 8 < dk ? (row * dk + g * 8) * 2 : kOutOfRange);
     }
-    rq.store(sQ, kPitchQ);
-  }
+  };
+  // The copies the first step of block b needs: the K block of its first
+  // scores and, when the first step is a tile, X_0.
+  auto first_copies = [&](const Blk& b) __attribute__((always_inline)) {
+    if (b.ns > 0) {
+      copy_k(b, 1 - b.ns, sK0);
+      copy_x(b, 0, sX0);
+    } else {
+      copy_k(b, 0, sK1);
+    }
+  };
+
+  int it = 0;
+  int L = block_of(0);
+  if (L < 0) return;  // no block for this workgroup (uniform)
+  Blk cur;
+  setup(L, cur);
+  copy_q(cur);
+  first_copies(cur);
   wait_vmem();
   __syncthreads();
-  // Query rows of this wave's score tiles as 16x16x32 B operands (zero past dk).
-  bf16x8 qf[SW][8];
-#pragma unroll
-  for (int j = 0; j < SW; ++j) {
-    const int qt = (wave + WAVES * j) & 3;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qf[j][s] = ld8(sQ + (qt * 16 + l16) * kPitchQ + 32 * s + lk16);
-  }
 
-  floatx16 acc[2][NVT];
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-    for (int nt = 0; nt < NVT; ++nt) acc[qt][nt] = floatx16{};
-
-  // Scores of key block kb from K block `kt`: this wave's 16 x 16 tiles of
-  // S^T = K Q^T, decayed and masked, as bf16 into `pdst`. Blocks outside
-  // 0..nkb-1 (zero K rows) write zeros into a buffer nobody reads before it is
-  // rewritten. The dk sum runs in four accumulators so the MFMAs need not wait
-  // for each other.
-  auto score_reads = [&](const uint16_t* kt, bf16x8 (&kfr)[SW][8]) {
+  for (;;) {
+    // Query rows of this wave's score tiles as 16x16x32 B operands (zero past dk).
+    bf16x8 qf[SW][8];
 #pragma unroll
     for (int j = 0; j < SW; ++j) {
-      const int tt = (wave + WAVES * j) >> 2;
+      const int qt = (wave + WAVES * j) & 3;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) kfr[j][s] = ld8(kt + k_swz(tt * 16 + l16, 4 * s + (lane >> 4)));
+      for (int s = 0; s < 8; ++s) qf[j][s] = ld8(sQ + k_swz(qt * 16 + l16, 4 * s + (lane >> 4)));
     }
-  };
-  auto scores = [&](int kb, const bf16x8 (&kfr)[SW][8], uint16_t* pdst) {
-    const int t0 = cs + kb * kTile;
-#pragma unroll
-    for (int j = 0; j < SW; ++j) {
-      const int u = wave + WAVES * j;
-      const int qt = u & 3, tt = u >> 2;
-      floatx4 sacc[4] = {};
-#pragma unroll
-      for (int s = 0; s < 8; ++s) sacc[s & 3] = mfma16(kfr[j][s], qf[j][s], sacc[s & 3]);  // zero past dk
-      const floatx4 sum = (sacc[0] + sacc[1]) + (sacc[2] + sacc[3]);
-      // sum[r] = S^T[t][q]: t = tt*16 + 4*(lane/16) + r, q = qt*16 + lane%16.
-      const int ql = qt * 16 + l16;
-      const int tl = tt * 16 + 4 * (lane >> 4);
-      const int d0 = q0 + ql - (t0 + tl);
-      float x[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int d = d0 - r;
-        const float e = gpow(lg, static_cast<float>(max(d, 0)));
-        x[r] = d >= 0 ? sum[r] * e : 0.f;
-      }
-      uint2 w;
-      w.x = pack_bf16x2(x[0], x[1]);
-      w.y = pack_bf16x2(x[2], x[3]);
-      *reinterpret_cast<uint2*>(pdst + ql * kPitchP + tl) = w;
-    }
-  };
 
-  // Step i (buffer parity PAR = i & 1): read the LDS operands of tile i and of
-  // the scores of key block i+1-ns; start the copies of X_{i+1} and of the K
-  // block of step i+1's scores into the other buffers (after the reads, so no
-  // read has to wait for them); O += A X_i; the scores; wait for the copies;
-  // barrier.
-  auto step = [&](int i, auto par_tag, auto slice_tag) {
-    constexpr int PAR = decltype(par_tag)::value;
-    constexpr bool kSlice = decltype(slice_tag)::value;
-    uint16_t* xcur = PAR ? sX1 : sX0;
-    uint16_t* xnext = PAR ? sX0 : sX1;
-    uint16_t* kcur = PAR ? sK1 : sK0;
-    uint16_t* knext = PAR ? sK0 : sK1;
-    uint16_t* pcur = PAR ? sP1 : sP0;
-    uint16_t* pnext = PAR ? sP0 : sP1;
-    bf16x8 av[2][2], bv[2][NVT];
-    if (i >= 0) {
-      const uint16_t* abase = kSlice ? sQ + i * kTile : pcur;
-      constexpr int apitch = kSlice ? kPitchQ : kPitchP;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) av[s][qt] = ld8(abase + (qt * 32 + l32) * apitch + 16 * s + lk);
-#pragma unroll
-        for (int nt = 0; nt < NVT; ++nt) bv[s][nt] = ld_tr8_x<DV>(xcur, 16 * s, vcol0 + 32 * nt, lane);
-      }
-    }
-    bf16x8 kfr[SW][8];
-    score_reads(kcur, kfr);
-    __builtin_amdgcn_sched_barrier(0);
-    copy_x(i + 1, xnext);
-    copy_k(i + 2 - ns, knext);
-    __builtin_amdgcn_sched_barrier(0);
-    if (i >= 0) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int nt = 0; nt < NVT; ++nt) {
-          acc[0][nt] = mfma32(av[s][0], bv[s][nt], acc[0][nt]);
-          acc[1][nt] = mfma32(av[s][1], bv[s][nt], acc[1][nt]);
-        }
-    }
-    scores(i + 1 - ns, kfr, pnext);
-    wait_vmem();
-    __syncthreads();
-  };
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-  // Steps begin..end-1 as straight-line even/odd pairs (the buffer parity is
-  // a compile-time constant in each).
-  auto run = [&](int begin, int end, auto slice_tag) {
-    int i = begin;
-    if (i < end && (i & 1)) step(i++, P1{}, slice_tag);
-    for (; i + 1 < end; i += 2) {
-      step(i, P0{}, slice_tag);
-      step(i + 1, P1{}, slice_tag);
-    }
-    if (i < end) step(i, P0{}, slice_tag);
-  };
-
-  // With no state slice the first key block's scores are formed in a step of
-  // its own (i = -1) before the first tile.
-  if (i0 < 0) step(-1, P1{}, std::false_type{});
-  run(0, ns, std::true_type{});
-  if (ns > 0) {
-    // Scale chunk-local row j of the read-out by xi_j = gamma^(j+1).
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = q0 + qt * 32 + acc_row(r, lane) - cs;
-        const float xi = gpow(lg, static_cast<float>(j + 1));
-#pragma unroll
-        for (int nt = 0; nt < NVT; ++nt) acc[qt][nt][r] *= xi;
-      }
-  }
-  run(ns, ntiles, std::false_type{});
-
-  // Epilogue: optional per-head GroupNorm over the DV columns of each row, then
-  // the bf16 store.
-  if (gn.enabled) {
-    float* s_stat = reinterpret_cast<float*>(sK0);  // [WAVES][64], then mean[64], rstd[64]
-    float* s_mean = s_stat + WAVES * kRows;
-    float* s_rstd = s_mean + kRows;
-    // Each lane holds 32 row slots (query tile qt, accumulator r); a
-    // reduce-scatter over the 32 lanes sharing them leaves lane l with the
-    // wave's sum for slot l%32; one thread per row then adds the waves.
-    const int my_slot = lane & 31;
-    const int my_row = (my_slot >> 4) * 32 + acc_row(my_slot & 15, lane);
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      float x[32];
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float mean = pass == 0 ? 0.f : s_mean[qt * 32 + acc_row(r, lane)];
-          float t = 0.f;
-#pragma unroll
-          for (int nt = 0; nt < NVT; ++nt) {
-            const float d = acc[qt][nt][r] - mean;
-            t += pass == 0 ? d : d * d;
-          }
-          x[qt * 16 + r] = t;
-        }
-      s_stat[wave * kRows + my_row] = reduce_scatter32(x, lane);
-      __syncthreads();
-      if (threadIdx.x < kRows) {
-        float t = 0.f;
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) t += s_stat[w * kRows + threadIdx.x];
-        t /= DV;
-        if (pass == 0) s_mean[threadIdx.x] = t;
-        else s_rstd[threadIdx.x] = 1.0f / sqrtf(t + gn.eps);
-      }
-      __syncthreads();
-    }
+    // GroupNorm weight and bias of this wave's columns, loaded before the
+    // tiles so that the first tile's wait covers them.
     float w[NVT], bb[NVT];
 #pragma unroll
     for (int nt = 0; nt < NVT; ++nt) {
       const int vcol = vcol0 + nt * 32 + l32;
-      w[nt] = gn.weight ? gn.weight[h * DV + vcol] : 1.f;
-      bb[nt] = gn.bias ? gn.bias[h * DV + vcol] : 0.f;
+      w[nt] = gn.weight ? gn.weight[cur.h * DV + vcol] : 1.f;
+      bb[nt] = gn.bias ? gn.bias[cur.h * DV + vcol] : 0.f;
     }
+
+    floatx16 acc[2][NVT];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = qt * 32 + acc_row(r, lane);
-        const float mean = s_mean[row], rstd = s_rstd[row];
-#pragma unroll
-        for (int nt = 0; nt < NVT; ++nt) acc[qt][nt][r] = (acc[qt][nt][r] - mean) * rstd * w[nt] + bb[nt];
-      }
-  }
+      for (int nt = 0; nt < NVT; ++nt) acc[qt][nt] = floatx16{};
 
-  // Store: stage the bf16 block in LDS (rows 0-31 in sX0, 32-63 in sX1), then
-  // write each row with 16-byte stores.
+    const int ns = cur.ns, ntiles = cur.ntiles;
+
+    // Scores of key block kb from K block `kt`: this wave's 16 x 16 tiles of
+    // S^T = K Q^T, decayed and masked, as bf16 into `pdst`. Blocks outside
+    // 0..nkb-1 (zero K rows) write zeros into a buffer nobody reads before it
+    // is rewritten. The dk sum runs in four accumulators so the MFMAs need not
+    // wait for each other.
+    auto score_reads = [&](const uint16_t* kt, bf16x8 (&kfr)[SW][8]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    uint16_t* stage = qt ? sX1 : sX0;
+      for (int j = 0; j < SW; ++j) {
+        const int tt = (wave + WAVES * j) >> 2;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = acc_row(r, lane);
+        for (int s = 0; s < 8; ++s) kfr[j][s] = ld8(kt + k_swz(tt * 16 + l16, 4 * s + (lane >> 4)));
+      }
+    };
+    auto scores = [&](int kb, const bf16x8 (&kfr)[SW][8], uint16_t* pdst) __attribute__((always_inline)) {
+      const int t0 = cur.cs + kb * kTile;
 #pragma unroll
-      for (int nt = 0; nt < NVT; ++nt) stage[row * DV + vcol0 + nt * 32 + l32] = f32_to_bf16(acc[qt][nt][r]);
+      for (int j = 0; j < SW; ++j) {
+        const int u = wave + WAVES * j;
+        const int qt = u & 3, tt = u >> 2;
+        floatx4 sacc[4] = {};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) sacc[s & 3] = mfma16(kfr[j][s], qf[j][s], sacc[s & 3]);  // zero past dk
+        const floatx4 sum = (sacc[0] + sacc[1]) + (sacc[2] + sacc[3]);
+        // sum[r] = S^T[t][q]: t = tt*16 + 4*(lane/16) + r, q = qt*16 + lane%16.
+        const int ql = qt * 16 + l16;
+        const int tl = tt * 16 + 4 * (lane >> 4);
+        const int d0 = cur.q0 + ql - (t0 + tl);
+        float x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int d = d0 - r;
+          const float e = gpow(cur.lg, static_cast<float>(max(d, 0)));
+          x[r] = d >= 0 ? sum[r] * e : 0.f;
+        }
+        uint2 w;
+        w.x = pack_bf16x2(x[0], x[1]);
+        w.y = pack_bf16x2(x[2], x[3]);
+        *reinterpret_cast<uint2*>(pdst + ql * kPitchP + tl) = w;
+      }
+    };
+
+    // Step i (buffer parity PAR = i & 1): read the LDS operands of tile i and
+    // of the scores of key block i+1-ns; start the copies of X_{i+1} and of
+    // the K block of step i+1's scores into the other buffers (after the
+    // reads, so no read has to wait for them); O += A X_i; the scores; wait
+    // for the copies; barrier.
+    auto step = [&](int i, auto par_tag, auto slice_tag) __attribute__((always_inline)) {
+      constexpr int PAR = decltype(par_tag)::value;
+      constexpr bool kSlice = decltype(slice_tag)::value;
+      uint16_t* xcur = PAR ? sX1 : sX0;
+      uint16_t* xnext = PAR ? sX0 : sX1;
+      uint16_t* kcur = PAR ? sK1 : sK0;
+      uint16_t* knext = PAR ? sK0 : sK1;
+      uint16_t* pcur = PAR ? sP1 : sP0;
+      uint16_t* pnext = PAR ? sP0 : sP1;
+      bf16x8 av[2][2], bv[2][NVT];
+      if (i >= 0) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt)
+            av[s][qt] = kSlice ? ld8(sQ + k_swz(qt * 32 + l32, 4 * i + 2 * s + (lane >> 5)))
+                               : ld8(pcur + (qt * 32 + l32) * kPitchP + 16 * s + lk);
+#pragma unroll
+          for (int nt = 0; nt < NVT; ++nt) bv[s][nt] = ld_tr8_x<DV>(xcur, 16 * s, vcol0 + 32 * nt, lane);
+        }
+      }
+      bf16x8 kfr[SW][8];
+      score_reads(kcur, kfr);
+      __builtin_amdgcn_sched_barrier(0);
+      copy_x(cur, i + 1, xnext);
+      copy_k(cur, i + 2 - ns, knext);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i >= 0) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int nt = 0; nt < NVT; ++nt) {
+            acc[0][nt] = mfma32(av[s][0], bv[s][nt], acc[0][nt]);
+            acc[1][nt] = mfma32(av[s][1], bv[s][nt], acc[1][nt]);
+          }
+      }
+      scores(i + 1 - ns, kfr, pnext);
+      wait_vmem();
+      __syncthreads();
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    // Steps begin..end-1 as straight-line even/odd pairs (the buffer parity is
+    // a compile-time constant in each).
+    auto run = [&](int begin, int end, auto slice_tag) __attribute__((always_inline)) {
+      int i = begin;
+      if (i < end && (i & 1)) step(i++, P1{}, slice_tag);
+      for (; i + 1 < end; i += 2) {
+        step(i, P0{}, slice_tag);
+        step(i + 1, P1{}, slice_tag);
+      }
+      if (i < end) step(i, P0{}, slice_tag);
+    };
+
+    // With no state slice the first key block's scores are formed in a step
+    // of its own (i = -1) before the first tile.
+    if (ns == 0) step(-1, P1{}, std::false_type{});
+    run(0, ns, std::true_type{});
+    if (ns > 0) {
+      // Scale chunk-local row j of the read-out by xi_j = gamma^(j+1).
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = cur.q0 + qt * 32 + acc_row(r, lane) - cur.cs;
+          const float xi = gpow(cur.lg, static_cast<float>(j + 1));
+#pragma unroll
+          for (int nt = 0; nt < NVT; ++nt) acc[qt][nt][r] *= xi;
+        }
     }
-  }
-  __syncthreads();
-  uint16_t* obase = a.o + (bh * a.N + q0) * static_cast<int64_t>(DV);
-  constexpr int per_row = DV / 8;
-  for (int i = threadIdx.x; i < kRows * per_row; i += NT) {
-    const int row = i / per_row, c8 = i - row * per_row;
-    const uint16_t* stage = row < kTile ? sX0 : sX1;
-    if (row < qvalid)
-      *reinterpret_cast<u32x4*>(obase + static_cast<int64_t>(row) * DV + c8 * 8) =
-          *reinterpret_cast<const u32x4*>(stage + (row & (kTile - 1)) * DV + c8 * 8);
+    run(ns, ntiles, std::false_type{});
+
+    // The tile buffers are free now: request the next block's Q rows and
+    // first tiles before this block's GroupNorm and store.
+    // This block's output rows; then the next block takes over `cur`.
+    uint16_t* const oblk = a.o + (cur.bh * a.N + cur.q0) * static_cast<int64_t>(DV);
+    const int oq = cur.qvalid;
+    const int Ln = block_of(++it);
+    if (Ln >= 0) {
+      setup(Ln, cur);
+      copy_q(cur);
+      first_copies(cur);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Optional per-head GroupNorm over the DV columns of each row.
+    if (gn.enabled) {
+      float* s_stat = reinterpret_cast<float*>(sP0);  // [WAVES][64], then mean[64], rstd[64]
+      float* s_mean = s_stat + WAVES * kRows;
+      float* s_rstd = s_mean + kRows;
+      // Each lane holds 32 row slots (query tile qt, accumulator r); a
+      // reduce-scatter over the 32 lanes sharing them leaves lane l with the
+      // wave's sum for slot l%32; one thread per row then adds the waves.
+      const int my_slot = lane & 31;
+      const int my_row = (my_slot >> 4) * 32 + acc_row(my_slot & 15, lane);
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        float x[32];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float mean = pass == 0 ? 0.f : s_mean[qt * 32 + acc_row(r, lane)];
+            float t = 0.f;
+#pragma unroll
+            for (int nt = 0; nt < NVT; ++nt) {
+              const float d = acc[qt][nt][r] - mean;
+              t += pass == 0 ? d : d * d;
+            }
+            x[qt * 16 + r] = t;
+          }
+        s_stat[wave * kRows + my_row] = reduce_scatter32(x, lane);
+        lds_barrier();  // the next block's copies stay in flight
+        if (threadIdx.x < kRows) {
+          float t = 0.f;
+#pragma unroll
+          for (int w = 0; w < WAVES; ++w) t += s_stat[w * kRows + threadIdx.x];
+          t /= DV;
+          if (pass == 0) s_mean[threadIdx.x] = t;
+          else s_rstd[threadIdx.x] = 1.0f / sqrtf(t + gn.eps);
+        }
+        lds_barrier();
+      }
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = qt * 32 + acc_row(r, lane);
+          const float mean = s_mean[row], rstd = s_rstd[row];
+#pragma unroll
+          for (int nt = 0; nt < NVT; ++nt) acc[qt][nt][r] = (acc[qt][nt][r] - mean) * rstd * w[nt] + bb[nt];
+        }
+    }
+
+    // Store: accumulators r and r+1 of a lane are rows rho and rho+1 of one
+    // column; swapping one value with the neighbouring lane (DPP) gives each
+    // lane two adjacent columns of one row, written as one 4-byte store. Rows
+    // go out in groups of eight (qt*32 + 8g ..), each through a descriptor
+    // whose range ends at the block's last valid row, so the lane offsets are
+    // the same for every group.
+    {
+      const bool odd = lane & 1;
+      const int voff = ((4 * (lane >> 5) + (odd ? 1 : 0)) * DV + vcol0 + (l32 & ~1)) * 2;
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int row0 = qt * 32 + 8 * g;
+          const __amdgpu_buffer_rsrc_t r =
+              make_rsrc(oblk + row0 * DV, min(max(oq - row0, 0), 8) * DV * 2);
+#pragma unroll
+          for (int nt = 0; nt < NVT; ++nt)
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp) {
+              // accumulators 4g + 2hp (row row0 + 4*(lane/32) + 2hp) and the next row
+              const int rr = 4 * g + 2 * hp;
+              const float v0 = acc[qt][nt][rr], v1 = acc[qt][nt][rr + 1];
+              const float y = dpp_f<0xB1>(odd ? v0 : v1);  // quad_perm [1,0,3,2]
+              const unsigned packed = odd ? pack_bf16x2(y, v1) : pack_bf16x2(v0, y);
+              __builtin_amdgcn_raw_buffer_store_b32(packed, r, voff + (2 * hp * DV + nt * 32) * 2, 0, 0);
+            }
+        }
+    }
+
+    if (Ln < 0) break;
+    // The next block's copies were issued before this block's O stores: wait
+    // for everything but those stores.
+    __builtin_amdgcn_s_waitcnt((OSTORES & 15) | ((OSTORES >> 4) << 14) | 0x70 | 0xF00);
+    __syncthreads();
   }
 }
 
@@ -1060,6 +1152,33 @@ hipError_t launch_mfma_state_walk(const uint16_t* k, const uint16_t* v, const fl
   return hipSuccess;
 }
 
+// Number of workgroups of `kernel` (with `threads` threads) resident on the
+// current device at once: CUs times workgroups per CU, cached per device and
+// kernel slot `which` (0..2).
+static hipError_t resident_workgroups(const void* kernel, int threads, int which, int* out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices][3];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = cache[dev][which].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *out = c;
+      return hipSuccess;
+    }
+  }
+  int cus = 0, per_cu = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
+  if (e != hipSuccess) return e;
+  const int n = std::max(1, cus * per_cu);
+  if (dev >= 0 && dev < kMaxDevices) cache[dev][which].store(n, std::memory_order_relaxed);
+  *out = n;
+  return hipSuccess;
+}
+
 hipError_t launch_mfma_chunk_out(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const uint16_t* chunk_states, bool state_for_chunk0, uint16_t* o, const Dims& d,
                                  int chunk, const HeadDecay& decay, const GnArgs& gn, hipStream_t stream) {
@@ -1077,13 +1196,24 @@ hipError_t launch_mfma_chunk_out(const uint16_t* q, const uint16_t* k, const uin
   a.chunk = chunk;
   a.nchunks = (d.N + chunk - 1) / chunk;
   a.nqb = (d.N + kRows - 1) / kRows;
-  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(d.B) * d.H * a.nqb));
+  const int64_t nblocks = static_cast<int64_t>(d.B) * d.H * a.nqb;
+  if (nblocks > INT32_MAX) return hipErrorInvalidValue;
+  a.nblocks = static_cast<int>(nblocks);
+  if (a.nblocks == 0) return hipSuccess;
+  // As many workgroups as are resident at once (each loops over its blocks).
+  auto launch = [&](auto kernel, int threads, int which) -> hipError_t {
+    int wgs = 0;
+    const hipError_t e = resident_workgroups(reinterpret_cast<const void*>(kernel), threads, which, &wgs);
+    if (e != hipSuccess) return e;
+    const dim3 grid(static_cast<unsigned>(std::min<int64_t>(wgs, nblocks)));
+    kernel<<<grid, threads, 0, stream>>>(a, decay, gn);
+    return hipGetLastError();
+  };
   switch (d.dv) {
-    case 128: mfma_chunk_out_kernel<1, 4><<<grid, 256, 0, stream>>>(a, decay, gn); break;
-    case 256: mfma_chunk_out_kernel<1, 8><<<grid, 512, 0, stream>>>(a, decay, gn); break;
-    default: mfma_chunk_out_kernel<2, 8><<<grid, 512, 0, stream>>>(a, decay, gn); break;
+    case 128: return launch(mfma_chunk_out_kernel<1, 4>, 256, 0);
+    case 256: return launch(mfma_chunk_out_kernel<1, 8>, 512, 1);
+    default: return launch(mfma_chunk_out_kernel<2, 8>, 512, 2);
   }
-  return hipGetLastError();
 }
 
 }  // namespace ret

@@ -161,6 +161,30 @@ def test_bf16_groupnorm_epilogue(affine, form):
     _check(o, ref, 2e-2, "gn")
 
 
+# Shapes with more 64-row query blocks than the output kernel runs workgroups
+# (one per CU), so each workgroup takes several blocks, from different heads,
+# chunk positions and a ragged tail, with state read-out and affine GroupNorm.
+MANY_BLOCK_SHAPES = [
+    # B, H, N, dk, dv, chunk
+    (4, 16, 1000, 32, 128, 128),
+    (4, 8, 700, 128, 256, 64),
+    (2, 8, 1100, 256, 512, 256),
+]
+
+
+@pytest.mark.parametrize("B,H,N,dk,dv,C", MANY_BLOCK_SHAPES)
+def test_bf16_chunkwise_many_blocks_per_workgroup(B, H, N, dk, dv, C):
+    _announce(f"bf16 chunkwise many blocks {B}x{H}x{N} dk={dk} dv={dv} C={C}")
+    q, k, v, g, S0 = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=N + dk + dv, with_state=True)
+    w, bvec = synthetic.make_gn_affine(H, dv, seed=N + 5)
+    raw, Sref = orc.chunkwise(q, k, v, g, C, state_in=S0)
+    ref = orc.group_norm(raw, eps=1e-5, weight=w, bias=bvec)
+    qd, kd, vd, S0d, wd, bd = _dev(q, k, v, S0, w, bvec)
+    o, S = ret.chunkwise(qd, kd, vd, g, C, state_in=S0d, state_out=True, gn=ret.GroupNorm(1e-5, wd, bd))
+    _check(o, ref, 2e-2, "o")
+    _check(S, Sref, 2e-2, "state")
+
+
 def test_bf16_generic_fallback_shapes():
     """bf16 sizes outside the MFMA kernels (dv=64, chunk not a multiple of 64) use the generic kernels."""
     _announce("bf16 generic fallback")
