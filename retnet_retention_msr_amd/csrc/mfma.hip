@@ -873,11 +873,22 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
 
     const int ns = cur.ns, ntiles = cur.ntiles;
 
+    // Decay of score (query q, key t): gamma^(q - t) = gamma^(q0 - t0) *
+    // gamma^(ql - tl - r), the first factor uniform per key block, the second
+    // fixed per lane for the whole block (q = q0 + ql, t = t0 + tl + r below).
+    float flane[SW][4];
+#pragma unroll
+    for (int j = 0; j < SW; ++j) {
+      const int u = wave + WAVES * j;
+      const int dl0 = (u & 3) * 16 + l16 - ((u >> 2) * 16 + 4 * (lane >> 4));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) flane[j][r] = gpow(cur.lg, static_cast<float>(dl0 - r));
+    }
+
     // Scores of key block kb from K block `kt`: this wave's 16 x 16 tiles of
     // S^T = K Q^T, decayed and masked, as bf16 into `pdst`. Blocks outside
     // 0..nkb-1 (zero K rows) write zeros into a buffer nobody reads before it
-    // is rewritten. The dk sum runs in four accumulators so the MFMAs need not
-    // wait for each other.
+    // is rewritten.
     auto score_reads = [&](const uint16_t* kt, bf16x8 (&kfr)[SW][8]) __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < SW; ++j) {
@@ -887,26 +898,21 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
       }
     };
     auto scores = [&](int kb, const bf16x8 (&kfr)[SW][8], uint16_t* pdst) __attribute__((always_inline)) {
-      const int t0 = cur.cs + kb * kTile;
+      const int dq = cur.q0 - (cur.cs + kb * kTile);
+      const float fblock = gpow(cur.lg, static_cast<float>(dq));
 #pragma unroll
       for (int j = 0; j < SW; ++j) {
         const int u = wave + WAVES * j;
         const int qt = u & 3, tt = u >> 2;
-        floatx4 sacc[4] = {};
+        floatx4 sacc = {};
 #pragma unroll
-        for (int s = 0; s < 8; ++s) sacc[s & 3] = mfma16(kfr[j][s], qf[j][s], sacc[s & 3]);  // zero past dk
-        const floatx4 sum = (sacc[0] + sacc[1]) + (sacc[2] + sacc[3]);
-        // sum[r] = S^T[t][q]: t = tt*16 + 4*(lane/16) + r, q = qt*16 + lane%16.
+        for (int s = 0; s < 8; ++s) sacc = mfma16(kfr[j][s], qf[j][s], sacc);  // zero past dk
+        // sacc[r] = S^T[t][q]: t = tt*16 + 4*(lane/16) + r, q = qt*16 + lane%16.
         const int ql = qt * 16 + l16;
         const int tl = tt * 16 + 4 * (lane >> 4);
-        const int d0 = cur.q0 + ql - (t0 + tl);
         float x[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int d = d0 - r;
-          const float e = gpow(cur.lg, static_cast<float>(max(d, 0)));
-          x[r] = d >= 0 ? sum[r] * e : 0.f;
-        }
+        for (int r = 0; r < 4; ++r) x[r] = ql - tl - r >= -dq ? sacc[r] * (fblock * flane[j][r]) : 0.f;
         uint2 w;
         w.x = pack_bf16x2(x[0], x[1]);
         w.y = pack_bf16x2(x[2], x[3]);
@@ -1007,7 +1013,7 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
     // Optional per-head GroupNorm over the DV columns of each row.
     if (gn.enabled) {
       float* s_stat = reinterpret_cast<float*>(sP0);  // [WAVES][64], then mean[64], rstd[64]
-      float* s_mean = s_stat + WAVES * kRows;
+      float* s_mean = s_stat + WAVES * kRows;        // the mean, later -mean * rstd
       float* s_rstd = s_mean + kRows;
       // Each lane holds 32 row slots (query tile qt, accumulator r); a
       // reduce-scatter over the 32 lanes sharing them leaves lane l with the
@@ -1037,31 +1043,51 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
 #pragma unroll
           for (int w = 0; w < WAVES; ++w) t += s_stat[w * kRows + threadIdx.x];
           t /= DV;
-          if (pass == 0) s_mean[threadIdx.x] = t;
-          else s_rstd[threadIdx.x] = 1.0f / sqrtf(t + gn.eps);
+          if (pass == 0) {
+            s_mean[threadIdx.x] = t;
+          } else {
+            const float rstd = 1.0f / sqrtf(t + gn.eps);
+            s_rstd[threadIdx.x] = rstd;
+            s_mean[threadIdx.x] = -s_mean[threadIdx.x] * rstd;
+          }
         }
         lds_barrier();
       }
+      // (x - mean) * rstd as one multiply-add per value, then the affine map.
+      const bool affine = gn.weight || gn.bias;
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = qt * 32 + acc_row(r, lane);
-          const float mean = s_mean[row], rstd = s_rstd[row];
+          const float rstd = s_rstd[row], shift = s_mean[row];
 #pragma unroll
-          for (int nt = 0; nt < NVT; ++nt) acc[qt][nt][r] = (acc[qt][nt][r] - mean) * rstd * w[nt] + bb[nt];
+          for (int nt = 0; nt < NVT; ++nt) acc[qt][nt][r] = fmaf(acc[qt][nt][r], rstd, shift);
         }
+      if (affine) {
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+#pragma unroll
+            for (int nt = 0; nt < NVT; ++nt) acc[qt][nt][r] = fmaf(acc[qt][nt][r], w[nt], bb[nt]);
+      }
     }
 
     // Store: accumulators r and r+1 of a lane are rows rho and rho+1 of one
-    // column; swapping one value with the neighbouring lane (DPP) gives each
-    // lane two adjacent columns of one row, written as one 4-byte store. Rows
+    // column. Packed to bf16 pairs, one exchange with the neighbouring lane
+    // (DPP) and a byte permute give each lane two adjacent columns of one row
+    // (the even lane row rho, the odd lane row rho+1), written as one 4-byte
+    // store. Rows
     // go out in groups of eight (qt*32 + 8g ..), each through a descriptor
     // whose range ends at the block's last valid row, so the lane offsets are
     // the same for every group.
     {
       const bool odd = lane & 1;
       const int voff = ((4 * (lane >> 5) + (odd ? 1 : 0)) * DV + vcol0 + (l32 & ~1)) * 2;
+      // v_perm byte selectors over {neighbour (bytes 4-7), own (bytes 0-3)}:
+      // even lanes take both low halves, odd lanes both high halves.
+      const unsigned sel = odd ? 0x03020706u : 0x05040100u;
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
@@ -1075,9 +1101,9 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
             for (int hp = 0; hp < 2; ++hp) {
               // accumulators 4g + 2hp (row row0 + 4*(lane/32) + 2hp) and the next row
               const int rr = 4 * g + 2 * hp;
-              const float v0 = acc[qt][nt][rr], v1 = acc[qt][nt][rr + 1];
-              const float y = dpp_f<0xB1>(odd ? v0 : v1);  // quad_perm [1,0,3,2]
-              const unsigned packed = odd ? pack_bf16x2(y, v1) : pack_bf16x2(v0, y);
+              const unsigned own = pack_bf16x2(acc[qt][nt][rr], acc[qt][nt][rr + 1]);
+              const unsigned nbr = __builtin_amdgcn_update_dpp(0u, own, 0xB1, 0xf, 0xf, true);  // quad_perm [1,0,3,2]
+              const unsigned packed = __builtin_amdgcn_perm(nbr, own, sel);
               __builtin_amdgcn_raw_buffer_store_b32(packed, r, voff + (2 * hp * DV + nt * 32) * 2, 0, 0);
             }
         }
