@@ -98,11 +98,12 @@ def measured_traffic():
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary.
 
     A figure is used only while the kernel source it was measured on is
-    unchanged (hash of the kernel file and common.h); otherwise it is None.
+    unchanged (hash of the kernel file and the headers it includes);
+    otherwise it is None.
     """
     current = {
-        "chunk_out": _source_hash(["mfma.hip", "common.h"]),
-        "state_walk": _source_hash(["mfma.hip", "common.h"]),
+        "chunk_out": _source_hash(["mfma.hip", "mfma_tiles.h", "common.h"]),
+        "state_walk": _source_hash(["mfma.hip", "mfma_tiles.h", "common.h"]),
         "decode_step": _source_hash(["decode.hip", "common.h"]),
     }
     out = {k: None for k in current}
@@ -363,7 +364,7 @@ def main():
             "mfma_frac": achieved / PEAK_BF16,
         },
         "state_walk": {
-            "kernel": "mfma_state_walk_kernel (retention_chunk_states: chunk-state carry)",
+            "kernel": "mfma_state_walk2_kernel (retention_chunk_states: chunk-state carry)",
             "launch_ms": walk_ms,
             "bound": "hbm",
             "algorithmic_bytes_per_launch": bytes_walk,
