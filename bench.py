@@ -20,8 +20,13 @@ against 8 TB/s. The same object also gives the matrix-core view (algorithmic
 flops over time against the 2.5 PFLOP/s dense bf16 peak). `step_roofline`
 does the same for the whole step (both stages), `state_walk` for the first
 stage. `decode` carries the decode step's latency and its HBM roofline
-(134,610,944 algorithmic bytes per step against 8 TB/s). `cpu_baseline` is
-the fp64 CPU oracle on a bounded sample.
+(134,610,944 algorithmic bytes per step against 8 TB/s);
+`decode_cache_defeating` repeats it at B=32, whose 256 MiB state does not fit
+the Infinity Cache. `small_config` times the parallel and chunkwise forms at
+B=2 H=8 N=2048, `long_sequence` the chunkwise form at B=1 H=16 from 8k to 64k
+tokens and chunk 64..512, each with its binding-roofline fraction.
+`cpu_baseline` is the fp64 CPU oracle on a bounded sample of the prefill
+(plus, under `other_cases`, the decode step and the B=2 chunkwise case).
 """
 
 from __future__ import annotations
@@ -164,7 +169,14 @@ def long_sequence_sweep(ret, synthetic, dev, reps=5):
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
-        return {"N": n, "chunk": chunk, "ms": ms, "tokens_per_s": n / (ms * 1e-3)}
+        flop = algorithmic_flops(1, H_, n, chunk)
+        byts = output_bytes(1, H_, n, chunk) + walk_bytes(1, H_, n, chunk)
+        # The binding roof of the whole forward: min(MFMA peak, AI * HBM peak).
+        roof = min(PEAK_BF16, flop / byts * PEAK_HBM)
+        return {"N": n, "chunk": chunk, "ms": ms, "tokens_per_s": n / (ms * 1e-3),
+                "algorithmic_flop": flop, "algorithmic_bytes": byts,
+                "binding_roof": "mfma" if roof == PEAK_BF16 else "hbm",
+                "binding_roof_frac": flop / (ms * 1e-3) / roof}
 
     by_length = [run(n, 512) for n in LONG_LENGTHS]
     by_chunk = [run(max(LONG_LENGTHS), c) for c in LONG_CHUNKS]
@@ -175,6 +187,105 @@ def long_sequence_sweep(ret, synthetic, dev, reps=5):
         "by_chunk_N65536": by_chunk,
         "flatness_min_over_max": min(tps) / max(tps),
     }
+
+
+def small_config(ret, synthetic, dev, reps=20):
+    """The 1.3B-shaped case (B=2, H=8, N=2048, dk=256, dv=512, chunk 256,
+    bf16, seed 1002): parallel and chunkwise forward, µs per call from HIP
+    events around `reps` calls after two warm-up calls, with tokens/s and the
+    binding-roofline fraction (algorithmic flop and bytes as for the prefill)."""
+    import torch
+
+    b, h, n, c = 2, 8, 2048, 256
+    gamma = synthetic.head_gammas(h)
+    q, k, v = synthetic.make_qkv(b, h, n, DK, DV, dtype=torch.bfloat16, seed=1002)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty(b, h, n, DV, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(ret.chunkwise_workspace_bytes(b, h, n, DK, DV, c), dtype=torch.uint8, device=dev)
+
+    def timed(f):
+        for _ in range(2):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    res = {"workload": "B=2 H=8 N=2048 dk=256 dv=512 bf16, no GroupNorm", "reps": reps}
+    # parallel: N(N+1)/2 score entries per head, each 2*dk + 2*dv flop; bytes Q, K, V, O.
+    par_flop = float(b * h * n * (n + 1) * (DK + DV))
+    par_bytes = float(b * h * n * (2 * DK + 2 * DV) * 2)
+    us = timed(lambda: ret.parallel(qd, kd, vd, gamma, out=out))
+    roof = min(PEAK_BF16, par_flop / par_bytes * PEAK_HBM)
+    res["parallel"] = {"us": us, "tokens_per_s": b * n / (us * 1e-6), "algorithmic_flop": par_flop,
+                       "binding_roof_frac": par_flop / (us * 1e-6) / roof}
+    ch_flop = algorithmic_flops(b, h, n, c)
+    ch_bytes = output_bytes(b, h, n, c) + walk_bytes(b, h, n, c)
+    us = timed(lambda: ret.chunkwise(qd, kd, vd, gamma, c, out=out, workspace=ws))
+    roof = min(PEAK_BF16, ch_flop / ch_bytes * PEAK_HBM)
+    res["chunkwise"] = {"us": us, "chunk": c, "tokens_per_s": b * n / (us * 1e-6), "algorithmic_flop": ch_flop,
+                        "algorithmic_bytes": ch_bytes, "binding_roof_frac": ch_flop / (us * 1e-6) / roof}
+    return res
+
+
+def decode_cache_defeating(ret, synthetic, dev, steps=64):
+    """Secondary decode measurement at B=32, H=16 (the fp32 state, 256 MiB,
+    exceeds the 256 MB Infinity Cache, so each step's state read and write
+    reach HBM): µs per step and algorithmic GB/s."""
+    import torch
+
+    b = 32
+    gamma = synthetic.head_gammas(H)
+    gen = torch.Generator().manual_seed(DECODE_SEED + 1)
+    st = torch.randn(b, H, DK, DV, generator=gen).to(dev)
+    qs = torch.randn(steps, b, H, DK, generator=gen).to(torch.bfloat16).to(dev)
+    ks = torch.randn(steps, b, H, DK, generator=gen).to(torch.bfloat16).to(dev)
+    vs = torch.randn(steps, b, H, DV, generator=gen).to(torch.bfloat16).to(dev)
+    o = torch.empty(b, H, DV, dtype=torch.bfloat16, device=dev)
+    for i in range(4):
+        ret.recurrent_step(qs[i], ks[i], vs[i], gamma, st, out=o)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        ret.recurrent_step(qs[i], ks[i], vs[i], gamma, st, out=o)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    byts = decode_bytes(b, H)
+    return {"B": b, "H": H, "steps": steps, "us_per_step": us, "algorithmic_bytes_per_step": byts,
+            "achieved_gbps": byts / (us * 1e-6) / 1e9, "frac": byts / (us * 1e-6) / PEAK_HBM}
+
+
+def cpu_extra(synthetic, gamma):
+    """The fp64 oracle on the other measured cases: the decode step over all
+    B*H heads (16 steps from a random state) and the 1.3B-shaped chunkwise
+    forward in full."""
+    import torch
+
+    from oracle import retention_oracle as orc
+
+    gen = torch.Generator().manual_seed(DECODE_SEED)
+    st = torch.randn(B, H, DK, DV, generator=gen)
+    qs = torch.randn(16, B, H, DK, generator=gen).to(torch.bfloat16)
+    ks = torch.randn(16, B, H, DK, generator=gen).to(torch.bfloat16)
+    vs = torch.randn(16, B, H, DV, generator=gen).to(torch.bfloat16)
+    t0 = time.perf_counter()
+    S = st
+    for i in range(16):
+        _, S = orc.recurrent_step(qs[i], ks[i], vs[i], gamma, S)
+    dec_us = (time.perf_counter() - t0) / 16 * 1e6
+    q2, k2, v2 = synthetic.make_qkv(2, 8, 2048, DK, DV, dtype=torch.bfloat16, seed=1002)
+    t0 = time.perf_counter()
+    orc.chunkwise(q2, k2, v2, synthetic.head_gammas(8), 256)
+    small_s = time.perf_counter() - t0
+    return {"decode_us_per_step": dec_us, "decode_workload": f"B={B} H={H} dk={DK} dv={DV}, 16 steps",
+            "small_chunkwise_s": small_s, "small_tokens_per_s": 2 * 2048 / small_s,
+            "small_workload": "B=2 H=8 N=2048 dk=256 dv=512 chunk 256"}
 
 
 def cpu_baseline(q, k, v, gamma, n_batch_rows=2):
@@ -217,6 +328,7 @@ def main():
                     help="run one plain device copy of this many MiB first (reference for HBM byte counters)")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-long", action="store_true", help="skip the long-sequence flatness sweep")
+    ap.add_argument("--skip-small", action="store_true", help="skip the B=2 H=8 N=2048 timings")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -273,6 +385,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     ms = ev[0][0].elapsed_time(ev[-1][2]) / args.steps
+    per_step = sorted(e[0].elapsed_time(e[2]) for e in ev)
+    ms_median, ms_min = per_step[len(per_step) // 2], per_step[0]
     walk_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     out_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
     tokens_per_s = B * N / (ms * 1e-3)
@@ -307,10 +421,21 @@ def main():
     dbytes = decode_bytes(B, H)
     dgbps = dbytes / (us_step * 1e-6) / 1e9
 
+    decode_b32 = None
+    if not args.skip_decode:
+        print("[bench] cache-defeating decode (B=32)", file=sys.stderr, flush=True)
+        decode_b32 = decode_cache_defeating(ret, synthetic, dev)
+
+    small = None
+    if not args.skip_small:
+        print("[bench] B=2 H=8 N=2048 parallel and chunkwise", file=sys.stderr, flush=True)
+        small = small_config(ret, synthetic, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(q, k, v, gamma, args.cpu_batch_rows)
+        cpu["other_cases"] = cpu_extra(synthetic, gamma)
 
     long_seq = None
     if not args.skip_long:
@@ -326,6 +451,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": ms_median,
+        "ms_per_step_min": ms_min,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -387,6 +514,8 @@ def main():
                 "algorithmic_bytes_per_step": dbytes,
             },
         },
+        "decode_cache_defeating": decode_b32,
+        "small_config": small,
         "long_sequence": long_seq,
         "cpu_baseline": cpu,
         "wall_s_timed": wall,
