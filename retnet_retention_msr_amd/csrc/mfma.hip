@@ -122,7 +122,10 @@ struct WalkArgs {
   float* seg_states;       // [B*H][nseg][dk][dv]
   int H, N, dk, dv, chunk, nchunks, nseg, chunks_per_seg;
   int nkt, nvt;
-  int mode;  // 0: end state of segments 0..nseg-2; 1: write chunk states from the true start
+  // 0: end state of segments 0..nseg-2; 1: write chunk states from the true
+  // start; 2: every segment from zero (segment 0 from state_in), chunk states
+  // and end states written (walk_fixup_kernel then makes them true).
+  int mode;
 };
 
 template <int MT>
@@ -212,7 +215,7 @@ __global__ void __launch_bounds__(kThreads) mfma_state_walk_kernel(WalkArgs a, H
     const int cs = c * a.chunk;
     const int L = min(a.chunk, a.N - cs);
     if (t0 == 0) {
-      if (a.mode == 1) {
+      if (a.mode >= 1) {
         // Store R_{c-1} as bf16, [k][v] layout; 32 lanes cover 64 contiguous bytes of a row.
         uint16_t* dst = a.chunk_states + ((bh * a.nchunks + c) * a.dk + k0) * static_cast<int64_t>(a.dv) + vcol;
 #pragma unroll
@@ -268,12 +271,12 @@ __global__ void __launch_bounds__(kThreads) mfma_state_walk_kernel(WalkArgs a, H
     t0 = nt0;
   }
 
-  // Mode 0 stores the segment's end state. Mode 1 stores the final state: to
-  // state_out when there is one segment, else into the spare last segment slot
-  // (the host copies it to state_out afterwards, so state_out may alias
-  // state_in while other segments still read it).
+  // Modes 0 and 2 store the segment's end state. Mode 1 stores the final
+  // state: to state_out when there is one segment, else into the spare last
+  // segment slot (the host copies it to state_out afterwards, so state_out may
+  // alias state_in while other segments still read it).
   float* out = nullptr;
-  if (a.mode == 0) out = a.seg_states + (bh * a.nseg + seg) * dkdv;
+  if (a.mode != 1) out = a.seg_states + (bh * a.nseg + seg) * dkdv;
   else if (seg == a.nseg - 1) {
     if (a.nseg > 1) out = a.seg_states + (bh * a.nseg + seg) * dkdv;
     else if (a.state_out) out = a.state_out + bh * dkdv;
@@ -419,7 +422,7 @@ __global__ void __launch_bounds__(kWalk2Threads) mfma_state_walk2_kernel(WalkArg
   while (c < c_end) {
     if (t0 == 0) {
       const int L = min(a.chunk, a.N - c * a.chunk);
-      if (a.mode == 1) {
+      if (a.mode >= 1) {
         // Store R_{c-1} as bf16 ([k][v], v fastest). Each 32x32 accumulator tile
         // goes through this wave's LDS patch, stored transposed (a lane's four
         // consecutive rows of one column in one 8-byte write), and comes back
@@ -497,12 +500,12 @@ __global__ void __launch_bounds__(kWalk2Threads) mfma_state_walk2_kernel(WalkArg
     buf ^= 1;
   }
 
-  // Mode 0 stores the segment's end state. Mode 1 stores the final state: to
-  // state_out when there is one segment, else into the spare last segment slot
-  // (the host copies it to state_out afterwards, so state_out may alias
-  // state_in while other segments still read it).
+  // Modes 0 and 2 store the segment's end state. Mode 1 stores the final
+  // state: to state_out when there is one segment, else into the spare last
+  // segment slot (the host copies it to state_out afterwards, so state_out may
+  // alias state_in while other segments still read it).
   float* out = nullptr;
-  if (a.mode == 0) out = a.seg_states + (bh * a.nseg + seg) * dkdv;
+  if (a.mode != 1) out = a.seg_states + (bh * a.nseg + seg) * dkdv;
   else if (seg == a.nseg - 1) {
     if (a.nseg > 1) out = a.seg_states + (bh * a.nseg + seg) * dkdv;
     else if (a.state_out) out = a.state_out + bh * dkdv;
@@ -515,6 +518,74 @@ __global__ void __launch_bounds__(kWalk2Threads) mfma_state_walk2_kernel(WalkArg
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           out[static_cast<int64_t>(krow0 + mt * 32 + acc_row(r, lane)) * a.dv + vcol + 32 * nt] = acc[mt][nt][r];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Segment fix-up after a mode-2 walk
+// ---------------------------------------------------------------------------
+// Segment 0 was walked from the true start, the others from zero. The true
+// state at the start of segment s >= 1 is S_s = gamma^len_{s-1} S_{s-1} +
+// U_{s-1} with S_1 = U_0 (U = the stored end states), and the true state
+// before chunk c of segment s is the stored one plus gamma^(chunk (c - c_s))
+// S_s: only full chunks precede a stored state. One thread per head and eight
+// consecutive state elements walks the segments in order, rewrites the bf16
+// chunk states of segments 1.. in place and writes the final state.
+constexpr int kFixThreads = 256;
+
+struct FixArgs {
+  uint16_t* chunk_states;  // [B*H][nchunks][dk][dv]
+  const float* seg_states; // [B*H][nseg][dk][dv]
+  float* state_out;        // [B*H][dk][dv] or null
+  int64_t heads;
+  int H, N, chunk, nchunks, nseg, chunks_per_seg, dkdv;
+};
+
+__global__ void __launch_bounds__(kFixThreads) walk_fixup_kernel(FixArgs a, HeadDecay decay) {
+  const int per_head = a.dkdv / 8;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kFixThreads + threadIdx.x;
+  if (idx >= a.heads * per_head) return;
+  const int64_t bh = idx / per_head;
+  const int e0 = static_cast<int>(idx % per_head) * 8;
+  const float lg = decay.log2g[bh % a.H];
+  const float* U = a.seg_states + bh * a.nseg * static_cast<int64_t>(a.dkdv) + e0;
+  float S[8];
+  {
+    const floatx4 lo = *reinterpret_cast<const floatx4*>(U);
+    const floatx4 hi = *reinterpret_cast<const floatx4*>(U + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      S[e] = lo[e];
+      S[e + 4] = hi[e];
+    }
+  }
+  for (int s = 1; s < a.nseg; ++s) {
+    const int c_s = s * a.chunks_per_seg;
+    const int c_e = min(a.nchunks, c_s + a.chunks_per_seg);
+    for (int c = c_s; c < c_e; ++c) {
+      const float f = gpow(lg, static_cast<float>((c - c_s) * a.chunk));
+      u32x4* p = reinterpret_cast<u32x4*>(a.chunk_states + (bh * a.nchunks + c) * static_cast<int64_t>(a.dkdv) + e0);
+      u32x4 v = *p;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[e] = pack_bf16x2(fmaf(f, S[2 * e], __uint_as_float(v[e] << 16)),
+                           fmaf(f, S[2 * e + 1], __uint_as_float(v[e] & 0xffff0000u)));
+      *p = v;
+    }
+    const float g = gpow(lg, static_cast<float>(min(a.N, c_e * a.chunk) - c_s * a.chunk));
+    const float* Us = U + static_cast<int64_t>(s) * a.dkdv;
+    const floatx4 lo = *reinterpret_cast<const floatx4*>(Us);
+    const floatx4 hi = *reinterpret_cast<const floatx4*>(Us + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      S[e] = fmaf(g, S[e], lo[e]);
+      S[e + 4] = fmaf(g, S[e + 4], hi[e]);
+    }
+  }
+  if (a.state_out) {
+    float* o = a.state_out + bh * static_cast<int64_t>(a.dkdv) + e0;
+    *reinterpret_cast<floatx4*>(o) = floatx4{S[0], S[1], S[2], S[3]};
+    *reinterpret_cast<floatx4*>(o + 4) = floatx4{S[4], S[5], S[6], S[7]};
   }
 }
 
@@ -970,6 +1041,17 @@ bool mfma_supports(int dk, int dv) {
 
 int walk_k_tiles(int dk) { return (dk % 64 == 0) ? 2 : 1; }
 
+// A segmented walk either runs twice (segment end states from zero, then every
+// segment from its true start) or once from zero followed by a fix-up pass
+// that reads and rewrites the chunk states of segments 1.. (2 x 2 bytes per
+// state element and chunk, against 2 (dk + dv) bytes per token for a second
+// walk's K and V). Measured on B1 H16 dk256 dv512: the fix-up wins from
+// chunk 256 on (where it moves up to twice the bytes of a second walk, which
+// is latency-bound) and loses at 64 and 128.
+bool walk_fixup_segments(int chunk, int dk, int dv) {
+  return 1LL * dk * dv < static_cast<int64_t>(chunk) * (dk + dv);
+}
+
 // The full-dk walk covers dk = 128 and 256 with one workgroup per 128 v columns.
 bool walk_full_dk(int dk) { return dk == 128 || dk == 256; }
 
@@ -1001,7 +1083,7 @@ hipError_t launch_mfma_state_walk(const uint16_t* k, const uint16_t* v, const fl
   a.nkt = full ? 1 : d.dk / (32 * MT);
   a.nvt = d.dv / (full ? kWalk2VT : kWalkVT);
   const int64_t per_seg = static_cast<int64_t>(d.B) * d.H * a.nkt * a.nvt;
-  for (int mode = (a.nseg > 1 ? 0 : 1); mode <= 1; ++mode) {
+  auto walk = [&](int mode) -> hipError_t {
     a.mode = mode;
     const int64_t nblocks = per_seg * (mode == 0 ? a.nseg - 1 : a.nseg);
     const dim3 grid(static_cast<unsigned>(nblocks));
@@ -1009,7 +1091,32 @@ hipError_t launch_mfma_state_walk(const uint16_t* k, const uint16_t* v, const fl
     else if (full) mfma_state_walk2_kernel<1><<<grid, kWalk2Threads, 0, stream>>>(a, decay);
     else if (MT == 2) mfma_state_walk_kernel<2><<<grid, kThreads, 0, stream>>>(a, decay);
     else mfma_state_walk_kernel<1><<<grid, kThreads, 0, stream>>>(a, decay);
-    const hipError_t e = hipGetLastError();
+    return hipGetLastError();
+  };
+  if (a.nseg > 1 && walk_fixup_segments(chunk, d.dk, d.dv)) {
+    // One walk of every segment (segment 0 from state_in, the rest from zero),
+    // then the fix-up pass.
+    hipError_t e = walk(2);
+    if (e != hipSuccess) return e;
+    FixArgs f;
+    f.chunk_states = chunk_states;
+    f.seg_states = seg_states;
+    f.state_out = state_out;
+    f.heads = static_cast<int64_t>(d.B) * d.H;
+    f.H = d.H;
+    f.N = d.N;
+    f.chunk = chunk;
+    f.nchunks = a.nchunks;
+    f.nseg = a.nseg;
+    f.chunks_per_seg = chunks_per_seg;
+    f.dkdv = d.dk * d.dv;
+    const int64_t threads = f.heads * (f.dkdv / 8);
+    walk_fixup_kernel<<<dim3(static_cast<unsigned>((threads + kFixThreads - 1) / kFixThreads)), kFixThreads, 0,
+                        stream>>>(f, decay);
+    return hipGetLastError();
+  }
+  for (int mode = (a.nseg > 1 ? 0 : 1); mode <= 1; ++mode) {
+    const hipError_t e = walk(mode);
     if (e != hipSuccess) return e;
   }
   if (a.nseg > 1 && state_out) {

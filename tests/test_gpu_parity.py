@@ -200,11 +200,22 @@ def test_bf16_generic_fallback_shapes():
     _check(ret.chunkwise(qd, kd, vd, g, 40)[0], ref, 2e-2, "o chunk 40")
 
 
-def test_bf16_segmented_walk_and_aliased_state():
+@pytest.mark.parametrize(
+    "B,H,N,dk,dv,C",
+    [
+        # two walks (segment end states, then every segment from its true start):
+        (1, 2, 1024 + 40, 96, 512, 64),  # 32-row k tiles
+        (1, 2, 1024 + 40, 128, 256, 64),  # full-dk walk
+        # one walk from zero per segment, then the fix-up pass:
+        (1, 2, 1024 + 40, 64, 128, 192),  # 64-row k tiles
+        (1, 3, 1000, 128, 256, 256),  # full-dk walk (dk 128)
+        (1, 2, 1600, 256, 512, 512),  # full-dk walk (dk 256), ragged last chunk
+    ],
+)
+def test_bf16_segmented_walk_and_aliased_state(B, H, N, dk, dv, C):
     """Few heads, many chunks: the state walk is cut into segments; state_out aliases state_in."""
-    _announce("bf16 segmented walk")
-    B, H, N, dk, dv, C = 1, 2, 1024 + 40, 64, 128, 64
-    q, k, v, g, S0 = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=11, with_state=True)
+    _announce(f"bf16 segmented walk {B}x{H}x{N} dk={dk} dv={dv} C={C}")
+    q, k, v, g, S0 = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=11 + N + C, with_state=True)
     ref, Sref = orc.chunkwise(q, k, v, g, C, state_in=S0)
     qd, kd, vd, Sd = _dev(q, k, v, S0)
     o, S = ret.chunkwise(qd, kd, vd, g, C, state_in=Sd, state_out=Sd)
