@@ -329,6 +329,7 @@ def main():
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-long", action="store_true", help="skip the long-sequence flatness sweep")
     ap.add_argument("--skip-small", action="store_true", help="skip the B=2 H=8 N=2048 timings")
+    ap.add_argument("--skip-decode-b32", action="store_true", help="skip the cache-defeating B=32 decode timing")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -422,7 +423,7 @@ def main():
     dgbps = dbytes / (us_step * 1e-6) / 1e9
 
     decode_b32 = None
-    if not args.skip_decode:
+    if not args.skip_decode and not args.skip_decode_b32:
         print("[bench] cache-defeating decode (B=32)", file=sys.stderr, flush=True)
         decode_b32 = decode_cache_defeating(ret, synthetic, dev)
 

@@ -593,9 +593,19 @@ __global__ void __launch_bounds__(kFixThreads) walk_fixup_kernel(FixArgs a, Head
 // Output
 // ---------------------------------------------------------------------------
 constexpr int kTile = 32;      // rows of a staged tile: 32 keys of V, or 32 rows of the chunk state
-constexpr int kPitchP = 40;    // sP pitch: 80 B, 16 consecutive rows fall on distinct banks
 
+// Buffer set P of three (P is a compile-time step phase).
+template <int P>
+__device__ __forceinline__ uint16_t* pick3(uint16_t* b0, uint16_t* b1, uint16_t* b2) {
+  return P == 0 ? b0 : (P == 1 ? b1 : b2);
+}
 
+// Wait until at most N of this wave's vector memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
 
 // One workgroup per CU, looping over 64-row query blocks (head, rows q0..q0+63);
 // wave w owns value columns [32*NVT*w, 32*NVT*(w+1)) of all 64 rows (2 x NVT
@@ -607,25 +617,29 @@ constexpr int kPitchP = 40;    // sP pitch: 80 B, 16 consecutive rows fall on di
 // count, each workgroup one block per group, rotated by one place per group so
 // every workgroup sees every position within a chunk (their work differs).
 //
-// A block's work is a sequence of tiles, each a 32-row bf16 matrix X in LDS
-// multiplied into O as O += A X: first the dk/32 slices of the stored chunk
+// A block's work is a sequence of steps, each multiplying a 32-row bf16 tile
+// X in LDS into O as O += A X: first the dk/32 slices of the stored chunk
 // state (A = the matching 32 columns of Q, the cross-chunk read-out), then the
 // 32-key blocks of the chunk up to the diagonal (A = the decayed scores of that
 // block, X = its V rows).
 //
 // Scores of a key block, S^T = K Q^T (32 keys x 64 queries), are formed one
-// tile ahead: wave (tt, qt) computes the 16 x 16 tile of keys 16*tt.. and
+// step ahead: wave (tt, qt) computes the 16 x 16 tile of keys 16*tt.. and
 // queries 16*qt.. on 16x16x32 MFMAs, K from LDS, its 16 query rows held in
-// registers for the whole block; it applies gamma^(n-m) (zero above the
-// diagonal) and writes the bf16 scores to sP for the next tile's product.
+// registers for the whole block (loaded once per block); it applies
+// gamma^(n-m) (zero above the diagonal) and writes the bf16 scores to the
+// score buffer of the next step. A state step's A operand, the 64 x 32 Q
+// slice, is copied into the score buffer of its step in the same layout, so
+// both kinds of step read A alike.
 //
-// X tiles and K blocks travel straight from global memory into LDS (buffer
-// loads with an LDS destination) one tile ahead, into the other of two buffer
-// pairs; each tile ends with a wait for those copies and one barrier. The
-// buffers are distinct LDS arrays chosen at compile time per tile parity, so
-// the LDS reads of a tile never wait for the copies in flight. The next
-// block's Q rows and first tiles are requested before the current block's
-// GroupNorm and store, which need no tile buffer.
+// Tiles travel straight from global memory into LDS (buffer loads with an LDS
+// destination) two steps ahead, in three buffer sets (X tile + K block, and a
+// score buffer): the copies of step i+2 go into the set step i-1 read, and step
+// i ends by waiting for all but its own copies, then one barrier. The sets are
+// distinct LDS arrays chosen at compile time per step phase (i mod 3), so the
+// LDS reads of a step never wait for the copies in flight. The next block's
+// first copies and Q rows are requested before the current block's GroupNorm
+// and store, which use no buffer those copies write.
 template <int NVT, int WAVES>
 __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, HeadDecay decay, GnArgs gn) {
   constexpr int DV = WAVES * 32 * NVT;
@@ -634,32 +648,96 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
   constexpr int KCH = kTile * 256 * 2 / 1024;      // ... of a K block (dk <= 256)
   constexpr int XI = XCH / WAVES, KI = KCH / WAVES;  // chunks copied per wave
   constexpr int GPR = DV / 8;                      // 16-byte granules per X row
-  constexpr int QI = 2 * KCH / WAVES;              // 1-KiB chunks of the Q block copied per wave
+  constexpr int PT = kRows * kTile;                // elements of a score tile
+  constexpr int QCH = PT * 2 / 1024;               // 1-KiB chunks of a Q slice (one per granule column)
+  constexpr int XK = kTile * DV + kTile * 256;     // elements of one X + K buffer
   constexpr int OSTORES = 2 * NVT * 8;             // 4-byte O stores per lane and block
-  static_assert(XI >= 1 && KI >= 1 && QI >= 1 && XCH % WAVES == 0 && KCH % WAVES == 0, "layout");
-  static_assert((GPR >= 16 && 64 % GPR == 0) || GPR % 64 == 0, "X rows");
+  static_assert(XI >= 1 && KI >= 1 && XCH % WAVES == 0 && KCH % WAVES == 0 && QCH <= WAVES, "layout");
+  static_assert((WAVES * 64 / GPR) % 4 == 0, "X copy offsets");
+  static_assert(XI + KI + 1 <= 7, "copies per step");
   static_assert(OSTORES <= 48, "O stores must fit the vector-memory counter");
-  __shared__ __attribute__((aligned(1024))) uint16_t sQ[kRows * 256];
-  __shared__ __attribute__((aligned(1024))) uint16_t sX0[kTile * DV];
-  __shared__ __attribute__((aligned(1024))) uint16_t sX1[kTile * DV];
-  __shared__ __attribute__((aligned(1024))) uint16_t sK0[kTile * 256];
-  __shared__ __attribute__((aligned(1024))) uint16_t sK1[kTile * 256];
-  __shared__ __attribute__((aligned(16))) uint16_t sP0[kRows * kPitchP];
-  __shared__ __attribute__((aligned(16))) uint16_t sP1[kRows * kPitchP];
-  static_assert(sizeof(sP0) >= (WAVES + 2) * kRows * sizeof(float), "GroupNorm statistics reuse sP0");
+  // X tile at 0 and K block at kTile*DV of each buffer set (copied at the same step).
+  __shared__ __attribute__((aligned(1024))) uint16_t sXK0[XK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sXK1[XK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sXK2[XK];
+  // Scores (or a Q slice) as [8-column granule][row][8]: the 16-byte operand
+  // reads of consecutive rows are contiguous.
+  __shared__ __attribute__((aligned(1024))) uint16_t sP0[PT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sP1[PT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sP2[PT];
+  static_assert(sizeof(sP2) >= (WAVES + 2) * kRows * sizeof(float), "GroupNorm statistics reuse sP2");
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: copy targets in scalars
   const int l32 = lane & 31;
-  const int lk = 8 * (lane >> 5);
   const int l16 = lane & 15;
   const int vcol0 = wave * 32 * NVT;
   const int dk = a.dk;
 
-  // This workgroup's blocks.
+  // Transposed X operands (B of the output product, the contraction index
+  // down the tile's rows), two ds_read_b64_tr_b16 each as in ld_tr8, from the
+  // unpadded swizzled X tile: lane l points at row 16s + 8*(l/32) + (l%16)/4
+  // (and that row + 4, same swizzle) and columns vcol0 + 32nt +
+  // 16*((l/16)%2) + 4*(l%4).., at xo[nt] + 16s*DV (+ 4*DV). The empty asm keeps
+  // each read's address one constant offset away from its buffer, so every
+  // read keeps the buffer's alias information and never waits for copies into
+  // the other buffers.
+  int xo[NVT];
+#pragma unroll
+  for (int nt = 0; nt < NVT; ++nt) {
+    const int g = lane >> 4, j = lane & 15;
+    const int row = 8 * (g >> 1) + (j >> 2);
+    const int col = vcol0 + 32 * nt + 16 * (g & 1) + 4 * (j & 3);
+    xo[nt] = row * DV + (x_pos(row, col >> 3) << 3) + (col & 7);
+    asm volatile("" : "+v"(xo[nt]));
+  }
+  auto ld_x = [&](const uint16_t* tile, int s, int nt) __attribute__((always_inline)) {
+    const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(tile + xo[nt] + 16 * s * DV));
+    const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(tile + xo[nt] + (16 * s + 4) * DV));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // Per-lane source offsets of the copies, fixed for the kernel. X tile: lane
+  // l of 1-KiB piece c = wave + WAVES*m holds granule 64c + l of the swizzled
+  // tile; the row advances by a multiple of four per m, so the swizzle
+  // (row % 4) is that of m = 0 and piece m lies m*WAVES KiB further.
+  int xoff;
+  {
+    const int flat = wave * 64 + lane;
+    const int row = flat / GPR, pos = flat % GPR;
+    xoff = (row * GPR + x_pos(row, pos)) * 16;
+  }
+  // K block: piece c holds rows 2c and 2c+1, granules swizzled with the row (zero past dk).
+  int koff[KI];
+#pragma unroll
+  for (int m = 0; m < KI; ++m) {
+    const int row = 2 * (wave + WAVES * m) + (lane >> 5), pos = lane & 31;
+    const int g = pos ^ (row & 15);
+    koff[m] = g * 8 < dk ? (row * dk + g * 8) * 2 : kOutOfRange;
+  }
+  // Q slice: piece g (one per wave below QCH) holds columns 8g..8g+7 of the
+  // slice for the 64 rows, lane l row l.
+  const int qsoff = lane * dk * 2;
+  // Score tile rows of Q: row (u % 4)*16 + lane%16 of tile u = wave + WAVES*j,
+  // from granule lane/16 on.
+  int qfoff[SW];
+#pragma unroll
+  for (int j = 0; j < SW; ++j) qfoff[j] = (((wave + WAVES * j) & 3) * 16 + l16) * dk * 2 + 16 * (lane >> 4);
+  // K reads of score tile j: granule 4s + lane/16 of row 16*tt + lane%16. For
+  // s and s+4 the swizzled granules differ by 16 (the row's XOR touches
+  // granule bits 0-3 only), so four per-lane offsets serve all eight reads.
+  int kread[SW][4];
+#pragma unroll
+  for (int j = 0; j < SW; ++j)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      kread[j][s] = k_swz(((wave + WAVES * j) >> 2) * 16 + l16, 4 * s + (lane >> 4));
+      asm volatile("" : "+v"(kread[j][s]));
+    }
+
   const int nx = min(kXcds, static_cast<int>(gridDim.x));
   const int xcd = blockIdx.x % nx, slot = blockIdx.x / nx;
-  const int nwg = (static_cast<int>(gridDim.x) - xcd + nx - 1) / nx;  // workgroups sharing this range
+  const int nwg = (static_cast<int>(gridDim.x) - xcd + nx - 1) / nx;
   const int per = (a.nblocks + nx - 1) / nx;
   const int lo = min(a.nblocks, xcd * per), hi = min(a.nblocks, lo + per);
   auto block_of = [&](int it) __attribute__((always_inline)) {
@@ -667,12 +745,11 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
     return L < hi ? L : -1;
   };
 
-  // Geometry of one query block.
   struct Blk {
     int64_t bh;
     int h, q0, cs, qvalid, nkb, ns, ntiles;
     float lg;
-    const uint16_t *kbase, *vbase, *rbase;
+    const uint16_t *kbase, *vbase, *rbase, *qbase;
   };
   auto setup = [&](int L, Blk& b) __attribute__((always_inline)) {
     b.bh = L / a.nqb;
@@ -691,9 +768,10 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
     b.kbase = a.k + b.bh * static_cast<int64_t>(a.N) * dk;
     b.vbase = a.v + b.bh * static_cast<int64_t>(a.N) * DV;
     b.rbase = has_state ? a.chunk_states + (b.bh * a.nchunks + c) * static_cast<int64_t>(dk) * DV : nullptr;
+    b.qbase = a.q + (b.bh * a.N + b.q0) * static_cast<int64_t>(dk);
   };
 
-  // Copy X tile `it` of block b (zeros past the data) into `dst`.
+  // X tile `it` of block b (it < ntiles) into buffer set `dst`.
   auto copy_x = [&](const Blk& b, int it, uint16_t* dst) __attribute__((always_inline)) {
     const uint16_t* src;
     int rows;
@@ -702,52 +780,67 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
       rows = kTile;
     } else {
       const int t0 = b.cs + (it - b.ns) * kTile;
-      src = b.vbase + static_cast<int64_t>(min(t0, a.N)) * DV;
-      rows = it < b.ntiles ? min(kTile, a.N - t0) : 0;
+      src = b.vbase + static_cast<int64_t>(t0) * DV;
+      rows = min(kTile, a.N - t0);
     }
     const __amdgpu_buffer_rsrc_t r = make_rsrc(src, rows * DV * 2);
 #pragma unroll
-    for (int m = 0; m < XI; ++m) {
-      const int chunk = wave + WAVES * m;
-      const int flat = chunk * 64 + lane;  // granule index in the tile
-      const int row = flat / GPR, pos = flat % GPR;
-      dma16(r, dst + chunk * 512, (row * GPR + x_pos(row, pos)) * 16);
-    }
+    for (int m = 0; m < XI; ++m) dma16s(r, dst + (wave + WAVES * m) * 512, xoff, m * WAVES * 1024);
   };
-  // Copy K block kb of block b (zeros outside the chunk's blocks, past N and past dk) into `dst`.
+  // K block kb of block b (0 <= kb < nkb) into buffer set `dst`.
   auto copy_k = [&](const Blk& b, int kb, uint16_t* dst) __attribute__((always_inline)) {
-    const bool ok = kb >= 0 && kb < b.nkb;
-    const int t0 = b.cs + (ok ? kb : 0) * kTile;
-    const int rows = ok ? min(kTile, a.N - t0) : 0;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(b.kbase + static_cast<int64_t>(t0) * dk, rows * dk * 2);
-#pragma unroll
-    for (int m = 0; m < KI; ++m) {
-      const int chunk = wave + WAVES * m;
-      const int row = 2 * chunk + (lane >> 5), pos = lane & 31;
-      const int g = pos ^ (row & 15);
-      dma16(r, dst + chunk * 512, g * 8 < dk ? (row * dk + g * 8) * 2 : kOutOfRange);
-    }
-  };
-  // Copy the Q rows of block b (zeros past N and past dk) into sQ, laid out as K blocks.
-  auto copy_q = [&](const Blk& b) __attribute__((always_inline)) {
+    const int t0 = b.cs + kb * kTile;
     const __amdgpu_buffer_rsrc_t r =
-        make_rsrc(a.q + (b.bh * a.N + b.q0) * static_cast<int64_t>(dk), b.qvalid * dk * 2);
+        make_rsrc(b.kbase + static_cast<int64_t>(t0) * dk, min(kTile, a.N - t0) * dk * 2);
 #pragma unroll
-    for (int m = 0; m < QI; ++m) {
-      const int chunk = wave + WAVES * m;
-      const int row = 2 * chunk + (lane >> 5), pos = lane & 31;
-      const int g = pos ^ (row & 15);
-      dma16(r, sQ + chunk * 512, g * 8 < dk ? (row * dk + g * 8) * 2 : kOutOfRange);
+    for (int m = 0; m < KI; ++m) dma16(r, dst + kTile * DV + (wave + WAVES * m) * 512, koff[m]);
+  };
+  // Columns 32s..32s+31 of the block's Q rows (zero past N) into score buffer
+  // `dst`; waves below QCH copy one granule column each.
+  auto copy_qs = [&](const Blk& b, int s, uint16_t* dst) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(b.qbase, b.qvalid * dk * 2);
+    dma16s(r, dst + wave * 512, qsoff, (s * kTile + wave * 8) * 2);
+  };
+  // The 16 query rows of each of this wave's score tiles as 16x16x32 B
+  // operands (zero past N and past dk): step s holds Q columns 32s.. . A block
+  // with state slices takes them from the slices as they pass through LDS
+  // (each Q element then leaves HBM once); a block without loads them here.
+  bf16x8 qf[SW][8];
+  auto load_qf = [&](const Blk& b) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(b.qbase, b.qvalid * dk * 2);
+#pragma unroll
+    for (int j = 0; j < SW; ++j) {
+      // Granule 4s + lane/16 of the row; step s lies past dk for every lane
+      // or for none (dk is a multiple of 32), so that test is uniform.
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        qf[j][s] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, qfoff[j], s * 32 < dk ? s * 64 : kOutOfRange, 0));
     }
   };
-  // The copies the first step of block b needs: the K block of its first
-  // scores and, when the first step is a tile, X_0.
+  // Everything the first two steps of block b need. Step j reads X_j, its A
+  // operand (Q slice or scores) and the K block of its scores (key block
+  // j+1-ns) from buffer sets j % 3; with no state slice the block starts at
+  // step -1 (set 2), which only forms the scores of key block 0.
   auto first_copies = [&](const Blk& b) __attribute__((always_inline)) {
     if (b.ns > 0) {
-      copy_k(b, 1 - b.ns, sK0);
-      copy_x(b, 0, sX0);
+#pragma unroll
+      for (int j = 0; j < SW; ++j)
+#pragma unroll
+        for (int s = 0; s < 8; ++s) qf[j][s] = bf16x8{};
+      copy_x(b, 0, sXK0);
+      copy_x(b, 1, sXK1);  // ntiles > ns
+      if (wave < QCH) {
+        copy_qs(b, 0, sP0);
+        if (b.ns > 1) copy_qs(b, 1, sP1);
+      }
+      if (b.ns <= 2) copy_k(b, 0, b.ns == 2 ? sXK1 : sXK0);
+      if (b.ns == 1 && b.nkb > 1) copy_k(b, 1, sXK1);
     } else {
-      copy_k(b, 0, sK1);
+      load_qf(b);
+      copy_k(b, 0, sXK2);
+      copy_x(b, 0, sXK0);
+      if (b.nkb > 1) copy_k(b, 1, sXK0);
     }
   };
 
@@ -756,38 +849,18 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
   if (L < 0) return;  // no block for this workgroup (uniform)
   Blk cur;
   setup(L, cur);
-  copy_q(cur);
   first_copies(cur);
   wait_vmem();
   __syncthreads();
 
   for (;;) {
-    // Query rows of this wave's score tiles as 16x16x32 B operands (zero past dk).
-    bf16x8 qf[SW][8];
-#pragma unroll
-    for (int j = 0; j < SW; ++j) {
-      const int qt = (wave + WAVES * j) & 3;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) qf[j][s] = ld8(sQ + k_swz(qt * 16 + l16, 4 * s + (lane >> 4)));
-    }
-
-    // GroupNorm weight and bias of this wave's columns, loaded before the
-    // tiles so that the first tile's wait covers them.
-    float w[NVT], bb[NVT];
-#pragma unroll
-    for (int nt = 0; nt < NVT; ++nt) {
-      const int vcol = vcol0 + nt * 32 + l32;
-      w[nt] = gn.weight ? gn.weight[cur.h * DV + vcol] : 1.f;
-      bb[nt] = gn.bias ? gn.bias[cur.h * DV + vcol] : 0.f;
-    }
-
     floatx16 acc[2][NVT];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt) acc[qt][nt] = floatx16{};
 
-    const int ns = cur.ns, ntiles = cur.ntiles;
+    const int ns = cur.ns, ntiles = cur.ntiles, nkb = cur.nkb;
 
     // Decay of score (query q, key t): gamma^(q - t) = gamma^(q0 - t0) *
     // gamma^(ql - tl - r), the first factor uniform per key block, the second
@@ -801,72 +874,118 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
       for (int r = 0; r < 4; ++r) flane[j][r] = gpow(cur.lg, static_cast<float>(dl0 - r));
     }
 
-    // Scores of key block kb from K block `kt`: this wave's 16 x 16 tiles of
-    // S^T = K Q^T, decayed and masked, as bf16 into `pdst`. Blocks outside
-    // 0..nkb-1 (zero K rows) write zeros into a buffer nobody reads before it
-    // is rewritten.
     auto score_reads = [&](const uint16_t* kt, bf16x8 (&kfr)[SW][8]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < SW; ++j) {
-        const int tt = (wave + WAVES * j) >> 2;
+      for (int j = 0; j < SW; ++j)
 #pragma unroll
-        for (int s = 0; s < 8; ++s) kfr[j][s] = ld8(kt + k_swz(tt * 16 + l16, 4 * s + (lane >> 4)));
-      }
+        for (int s = 0; s < 8; ++s) kfr[j][s] = ld8(kt + kread[j][s & 3] + 128 * (s >> 2));
     };
-    auto scores = [&](int kb, const bf16x8 (&kfr)[SW][8], uint16_t* pdst) __attribute__((always_inline)) {
+    // Decay, mask and store the scores of key block kb (S^T tiles in sacc).
+    auto score_out = [&](int kb, const floatx4 (&sacc)[SW], uint16_t* pdst) __attribute__((always_inline)) {
       const int dq = cur.q0 - (cur.cs + kb * kTile);
       const float fblock = gpow(cur.lg, static_cast<float>(dq));
 #pragma unroll
       for (int j = 0; j < SW; ++j) {
         const int u = wave + WAVES * j;
         const int qt = u & 3, tt = u >> 2;
-        floatx4 sacc = {};
-#pragma unroll
-        for (int s = 0; s < 8; ++s) sacc = mfma16(kfr[j][s], qf[j][s], sacc);  // zero past dk
         // sacc[r] = S^T[t][q]: t = tt*16 + 4*(lane/16) + r, q = qt*16 + lane%16.
         const int ql = qt * 16 + l16;
         const int tl = tt * 16 + 4 * (lane >> 4);
         float x[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = ql - tl - r >= -dq ? sacc[r] * (fblock * flane[j][r]) : 0.f;
+        for (int r = 0; r < 4; ++r) x[r] = ql - tl - r >= -dq ? sacc[j][r] * (fblock * flane[j][r]) : 0.f;
         uint2 w;
         w.x = pack_bf16x2(x[0], x[1]);
         w.y = pack_bf16x2(x[2], x[3]);
-        *reinterpret_cast<uint2*>(pdst + ql * kPitchP + tl) = w;
+        *reinterpret_cast<uint2*>(pdst + (tl >> 3) * (kRows * 8) + ql * 8 + (tl & 7)) = w;
       }
     };
 
-    // Step i (buffer parity PAR = i & 1): read the LDS operands of tile i and
-    // of the scores of key block i+1-ns; start the copies of X_{i+1} and of
-    // the K block of step i+1's scores into the other buffers (after the
-    // reads, so no read has to wait for them); O += A X_i; the scores; wait
-    // for the copies; barrier.
-    auto step = [&](int i, auto par_tag, auto slice_tag) __attribute__((always_inline)) {
-      constexpr int PAR = decltype(par_tag)::value;
-      constexpr bool kSlice = decltype(slice_tag)::value;
-      uint16_t* xcur = PAR ? sX1 : sX0;
-      uint16_t* xnext = PAR ? sX0 : sX1;
-      uint16_t* kcur = PAR ? sK1 : sK0;
-      uint16_t* knext = PAR ? sK0 : sK1;
-      uint16_t* pcur = PAR ? sP1 : sP0;
-      uint16_t* pnext = PAR ? sP0 : sP1;
+    // Scale chunk-local row j of the read-out by xi_j = gamma^(j+1).
+    // Row j = jb + 32qt + 8(r/4) + r%4 for accumulator r of query tile qt,
+    // jb = q0 - cs + 4*(lane/32). (The empty asm keeps the 32 factors from
+    // being computed ahead of the tile loop and held in registers through it.)
+    auto xi_scale = [&]() __attribute__((always_inline)) {
+      float lg = cur.lg;
+      int jb = cur.q0 - cur.cs + 1 + 4 * (lane >> 5);
+      asm volatile("" : "+v"(lg), "+v"(jb));
+      const float fjb = static_cast<float>(jb);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float xi = gpow(lg, fjb + static_cast<float>(qt * 32 + 8 * (r >> 2) + (r & 3)));
+#pragma unroll
+          for (int nt = 0; nt < NVT; ++nt) acc[qt][nt][r] *= xi;
+        }
+    };
+
+    // Wait for all but this step's n copies (memory operations complete in order).
+    auto wait_keep = [&](int n) __attribute__((always_inline)) {
+      switch (n) {
+        case 1: wait_vm_keep<1>(); break;
+        case 2: wait_vm_keep<2>(); break;
+        case 3: wait_vm_keep<3>(); break;
+        case 4: wait_vm_keep<4>(); break;
+        case 5: wait_vm_keep<5>(); break;
+        case 6: wait_vm_keep<6>(); break;
+        case 7: wait_vm_keep<7>(); break;
+        default: wait_vm_keep<0>(); break;
+      }
+    };
+
+    // Step i (buffer phase PH = i mod 3): read the operands of tile i (A from
+    // the step's score buffer: the Q slice of a state tile or the scores of a
+    // key block) and the K block of the scores of key block i+1-ns; start the
+    // copies of step i+2 into the buffers step i-1 read; O += A X_i; the
+    // scores; wait for all but this step's copies; barrier.
+    auto step = [&](int i, auto ph_tag) __attribute__((always_inline)) {
+      constexpr int PH = decltype(ph_tag)::value;
+      constexpr int PN = (PH + 1) % 3, PF = (PH + 2) % 3;
+      uint16_t* xkcur = pick3<PH>(sXK0, sXK1, sXK2);
+      uint16_t* xkfar = pick3<PF>(sXK0, sXK1, sXK2);
+      uint16_t* pcur = pick3<PH>(sP0, sP1, sP2);
+      uint16_t* pnext = pick3<PN>(sP0, sP1, sP2);
+      uint16_t* pfar = pick3<PF>(sP0, sP1, sP2);
+      const int kb = i + 1 - ns;
+      const bool sc = kb >= 0 && kb < nkb;
       bf16x8 av[2][2], bv[2][NVT];
       if (i >= 0) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
 #pragma unroll
-          for (int qt = 0; qt < 2; ++qt)
-            av[s][qt] = kSlice ? ld8(sQ + k_swz(qt * 32 + l32, 4 * i + 2 * s + (lane >> 5)))
-                               : ld8(pcur + (qt * 32 + l32) * kPitchP + 16 * s + lk);
+          for (int qt = 0; qt < 2; ++qt) av[s][qt] = ld8(pcur + (2 * s + (lane >> 5)) * (kRows * 8) + (qt * 32 + l32) * 8);
 #pragma unroll
-          for (int nt = 0; nt < NVT; ++nt) bv[s][nt] = ld_tr8_x<DV>(xcur, 16 * s, vcol0 + 32 * nt, lane);
+          for (int nt = 0; nt < NVT; ++nt) bv[s][nt] = ld_x(xkcur, s, nt);
+        }
+      }
+      if (i >= 0 && i < ns) {
+        // This slice's columns of the score tiles' query rows.
+#pragma unroll
+        for (int j = 0; j < SW; ++j) {
+          const bf16x8 v = ld8(pcur + (lane >> 4) * (kRows * 8) + (((wave + WAVES * j) & 3) * 16 + l16) * 8);
+          switch (i) {
+            case 0: qf[j][0] = v; break;
+            case 1: qf[j][1] = v; break;
+            case 2: qf[j][2] = v; break;
+            case 3: qf[j][3] = v; break;
+            case 4: qf[j][4] = v; break;
+            case 5: qf[j][5] = v; break;
+            case 6: qf[j][6] = v; break;
+            default: qf[j][7] = v; break;
+          }
         }
       }
       bf16x8 kfr[SW][8];
-      score_reads(kcur, kfr);
+      if (sc) score_reads(xkcur + kTile * DV, kfr);
       __builtin_amdgcn_sched_barrier(0);
-      copy_x(cur, i + 1, xnext);
-      copy_k(cur, i + 2 - ns, knext);
+      const bool cx = i + 2 < ntiles;
+      if (cx) copy_x(cur, i + 2, xkfar);
+      const int kn = i + 3 - ns;
+      const bool ck = kn >= 0 && kn < nkb;
+      if (ck) copy_k(cur, kn, xkfar);
+      const bool cq = i + 2 < ns && wave < QCH;
+      if (cq) copy_qs(cur, i + 2, pfar);
       __builtin_amdgcn_sched_barrier(0);
       if (i >= 0) {
 #pragma unroll
@@ -877,58 +996,64 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
             acc[1][nt] = mfma32(av[s][1], bv[s][nt], acc[1][nt]);
           }
       }
-      scores(i + 1 - ns, kfr, pnext);
-      wait_vmem();
-      __syncthreads();
-    };
-    using P0 = std::integral_constant<int, 0>;
-    using P1 = std::integral_constant<int, 1>;
-    // Steps begin..end-1 as straight-line even/odd pairs (the buffer parity is
-    // a compile-time constant in each).
-    auto run = [&](int begin, int end, auto slice_tag) __attribute__((always_inline)) {
-      int i = begin;
-      if (i < end && (i & 1)) step(i++, P1{}, slice_tag);
-      for (; i + 1 < end; i += 2) {
-        step(i, P0{}, slice_tag);
-        step(i + 1, P1{}, slice_tag);
-      }
-      if (i < end) step(i, P0{}, slice_tag);
-    };
-
-    // With no state slice the first key block's scores are formed in a step
-    // of its own (i = -1) before the first tile.
-    if (ns == 0) step(-1, P1{}, std::false_type{});
-    run(0, ns, std::true_type{});
-    if (ns > 0) {
-      // Scale chunk-local row j of the read-out by xi_j = gamma^(j+1).
+      floatx4 sacc[SW];
+      if (sc) {
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+        for (int j = 0; j < SW; ++j) {
+          sacc[j] = floatx4{};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = cur.q0 + qt * 32 + acc_row(r, lane) - cur.cs;
-          const float xi = gpow(cur.lg, static_cast<float>(j + 1));
-#pragma unroll
-          for (int nt = 0; nt < NVT; ++nt) acc[qt][nt][r] *= xi;
+          for (int s = 0; s < 8; ++s) sacc[j] = mfma16(kfr[j][s], qf[j][s], sacc[j]);  // zero past dk
         }
-    }
-    run(ns, ntiles, std::false_type{});
+      }
+      if (sc) score_out(kb, sacc, pnext);
+      wait_keep((cx ? XI : 0) + (ck ? KI : 0) + (cq ? 1 : 0));
+      lds_barrier();
+    };
+    using H0 = std::integral_constant<int, 0>;
+    using H1 = std::integral_constant<int, 1>;
+    using H2 = std::integral_constant<int, 2>;
 
-    // The tile buffers are free now: request the next block's Q rows and
-    // first tiles before this block's GroupNorm and store.
-    // This block's output rows; then the next block takes over `cur`.
+    int i = 0;
+    if (ns == 0) step(-1, H2{});
+    for (;;) {
+      if (i >= ntiles) break;
+      if (i == ns && ns > 0) xi_scale();
+      step(i++, H0{});
+      if (i >= ntiles) break;
+      if (i == ns && ns > 0) xi_scale();
+      step(i++, H1{});
+      if (i >= ntiles) break;
+      if (i == ns && ns > 0) xi_scale();
+      step(i++, H2{});
+    }
+
+    // This block's output rows; then the next block takes over `cur` and its
+    // first copies go out before this block's GroupNorm and store (which use
+    // no buffer those copies write: the statistics live in sP2).
     uint16_t* const oblk = a.o + (cur.bh * a.N + cur.q0) * static_cast<int64_t>(DV);
     const int oq = cur.qvalid;
+    // GroupNorm weight and bias of this wave's columns, requested before the
+    // next block's copies so that waiting for them does not wait for those.
+    const bool affine = gn.enabled && (gn.weight || gn.bias);
+    float w[NVT], bb[NVT];
+    if (affine) {
+#pragma unroll
+      for (int nt = 0; nt < NVT; ++nt) {
+        const int vcol = vcol0 + nt * 32 + l32;
+        w[nt] = gn.weight ? gn.weight[cur.h * DV + vcol] : 1.f;
+        bb[nt] = gn.bias ? gn.bias[cur.h * DV + vcol] : 0.f;
+      }
+    }
     const int Ln = block_of(++it);
     if (Ln >= 0) {
       setup(Ln, cur);
-      copy_q(cur);
       first_copies(cur);
     }
     __builtin_amdgcn_sched_barrier(0);
 
     // Optional per-head GroupNorm over the DV columns of each row.
     if (gn.enabled) {
-      float* s_stat = reinterpret_cast<float*>(sP0);  // [WAVES][64], then mean[64], rstd[64]
+      float* s_stat = reinterpret_cast<float*>(sP2);  // [WAVES][64], then mean[64], rstd[64]
       float* s_mean = s_stat + WAVES * kRows;        // the mean, later -mean * rstd
       float* s_rstd = s_mean + kRows;
       // Each lane holds 32 row slots (query tile qt, accumulator r); a
@@ -957,7 +1082,7 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
         if (threadIdx.x < kRows) {
           float t = 0.f;
 #pragma unroll
-          for (int w = 0; w < WAVES; ++w) t += s_stat[w * kRows + threadIdx.x];
+          for (int w2 = 0; w2 < WAVES; ++w2) t += s_stat[w2 * kRows + threadIdx.x];
           t /= DV;
           if (pass == 0) {
             s_mean[threadIdx.x] = t;
@@ -970,7 +1095,6 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
         lds_barrier();
       }
       // (x - mean) * rstd as one multiply-add per value, then the affine map.
-      const bool affine = gn.weight || gn.bias;
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
@@ -994,10 +1118,9 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
     // column. Packed to bf16 pairs, one exchange with the neighbouring lane
     // (DPP) and a byte permute give each lane two adjacent columns of one row
     // (the even lane row rho, the odd lane row rho+1), written as one 4-byte
-    // store. Rows
-    // go out in groups of eight (qt*32 + 8g ..), each through a descriptor
-    // whose range ends at the block's last valid row, so the lane offsets are
-    // the same for every group.
+    // store. Rows go out in groups of eight (qt*32 + 8g ..), each through a
+    // descriptor whose range ends at the block's last valid row, so the lane
+    // offsets are the same for every group.
     {
       const bool odd = lane & 1;
       const int voff = ((4 * (lane >> 5) + (odd ? 1 : 0)) * DV + vcol0 + (l32 & ~1)) * 2;
@@ -1009,8 +1132,7 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int row0 = qt * 32 + 8 * g;
-          const __amdgpu_buffer_rsrc_t r =
-              make_rsrc(oblk + row0 * DV, min(max(oq - row0, 0), 8) * DV * 2);
+          const __amdgpu_buffer_rsrc_t r = make_rsrc(oblk + row0 * DV, min(max(oq - row0, 0), 8) * DV * 2);
 #pragma unroll
           for (int nt = 0; nt < NVT; ++nt)
 #pragma unroll
@@ -1026,10 +1148,10 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
     }
 
     if (Ln < 0) break;
-    // The next block's copies were issued before this block's O stores: wait
-    // for everything but those stores.
-    __builtin_amdgcn_s_waitcnt((OSTORES & 15) | ((OSTORES >> 4) << 14) | 0x70 | 0xF00);
-    __syncthreads();
+    // The next block's copies and loads were issued before this block's O
+    // stores: wait for everything but those stores.
+    wait_vm_keep<OSTORES>();
+    lds_barrier();
   }
 }
 

@@ -143,20 +143,6 @@ __device__ __forceinline__ int k_swz(int row, int g) { return row * 256 + ((g ^ 
 // 64-byte bank groups.
 __device__ __forceinline__ int x_pos(int row, int g) { return g ^ ((row & 3) << 2); }
 
-// Transposed MFMA operand (see ld_tr8) from an unpadded, swizzled X tile with
-// DV columns.
-template <int DV>
-__device__ __forceinline__ bf16x8 ld_tr8_x(const uint16_t* tile, int row0, int col0, int lane) {
-  const int g = lane >> 4, j = lane & 15;
-  const int row = row0 + 8 * (g >> 1) + (j >> 2);
-  const int col = col0 + 16 * (g & 1) + 4 * (j & 3);
-  const uint16_t* p = tile + row * DV + (x_pos(row, col >> 3) << 3) + (col & 7);
-  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p));
-  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p + 4 * DV));  // row+4: same swizzle
-  const shortx8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
-}
-
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
@@ -164,6 +150,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 // global side is `byte_offset` into the descriptor's range (zeros past it).
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds_chunk, int byte_offset) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds_chunk), 16, byte_offset, 0, 0, 0);
+}
+// The same with a wave-uniform part of the offset in a scalar register.
+__device__ __forceinline__ void dma16s(__amdgpu_buffer_rsrc_t r, uint16_t* lds_chunk, int byte_offset,
+                                       int uniform_offset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds_chunk), 16, byte_offset, uniform_offset, 0, 0);
 }
 
 }  // namespace
