@@ -27,6 +27,10 @@ B=2 H=8 N=2048, `long_sequence` the chunkwise form at B=1 H=16 from 8k to 64k
 tokens and chunk 64..512, each with its binding-roofline fraction.
 `cpu_baseline` is the fp64 CPU oracle on a bounded sample of the prefill
 (plus, under `other_cases`, the decode step and the B=2 chunkwise case).
+
+The default 30 untimed warm-up steps (about 60 ms of load) let the GPU reach
+its sustained clocks first: from idle, the first 40 ms or so of this workload
+run up to 20% slower.
 """
 
 from __future__ import annotations
@@ -320,7 +324,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-batch-rows", type=int, default=8)
