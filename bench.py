@@ -144,11 +144,14 @@ LONG_LENGTHS = (8192, 16384, 32768, 65536)
 LONG_CHUNKS = (64, 128, 256, 512)
 
 
-def long_sequence_sweep(ret, synthetic, dev, reps=5):
+def long_sequence_sweep(ret, synthetic, dev, min_reps=5, warm_s=0.05, timed_s=0.02):
     """Tokens/s of the chunkwise forward (GroupNorm, fp32 state out) for one
     batch row of 16 heads as the sequence grows (chunk 512), and across chunk
-    sizes at 65,536 tokens. Each point: HIP events around `reps` calls after
-    one warm-up call."""
+    sizes at 65,536 tokens. Each point: calls back to back for `warm_s`
+    seconds first (the clocks drop while the GPU idles, e.g. during the CPU
+    baseline, and the shortest points last well under a millisecond), then
+    HIP events around at least `min_reps` calls and at least `timed_s`
+    seconds of them."""
     import torch
 
     H_ = 16
@@ -164,8 +167,15 @@ def long_sequence_sweep(ret, synthetic, dev, reps=5):
         st = torch.empty(1, H_, DK, DV, dtype=torch.float32, device=dev)
         ws = torch.empty(ret.chunkwise_workspace_bytes(1, H_, n, DK, DV, chunk), dtype=torch.uint8, device=dev)
         f = lambda: ret.chunkwise(qs, ks, vs, gamma, chunk, state_out=st, gn=gn, out=out, workspace=ws)
-        f()
-        torch.cuda.synchronize()
+        t0, calls = time.perf_counter(), 0
+        while True:
+            f()
+            calls += 1
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= warm_s:
+                break
+        per_call = (time.perf_counter() - t0) / calls
+        reps = max(min_reps, int(timed_s / per_call) + 1)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
@@ -177,7 +187,7 @@ def long_sequence_sweep(ret, synthetic, dev, reps=5):
         byts = output_bytes(1, H_, n, chunk) + walk_bytes(1, H_, n, chunk)
         # The binding roof of the whole forward: min(MFMA peak, AI * HBM peak).
         roof = min(PEAK_BF16, flop / byts * PEAK_HBM)
-        return {"N": n, "chunk": chunk, "ms": ms, "tokens_per_s": n / (ms * 1e-3),
+        return {"N": n, "chunk": chunk, "ms": ms, "reps": reps, "tokens_per_s": n / (ms * 1e-3),
                 "algorithmic_flop": flop, "algorithmic_bytes": byts,
                 "binding_roof": "mfma" if roof == PEAK_BF16 else "hbm",
                 "binding_roof_frac": flop / (ms * 1e-3) / roof}
@@ -193,11 +203,12 @@ def long_sequence_sweep(ret, synthetic, dev, reps=5):
     }
 
 
-def small_config(ret, synthetic, dev, reps=20):
+def small_config(ret, synthetic, dev, reps=200, warm_s=0.05):
     """The 1.3B-shaped case (B=2, H=8, N=2048, dk=256, dv=512, chunk 256,
     bf16, seed 1002): parallel and chunkwise forward, µs per call from HIP
-    events around `reps` calls after two warm-up calls, with tokens/s and the
-    binding-roofline fraction (algorithmic flop and bytes as for the prefill)."""
+    events around `reps` calls after `warm_s` seconds of calls back to back
+    (clocks settle), with tokens/s and the binding-roofline fraction
+    (algorithmic flop and bytes as for the prefill)."""
     import torch
 
     b, h, n, c = 2, 8, 2048, 256
@@ -208,9 +219,10 @@ def small_config(ret, synthetic, dev, reps=20):
     ws = torch.empty(ret.chunkwise_workspace_bytes(b, h, n, DK, DV, c), dtype=torch.uint8, device=dev)
 
     def timed(f):
-        for _ in range(2):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < warm_s:
             f()
-        torch.cuda.synchronize()
+            torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
