@@ -26,7 +26,9 @@ the Infinity Cache. `small_config` times the parallel and chunkwise forms at
 B=2 H=8 N=2048, `long_sequence` the chunkwise form at B=1 H=16 from 8k to 64k
 tokens and chunk 64..512, each with its binding-roofline fraction.
 `cpu_baseline` is the fp64 CPU oracle on a bounded sample of the prefill
-(plus, under `other_cases`, the decode step and the B=2 chunkwise case).
+(plus, under `other_cases`, the decode step, the B=2 chunkwise case and the
+65,536-token B=1 chunkwise case). `device` records the GPU, the HIP and torch
+versions and the clocks rocm-smi reports after the timed work.
 
 The default 30 untimed warm-up steps (about 60 ms of load) let the GPU reach
 its sustained clocks first: from idle, the first 40 ms or so of this workload
@@ -194,12 +196,17 @@ def long_sequence_sweep(ret, synthetic, dev, min_reps=5, warm_s=0.05, timed_s=0.
 
     by_length = [run(n, 512) for n in LONG_LENGTHS]
     by_chunk = [run(max(LONG_LENGTHS), c) for c in LONG_CHUNKS]
+    by_chunk_short = [run(min(LONG_LENGTHS), c) for c in LONG_CHUNKS]
     tps = [r["tokens_per_s"] for r in by_length]
     return {
         "workload": "B=1 H=16 dk=256 dv=512 bf16, GroupNorm, fp32 state out",
         "by_length_chunk512": by_length,
         "by_chunk_N65536": by_chunk,
+        "by_chunk_N8192": by_chunk_short,
         "flatness_min_over_max": min(tps) / max(tps),
+        # tokens/s at the longest length over tokens/s at the shortest, per chunk size
+        "flatness_by_chunk": {str(c): hi["tokens_per_s"] / lo["tokens_per_s"]
+                              for c, lo, hi in zip(LONG_CHUNKS, by_chunk_short, by_chunk)},
     }
 
 
@@ -279,8 +286,9 @@ def decode_cache_defeating(ret, synthetic, dev, steps=64):
 
 def cpu_extra(synthetic, gamma):
     """The fp64 oracle on the other measured cases: the decode step over all
-    B*H heads (16 steps from a random state) and the 1.3B-shaped chunkwise
-    forward in full."""
+    B*H heads (16 steps from a random state), the 1.3B-shaped chunkwise
+    forward in full and the 65,536-token B=1 chunkwise forward (chunk 512,
+    GroupNorm) in full."""
     import torch
 
     from oracle import retention_oracle as orc
@@ -299,9 +307,38 @@ def cpu_extra(synthetic, gamma):
     t0 = time.perf_counter()
     orc.chunkwise(q2, k2, v2, synthetic.head_gammas(8), 256)
     small_s = time.perf_counter() - t0
+    n_long = max(LONG_LENGTHS)
+    q3, k3, v3 = synthetic.make_qkv(1, H, n_long, DK, DV, dtype=torch.bfloat16, seed=SEED + 7)
+    t0 = time.perf_counter()
+    o3, _ = orc.chunkwise(q3, k3, v3, synthetic.head_gammas(H), CHUNK)
+    orc.group_norm(o3, eps=1e-5)
+    long_s = time.perf_counter() - t0
     return {"decode_us_per_step": dec_us, "decode_workload": f"B={B} H={H} dk={DK} dv={DV}, 16 steps",
             "small_chunkwise_s": small_s, "small_tokens_per_s": 2 * 2048 / small_s,
-            "small_workload": "B=2 H=8 N=2048 dk=256 dv=512 chunk 256"}
+            "small_workload": "B=2 H=8 N=2048 dk=256 dv=512 chunk 256",
+            "long_chunkwise_s": long_s, "long_tokens_per_s": n_long / long_s,
+            "long_workload": f"B=1 H={H} N={n_long} dk={DK} dv={DV} chunk {CHUNK}, GroupNorm"}
+
+
+def device_info():
+    """GPU name and architecture, HIP and torch versions, and the clocks rocm-smi
+    reports right after the timed work (None where unavailable)."""
+    import subprocess
+
+    import torch
+
+    props = torch.cuda.get_device_properties(0)
+    info = {"name": props.name, "arch": getattr(props, "gcnArchName", None), "hip": torch.version.hip,
+            "torch": torch.__version__, "rocm_smi_clocks": None}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        if r.returncode == 0:
+            data = json.loads(r.stdout)
+            card = next(iter(data.values())) if data else {}
+            info["rocm_smi_clocks"] = {k: v for k, v in card.items() if "clock" in k.lower()}
+    except (OSError, ValueError, subprocess.SubprocessError, StopIteration):
+        pass
+    return info
 
 
 def cpu_baseline(q, k, v, gamma, n_batch_rows=2):
@@ -535,6 +572,7 @@ def main():
         "small_config": small,
         "long_sequence": long_seq,
         "cpu_baseline": cpu,
+        "device": device_info(),
         "wall_s_timed": wall,
     }
     print(json.dumps(line), flush=True)
