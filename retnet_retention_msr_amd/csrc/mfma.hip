@@ -649,7 +649,7 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
   constexpr int XI = XCH / WAVES, KI = KCH / WAVES;  // chunks copied per wave
   constexpr int GPR = DV / 8;                      // 16-byte granules per X row
   constexpr int PT = kRows * kTile;                // elements of a score tile
-  constexpr int QCH = PT * 2 / 1024;               // 1-KiB chunks of a Q slice (one per granule column)
+  constexpr int QCH = PT * 2 / 1024;               // 1-KiB chunks of a Q slice (16 rows each)
   constexpr int XK = kTile * DV + kTile * 256;     // elements of one X + K buffer
   constexpr int OSTORES = 2 * NVT * 8;             // 4-byte O stores per lane and block
   static_assert(XI >= 1 && KI >= 1 && XCH % WAVES == 0 && KCH % WAVES == 0 && QCH <= WAVES, "layout");
@@ -660,8 +660,9 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
   __shared__ __attribute__((aligned(1024))) uint16_t sXK0[XK];
   __shared__ __attribute__((aligned(1024))) uint16_t sXK1[XK];
   __shared__ __attribute__((aligned(1024))) uint16_t sXK2[XK];
-  // Scores (or a Q slice) as [8-column granule][row][8]: the 16-byte operand
-  // reads of consecutive rows are contiguous.
+  // Scores (or a Q slice), row-major with 64-byte rows of four 16-byte
+  // granules, granule g of row r at slot g ^ ((r / 4) % 4) (p_off below), so the
+  // 16-byte operand reads of 16 consecutive rows hit 16 different bank groups.
   __shared__ __attribute__((aligned(1024))) uint16_t sP0[PT];
   __shared__ __attribute__((aligned(1024))) uint16_t sP1[PT];
   __shared__ __attribute__((aligned(1024))) uint16_t sP2[PT];
@@ -715,9 +716,34 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
     const int g = pos ^ (row & 15);
     koff[m] = g * 8 < dk ? (row * dk + g * 8) * 2 : kOutOfRange;
   }
-  // Q slice: piece g (one per wave below QCH) holds columns 8g..8g+7 of the
-  // slice for the 64 rows, lane l row l.
-  const int qsoff = lane * dk * 2;
+  // Score-buffer element offset of granule g (8 columns) of row r.
+  auto p_off = [](int r, int g) __attribute__((always_inline)) { return r * kTile + ((g ^ ((r >> 2) & 3)) << 3); };
+  // Q slice: piece w (one per wave below QCH) holds rows 16w..16w+15, lane l
+  // slot l%4 of row 16w + l/4, so each lane reads 16 of the row's 64
+  // contiguous bytes (the granule that lands in that slot).
+  int qsoff;
+  {
+    const int row = wave * 16 + (lane >> 2), slot = lane & 3;
+    qsoff = (row * dk + 8 * (slot ^ ((row >> 2) & 3))) * 2;
+  }
+  // Per-lane score-buffer offsets (elements), fixed for the kernel and kept
+  // opaque (see xo): the A operand of step half s and query tile qt (rows
+  // qt*32 + lane%32, granule 2s + lane/32), and the Q rows of score tile j
+  // (rows ((wave + WAVES*j) % 4)*16 + lane%16, granule lane/16).
+  int pa[2][2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      pa[s2][qt] = p_off(qt * 32 + l32, 2 * s2 + (lane >> 5));
+      asm volatile("" : "+v"(pa[s2][qt]));
+    }
+  int pq[SW];
+#pragma unroll
+  for (int j = 0; j < SW; ++j) {
+    pq[j] = p_off(((wave + WAVES * j) & 3) * 16 + l16, lane >> 4);
+    asm volatile("" : "+v"(pq[j]));
+  }
   // Score tile rows of Q: row (u % 4)*16 + lane%16 of tile u = wave + WAVES*j,
   // from granule lane/16 on.
   int qfoff[SW];
@@ -796,10 +822,10 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
     for (int m = 0; m < KI; ++m) dma16(r, dst + kTile * DV + (wave + WAVES * m) * 512, koff[m]);
   };
   // Columns 32s..32s+31 of the block's Q rows (zero past N) into score buffer
-  // `dst`; waves below QCH copy one granule column each.
+  // `dst`; waves below QCH copy 16 rows each.
   auto copy_qs = [&](const Blk& b, int s, uint16_t* dst) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(b.qbase, b.qvalid * dk * 2);
-    dma16s(r, dst + wave * 512, qsoff, (s * kTile + wave * 8) * 2);
+    dma16s(r, dst + wave * 512, qsoff, s * kTile * 2);
   };
   // The 16 query rows of each of this wave's score tiles as 16x16x32 B
   // operands (zero past N and past dk): step s holds Q columns 32s.. . A block
@@ -897,7 +923,7 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
         uint2 w;
         w.x = pack_bf16x2(x[0], x[1]);
         w.y = pack_bf16x2(x[2], x[3]);
-        *reinterpret_cast<uint2*>(pdst + (tl >> 3) * (kRows * 8) + ql * 8 + (tl & 7)) = w;
+        *reinterpret_cast<uint2*>(pdst + p_off(ql, tl >> 3) + (tl & 7)) = w;
       }
     };
 
@@ -954,7 +980,7 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
 #pragma unroll
-          for (int qt = 0; qt < 2; ++qt) av[s][qt] = ld8(pcur + (2 * s + (lane >> 5)) * (kRows * 8) + (qt * 32 + l32) * 8);
+          for (int qt = 0; qt < 2; ++qt) av[s][qt] = ld8(pcur + pa[s][qt]);
 #pragma unroll
           for (int nt = 0; nt < NVT; ++nt) bv[s][nt] = ld_x(xkcur, s, nt);
         }
@@ -963,7 +989,7 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
         // This slice's columns of the score tiles' query rows.
 #pragma unroll
         for (int j = 0; j < SW; ++j) {
-          const bf16x8 v = ld8(pcur + (lane >> 4) * (kRows * 8) + (((wave + WAVES * j) & 3) * 16 + l16) * 8);
+          const bf16x8 v = ld8(pcur + pq[j]);
           switch (i) {
             case 0: qf[j][0] = v; break;
             case 1: qf[j][1] = v; break;
