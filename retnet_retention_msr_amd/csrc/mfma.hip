@@ -612,10 +612,14 @@ __device__ __forceinline__ void wait_vm_keep() {
 // accumulator tiles).
 //
 // Block order: the blocks are split into one contiguous range per XCD (so the
-// eight query blocks of a chunk, which read the same K, V and state, meet in
-// one L2), and the workgroups of an XCD take the range in groups of their
-// count, each workgroup one block per group, rotated by one place per group so
-// every workgroup sees every position within a chunk (their work differs).
+// query blocks of a chunk, which read the same K, V and state, meet in one
+// L2), and the workgroups of an XCD take the range in groups of their count,
+// each workgroup one block per group. The work per block grows along the
+// chunk, so the assignment within a group moves between groups: rotated by one
+// place per group when there are several chunks (every workgroup sweeps the
+// positions of a chunk), reversed on every other group when one chunk spans
+// the sequence (the parallel form: a workgroup that drew a late, long block
+// next draws an early, short one).
 //
 // A block's work is a sequence of steps, each multiplying a 32-row bf16 tile
 // X in LDS into O as O += A X: first the dk/32 slices of the stored chunk
@@ -767,7 +771,8 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
   const int per = (a.nblocks + nx - 1) / nx;
   const int lo = min(a.nblocks, xcd * per), hi = min(a.nblocks, lo + per);
   auto block_of = [&](int it) __attribute__((always_inline)) {
-    const int L = lo + it * nwg + (slot + it) % nwg;
+    const int pos = a.nchunks > 1 ? (slot + it) % nwg : ((it & 1) ? nwg - 1 - slot : slot);
+    const int L = lo + it * nwg + pos;
     return L < hi ? L : -1;
   };
 
