@@ -81,8 +81,8 @@ ChunkPlan plan_chunkwise(int B, int H, int N, int dk, int dv, int chunk, int dty
   const size_t heads = static_cast<size_t>(B) * H;
   const size_t dkdv = static_cast<size_t>(dk) * dv;
   if (p.mfma) {
-    const int64_t per_seg = static_cast<int64_t>(heads) * ret::walk_tiles_per_head(dk, dv);
-    int64_t want = (kWalkTargetBlocks + per_seg - 1) / per_seg;
+    const int64_t per_seg = static_cast<int64_t>(heads) * ret::walk_tiles_per_head(heads, dk, dv);
+    int64_t want = ret::walk_wide(heads, dk, dv) ? 1 : (kWalkTargetBlocks + per_seg - 1) / per_seg;
     if (want < 1) want = 1;
     if (want > p.nchunks) want = p.nchunks;
     p.chunks_per_seg = static_cast<int>((p.nchunks + want - 1) / want);

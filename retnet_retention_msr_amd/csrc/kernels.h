@@ -46,9 +46,13 @@ hipError_t launch_mfma_state_walk(const uint16_t* k, const uint16_t* v, const fl
                                   const Dims& d, int chunk, const HeadDecay& decay, hipStream_t stream);
 
 // k-tile height of the walk is 32 * walk_k_tiles(dk); walk_tiles_per_head is
-// the number of workgroups per head and segment.
+// the number of workgroups per head and segment for `heads` = B*H heads.
+// walk_wide: the full-dk walk takes 256 v columns per workgroup, used when
+// those workgroups alone are enough to fill the GPU (the walk is then not
+// segmented); otherwise 128.
 int walk_k_tiles(int dk);
-int walk_tiles_per_head(int dk, int dv);
+bool walk_wide(int64_t heads, int dk, int dv);
+int walk_tiles_per_head(int64_t heads, int dk, int dv);
 
 // bf16 MFMA output: per 64-row query block, intra-chunk causal product plus the
 // read-out of the bf16 chunk state (when chunk_states is non-null), then the

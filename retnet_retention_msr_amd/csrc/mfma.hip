@@ -293,26 +293,29 @@ __global__ void __launch_bounds__(kThreads) mfma_state_walk_kernel(WalkArgs a, H
 // ---------------------------------------------------------------------------
 // State walk, full-dk form (dk = 128 or 256)
 // ---------------------------------------------------------------------------
-// One workgroup of eight waves per (head, 128-column v tile, segment) owns the
-// whole dk x 128 slab of R: wave (kw, vw) keeps rows 32*MTW*kw.. and columns
-// 64*vw.. (MTW x 2 accumulator tiles), so each V row is read once and each K
-// row once per v tile. 64-key blocks are double-buffered in LDS (register
-// staging, zeta applied to V rows on the way), one barrier per block.
+// One workgroup of eight waves per (head, 64*NTW-column v tile, segment) owns
+// the whole dk x 64*NTW slab of R: wave (kw, vw) keeps rows 32*MTW*kw.. and
+// columns 32*NTW*vw.. (MTW x NTW accumulator tiles), so each V row is read once
+// and each K row once per v tile. 64-key blocks are double-buffered in LDS
+// (register staging, zeta applied to V rows on the way), one barrier per block.
+// The V tile is unpadded with its 16-byte granules XOR-swizzled by the row, so
+// the transposed operand reads of four consecutive rows hit four bank groups.
 constexpr int kWalk2Threads = 512;
-constexpr int kWalk2VT = 128;      // v columns per workgroup
-constexpr int kWalk2PV = 160;      // sV pitch: 320 B, rows 64 B apart mod 256
+constexpr int kWalk2VT = 128;      // v columns per workgroup at NTW = 2
 constexpr int kWalk2PP = 36;       // store patch pitch: 72 B, 32 rows start on distinct bank pairs
 
 
-template <int MTW>
+template <int MTW, int NTW>
 __global__ void __launch_bounds__(kWalk2Threads) mfma_state_walk2_kernel(WalkArgs a, HeadDecay decay) {
   constexpr int NT = kWalk2Threads;
   constexpr int DK = 128 * MTW;
   constexpr int PK = DK + 32;                  // sK pitch: rows 64 B apart mod 256
   constexpr int KP = kRows * DK / 8 / NT;      // 16-byte pieces per thread of a K block
-  constexpr int VP = kRows * kWalk2VT / 8 / NT;  // ... of a V block
+  constexpr int VT = 64 * NTW;                 // v columns per workgroup
+  constexpr int VGPR = VT / 8;                 // 16-byte granules per V row
+  constexpr int VP = kRows * VT / 8 / NT;      // ... of a V block
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kRows * PK];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kRows * kWalk2PV];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kRows * VT];
   __shared__ __attribute__((aligned(16))) uint16_t sPatch[8][32 * kWalk2PP];  // per-wave store patch
 
   const int lane = threadIdx.x & 63;
@@ -326,18 +329,18 @@ __global__ void __launch_bounds__(kWalk2Threads) mfma_state_walk2_kernel(WalkArg
   const int64_t bh = idx / nseg_launch;
   const int h = static_cast<int>(bh % a.H);
   const float lg = decay.log2g[h];
-  const int v0 = vt * kWalk2VT;
+  const int v0 = vt * VT;
   const int krow0 = kw * 32 * MTW;                 // this wave's first state row
-  const int vcol = v0 + vw * 64 + (lane & 31);     // state column of accumulator tile 0
+  const int vcol = v0 + vw * 32 * NTW + (lane & 31);  // state column of accumulator tile 0
   const int c_begin = seg * a.chunks_per_seg;
   const int c_end = min(a.nchunks, c_begin + a.chunks_per_seg);
   const int64_t dkdv = static_cast<int64_t>(DK) * a.dv;
 
-  floatx16 acc[MTW][2];
+  floatx16 acc[MTW][NTW];
 #pragma unroll
   for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = floatx16{};
+    for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = floatx16{};
 
   auto state_at = [&](const float* S, int mt, int nt, int r) -> float {
     return S[static_cast<int64_t>(krow0 + mt * 32 + acc_row(r, lane)) * a.dv + vcol + 32 * nt];
@@ -348,7 +351,7 @@ __global__ void __launch_bounds__(kWalk2Threads) mfma_state_walk2_kernel(WalkArg
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mt][nt][r] = state_at(S0, mt, nt, r);
   } else if (a.mode == 1) {
@@ -362,7 +365,7 @@ __global__ void __launch_bounds__(kWalk2Threads) mfma_state_walk2_kernel(WalkArg
 #pragma unroll
       for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[mt][nt][r] = fmaf(f, state_at(U, mt, nt, r), acc[mt][nt][r]);
     }
@@ -376,12 +379,30 @@ __global__ void __launch_bounds__(kWalk2Threads) mfma_state_walk2_kernel(WalkArg
   const uint16_t* kb = a.k + bh * static_cast<int64_t>(a.N) * DK;
   const uint16_t* vb = a.v + bh * static_cast<int64_t>(a.N) * a.dv + v0;
   TileRegs<KP, NT, DK> rk;
-  TileRegs<VP, NT, kWalk2VT> rv;
+  TileRegs<VP, NT, VT> rv;
   // zeta_t = gamma^(L-1-t) = gamma^(L-1-t0) * gamma^(-r) for row r of a block
   // at t0; the gamma^(-r) factors of this thread's V rows are fixed.
   float zrow[VP];
 #pragma unroll
-  for (int m = 0; m < VP; ++m) zrow[m] = gpow(lg, -static_cast<float>(TileRegs<VP, NT, kWalk2VT>::row_of(m)));
+  for (int m = 0; m < VP; ++m) zrow[m] = gpow(lg, -static_cast<float>(TileRegs<VP, NT, VT>::row_of(m)));
+  // LDS positions of this thread's V pieces in the swizzled tile, and the
+  // per-lane parts of the transposed V operand reads (rows 8*(lane/32) +
+  // (lane%16)/4 of columns 32*NTW*vw + 32nt + 16*((lane/16)%2) + 4*(lane%4)..;
+  // a step of 16 rows or 4 rows keeps the swizzle).
+  int vput[VP];
+#pragma unroll
+  for (int m = 0; m < VP; ++m) {
+    const int row = TileRegs<VP, NT, VT>::row_of(m), g = TileRegs<VP, NT, VT>::col_of(m) / 8;
+    vput[m] = row * VT + (x_pos(row, g) << 3);
+  }
+  int vread[NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int g = lane >> 4, j = lane & 15;
+    const int row = 8 * (g >> 1) + (j >> 2);
+    const int col = vw * 32 * NTW + 32 * nt + 16 * (g & 1) + 4 * (j & 3);
+    vread[nt] = row * VT + (x_pos(row, col >> 3) << 3) + (col & 7);
+  }
 
   // Blocks are (chunk, 64-row block) pairs in sequence order; `load` fetches
   // block (c, t0) into registers, `put` stores it scaled into LDS buffer b.
@@ -390,7 +411,7 @@ __global__ void __launch_bounds__(kWalk2Threads) mfma_state_walk2_kernel(WalkArg
     const int L = min(a.chunk, a.N - cs);
     const int nvalid = min(kRows, L - t0);
     rk.load(kb + static_cast<int64_t>(cs + t0) * DK, DK, nvalid, DK);
-    rv.load(vb + static_cast<int64_t>(cs + t0) * a.dv, a.dv, nvalid, kWalk2VT);
+    rv.load(vb + static_cast<int64_t>(cs + t0) * a.dv, a.dv, nvalid, VT);
   };
   auto put = [&](int c, int t0, int b) {
     const int L = min(a.chunk, a.N - c * a.chunk);
@@ -399,7 +420,15 @@ __global__ void __launch_bounds__(kWalk2Threads) mfma_state_walk2_kernel(WalkArg
 #pragma unroll
     for (int m = 0; m < VP; ++m) z[m] = z0 * zrow[m];
     rk.store(sK[b], PK);
-    rv.store_scaled(sV[b], kWalk2PV, z);
+    // V rows scaled by zeta into their swizzled places.
+#pragma unroll
+    for (int m = 0; m < VP; ++m) {
+      u32x4 w = rv.p[m];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = pack_bf16x2(__uint_as_float(w[e] << 16) * z[m], __uint_as_float(w[e] & 0xffff0000u) * z[m]);
+      *reinterpret_cast<u32x4*>(sV[b] + vput[m]) = w;
+    }
   };
   auto advance = [&](int& c, int& t0) {
     t0 += kRows;
@@ -434,7 +463,7 @@ __global__ void __launch_bounds__(kWalk2Threads) mfma_state_walk2_kernel(WalkArg
 #pragma unroll
         for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
+          for (int nt = 0; nt < NTW; ++nt) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               uint2 w;
@@ -446,7 +475,7 @@ __global__ void __launch_bounds__(kWalk2Threads) mfma_state_walk2_kernel(WalkArg
             for (int half = 0; half < 2; ++half) {
               const bf16x8 v8 = ld_tr8(patch, kWalk2PP, 16 * half, 0, lane);
               const int row = krow0 + mt * 32 + (lane & 31);
-              const int col = v0 + vw * 64 + nt * 32 + 16 * half + 8 * (lane >> 5);
+              const int col = v0 + vw * 32 * NTW + nt * 32 + 16 * half + 8 * (lane >> 5);
               buffer_store16(rs, (row * a.dv + col) * 2, v8);
             }
           }
@@ -455,7 +484,7 @@ __global__ void __launch_bounds__(kWalk2Threads) mfma_state_walk2_kernel(WalkArg
 #pragma unroll
       for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] *= carry;
+        for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] *= carry;
     }
     // U += K^T (zeta V) over the block's 64 keys.
     auto multiply = [&]() {
@@ -463,15 +492,19 @@ __global__ void __launch_bounds__(kWalk2Threads) mfma_state_walk2_kernel(WalkArg
       const uint16_t* vt_ = sV[buf];
 #pragma unroll
       for (int s = 0; s < kRows / 16; ++s) {
-        bf16x8 bv[2], av[MTW];
+        bf16x8 bv[NTW], av[MTW];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) bv[nt] = ld_tr8(vt_, kWalk2PV, s * 16, vw * 64 + 32 * nt, lane);
+        for (int nt = 0; nt < NTW; ++nt) {
+          const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(vt_ + vread[nt] + s * 16 * VT));
+          const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(vt_ + vread[nt] + (s * 16 + 4) * VT));
+          bv[nt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
 #pragma unroll
         for (int mt = 0; mt < MTW; ++mt) av[mt] = ld_tr8(kt, PK, s * 16, krow0 + mt * 32, lane);
 #pragma unroll
         for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32(av[mt], bv[nt], acc[mt][nt]);
+          for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = mfma32(av[mt], bv[nt], acc[mt][nt]);
       }
     };
     // The next block goes into the other buffer (read one block ago), the
@@ -514,7 +547,7 @@ __global__ void __launch_bounds__(kWalk2Threads) mfma_state_walk2_kernel(WalkArg
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           out[static_cast<int64_t>(krow0 + mt * 32 + acc_row(r, lane)) * a.dv + vcol + 32 * nt] = acc[mt][nt][r];
@@ -1208,8 +1241,17 @@ bool walk_fixup_segments(int chunk, int dk, int dv) {
 // The full-dk walk covers dk = 128 and 256 with one workgroup per 128 v columns.
 bool walk_full_dk(int dk) { return dk == 128 || dk == 256; }
 
-int walk_tiles_per_head(int dk, int dv) {
-  if (walk_full_dk(dk)) return dv / kWalk2VT;
+// 256 v columns per workgroup (each K row then crosses from L2 to LDS dv/256
+// times instead of dv/128, and a wave's 64 x 128 accumulator slab halves the
+// LDS operand reads per product) when those workgroups alone fill the GPU;
+// with fewer heads, 128-column workgroups and segments give more parallelism.
+constexpr int64_t kWalkWideBlocks = 256;
+bool walk_wide(int64_t heads, int dk, int dv) {
+  return walk_full_dk(dk) && dv % 256 == 0 && heads * (dv / 256) >= kWalkWideBlocks;
+}
+
+int walk_tiles_per_head(int64_t heads, int dk, int dv) {
+  if (walk_full_dk(dk)) return dv / (walk_wide(heads, dk, dv) ? 256 : kWalk2VT);
   return (dk / (32 * walk_k_tiles(dk))) * (dv / kWalkVT);
 }
 
@@ -1234,14 +1276,17 @@ hipError_t launch_mfma_state_walk(const uint16_t* k, const uint16_t* v, const fl
   const bool full = walk_full_dk(d.dk);
   const int MT = walk_k_tiles(d.dk);
   a.nkt = full ? 1 : d.dk / (32 * MT);
-  a.nvt = d.dv / (full ? kWalk2VT : kWalkVT);
+  const bool wide = walk_wide(static_cast<int64_t>(d.B) * d.H, d.dk, d.dv);
+  a.nvt = d.dv / (full ? (wide ? 256 : kWalk2VT) : kWalkVT);
   const int64_t per_seg = static_cast<int64_t>(d.B) * d.H * a.nkt * a.nvt;
   auto walk = [&](int mode) -> hipError_t {
     a.mode = mode;
     const int64_t nblocks = per_seg * (mode == 0 ? a.nseg - 1 : a.nseg);
     const dim3 grid(static_cast<unsigned>(nblocks));
-    if (full && d.dk == 256) mfma_state_walk2_kernel<2><<<grid, kWalk2Threads, 0, stream>>>(a, decay);
-    else if (full) mfma_state_walk2_kernel<1><<<grid, kWalk2Threads, 0, stream>>>(a, decay);
+    if (full && d.dk == 256 && wide) mfma_state_walk2_kernel<2, 4><<<grid, kWalk2Threads, 0, stream>>>(a, decay);
+    else if (full && d.dk == 256) mfma_state_walk2_kernel<2, 2><<<grid, kWalk2Threads, 0, stream>>>(a, decay);
+    else if (full && wide) mfma_state_walk2_kernel<1, 4><<<grid, kWalk2Threads, 0, stream>>>(a, decay);
+    else if (full) mfma_state_walk2_kernel<1, 2><<<grid, kWalk2Threads, 0, stream>>>(a, decay);
     else if (MT == 2) mfma_state_walk_kernel<2><<<grid, kThreads, 0, stream>>>(a, decay);
     else mfma_state_walk_kernel<1><<<grid, kThreads, 0, stream>>>(a, decay);
     return hipGetLastError();

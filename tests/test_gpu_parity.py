@@ -224,6 +224,24 @@ def test_bf16_segmented_walk_and_aliased_state(B, H, N, dk, dv, C):
     _check(Sd, Sref, 2e-2, "state")
 
 
+@pytest.mark.parametrize(
+    "B,H,N,dk,dv,C",
+    [
+        (16, 16, 200, 256, 512, 64),  # 256 heads x 2 wide tiles: 256-column walk, dk 256
+        (16, 16, 150, 128, 256, 64),  # 256 heads x 1 wide tile: 256-column walk, dk 128
+    ],
+)
+def test_bf16_wide_walk_many_heads(B, H, N, dk, dv, C):
+    """Enough heads for 256-column walk workgroups (no segmentation); ragged last chunk and a state in."""
+    _announce(f"bf16 wide walk {B}x{H}x{N} dk={dk} dv={dv} C={C}")
+    q, k, v, g, S0 = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=21 + N + dk, with_state=True)
+    ref, Sref = orc.chunkwise(q, k, v, g, C, state_in=S0)
+    qd, kd, vd, S0d = _dev(q, k, v, S0)
+    o, S = ret.chunkwise(qd, kd, vd, g, C, state_in=S0d, state_out=True)
+    _check(o, ref, 2e-2, "o")
+    _check(S, Sref, 2e-2, "state")
+
+
 # ---------------------------------------------------------------------------
 # Decode step
 # ---------------------------------------------------------------------------
