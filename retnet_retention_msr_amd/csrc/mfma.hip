@@ -663,11 +663,12 @@ __device__ __forceinline__ void wait_vm_keep() {
 // Scores of a key block, S^T = K Q^T (32 keys x 64 queries), are formed one
 // step ahead: wave (tt, qt) computes the 16 x 16 tile of keys 16*tt.. and
 // queries 16*qt.. on 16x16x32 MFMAs, K from LDS, its 16 query rows held in
-// registers for the whole block (loaded once per block); it applies
-// gamma^(n-m) (zero above the diagonal) and writes the bf16 scores to the
-// score buffer of the next step. A state step's A operand, the 64 x 32 Q
-// slice, is copied into the score buffer of its step in the same layout, so
-// both kinds of step read A alike.
+// registers for the whole block; it applies gamma^(n-m) (zero above the
+// diagonal) and writes the bf16 scores to the score buffer of the next step. A
+// state step's A operand, the 64 x 32 Q slice, is copied into the score buffer
+// of its step in the same layout, so both kinds of step read A alike, and the
+// waves take their score tiles' query rows from those slices as they pass (a
+// block without state slices loads them once instead).
 //
 // Tiles travel straight from global memory into LDS (buffer loads with an LDS
 // destination) two steps ahead, in three buffer sets (X tile + K block, and a
