@@ -7,6 +7,7 @@ package. It never imports the HIP library or its binding.
 from .retention_oracle import (  # noqa: F401
     chunkwise,
     decay_mask,
+    gated_group_norm,
     group_norm,
     group_norm_rows,
     parallel,
@@ -14,4 +15,5 @@ from .retention_oracle import (  # noqa: F401
     recurrent,
     recurrent_step,
     state_after,
+    swish,
 )

@@ -14,6 +14,8 @@ Sources (the pages this follows; cited by tag below):
   [EN]  "What Is RetNet ? could it challenge the dominance of the Transformer ?"
         (medium.com, Publicis Sapient): "How is this dual representation
         achieved?" (the matrix D and the GroupNorm that follows it).
+  [AN]  "RetNet入門" (news.ainew.jp): Multi-Scale Retention (MSR) (the
+        normalised head outputs multiplied elementwise by a gated branch).
 
 Conventions (readings where the pages are silent, all listed in the design doc):
   * positions n, m and the head index h are 0-based;
@@ -234,3 +236,28 @@ def group_norm(o, eps=1e-5, weight=None, bias=None):
 def group_norm_rows(o_rows, eps=1e-5, weight=None, bias=None):
     """GroupNorm of sampled rows [B, H, R, dv]; same definition as group_norm."""
     return group_norm(o_rows, eps, weight, bias)
+
+
+def swish(x):
+    """swish(x) = x * sigmoid(x) = x / (1 + exp(-x)), elementwise.
+
+    [KR] Key components, 4. block names a swish gate after the GroupNorm; the
+    pages do not define swish, and this is its usual definition (also called
+    SiLU). Written so that no exp overflows: for x < 0 it uses
+    x * e^x / (1 + e^x).
+    """
+    x = _f64(x)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, x / (1.0 + e), x * e / (1.0 + e))
+
+
+def gated_group_norm(o, gate, eps=1e-5, weight=None, bias=None):
+    """The gated epilogue: swish(gate) * GroupNorm(o), elementwise.
+
+    [KR] Key components, 4. block (GroupNorm with swish gating); [AN]
+    Multi-Scale Retention (MSR) (the normalised head outputs times the gated
+    branch, before the output projection, which is not part of this). ``gate``
+    is the gate branch's pre-activation for these outputs, in o's layout
+    [B, H, N, dv] (head h's dv channels of it).
+    """
+    return swish(gate) * group_norm(o, eps, weight, bias)

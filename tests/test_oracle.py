@@ -366,3 +366,55 @@ def test_group_norm_invariants():
     scale = np.array([3.0, 0.25])[None, :, None, None]
     y2 = orc.group_norm(o * scale, eps=0.0)
     np.testing.assert_allclose(y2, orc.group_norm(o, eps=0.0), rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Gated epilogue: swish(gate) * GroupNorm(o)
+# --------------------------------------------------------------------------
+
+
+def _swish_by_tanh(x):
+    # sigmoid(x) = (1 + tanh(x / 2)) / 2, an identity independent of the
+    # exp-based form the oracle uses.
+    return x * 0.5 * (1.0 + np.tanh(0.5 * x))
+
+
+def test_swish_values_and_identities():
+    # sigmoid(1) = e / (1 + e); swish(0) = 0.
+    assert orc.swish(np.array([1.0]))[0] == pytest.approx(np.e / (1.0 + np.e), rel=1e-15)
+    assert orc.swish(np.array([0.0]))[0] == 0.0
+    x = _rand((4000,), seed=80, std=6.0)
+    # (the tanh form cancels for very negative x, hence the absolute floor)
+    np.testing.assert_allclose(orc.swish(x), _swish_by_tanh(x), rtol=1e-13, atol=1e-14)
+    # sigmoid(-x) = 1 - sigmoid(x)  =>  swish(-x) = swish(x) - x
+    np.testing.assert_allclose(orc.swish(-x), orc.swish(x) - x, rtol=0, atol=1e-12)
+    # limits: identity far right, zero far left, no overflow
+    big = np.array([50.0, 700.0, 1e4])
+    np.testing.assert_allclose(orc.swish(big), big, rtol=1e-15)
+    assert np.all(np.abs(orc.swish(-big)) < 1e-15)
+
+
+def test_swish_matches_torch_silu():
+    x = _rand((1000,), seed=81, std=4.0)
+    ref = torch.nn.functional.silu(torch.from_numpy(x)).numpy()
+    np.testing.assert_allclose(orc.swish(x), ref, rtol=1e-14, atol=1e-300)
+
+
+def test_gated_group_norm_special_cases():
+    B, H, N, dv = 1, 2, 5, 16
+    o = _rand((B, H, N, dv), seed=82, std=2.0) + 0.5
+    w = _rand((H * dv,), seed=83)
+    bvec = _rand((H * dv,), seed=84)
+    y = orc.group_norm(o, 1e-5, w, bvec)
+    # a zero gate closes the branch
+    np.testing.assert_array_equal(orc.gated_group_norm(o, np.zeros_like(o), 1e-5, w, bvec), 0.0)
+    # a large positive gate passes gate * GN(o) (swish(g) = g up to e^-g)
+    g = np.full_like(o, 40.0)
+    np.testing.assert_allclose(orc.gated_group_norm(o, g, 1e-5, w, bvec), 40.0 * y, rtol=1e-15)
+    # elementwise: against the library's silu and group_norm
+    gate = _rand((B, H, N, dv), seed=85, std=2.0)
+    x = torch.from_numpy(o).permute(0, 2, 1, 3).reshape(B * N, H * dv)
+    gn = torch.nn.functional.group_norm(x, H, torch.from_numpy(w), torch.from_numpy(bvec), eps=1e-5)
+    gt = torch.from_numpy(gate).permute(0, 2, 1, 3).reshape(B * N, H * dv)
+    ref = (torch.nn.functional.silu(gt) * gn).reshape(B, N, H, dv).permute(0, 2, 1, 3).numpy()
+    np.testing.assert_allclose(orc.gated_group_norm(o, gate, 1e-5, w, bvec), ref, rtol=0, atol=1e-12)

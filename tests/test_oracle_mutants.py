@@ -81,3 +81,22 @@ def test_transposed_operand_is_caught():
     ref = _brute_parallel(q, k, v, g)
     swapped = orc.parallel(k, q, v, g)
     assert np.max(np.abs(swapped - ref)) > 1e-6
+
+
+@pytest.mark.parametrize("kind", ["sign_flipped", "sigmoid_only", "gate_before_norm"])
+def test_gate_mutants_are_caught(kind):
+    """Slips in the gated epilogue: exp(+x) for exp(-x), sigmoid without the
+    factor x, and the gate applied before the GroupNorm instead of after.
+    The pin is the tanh form of the sigmoid times the library GroupNorm."""
+    rng = np.random.default_rng(90)
+    o = rng.standard_normal((1, 2, 4, 8)) * 2.0 + 0.3
+    gate = rng.standard_normal((1, 2, 4, 8)) * 2.0
+    pin = gate * 0.5 * (1.0 + np.tanh(0.5 * gate)) * orc.group_norm(o)
+    if kind == "sign_flipped":
+        y = gate / (1.0 + np.exp(gate)) * orc.group_norm(o)
+    elif kind == "sigmoid_only":
+        y = 1.0 / (1.0 + np.exp(-gate)) * orc.group_norm(o)
+    else:
+        y = orc.group_norm(orc.swish(gate) * o)
+    assert np.max(np.abs(y - pin)) > 1e-6, kind
+    np.testing.assert_allclose(orc.gated_group_norm(o, gate), pin, rtol=0, atol=1e-13)
