@@ -109,12 +109,13 @@ def measured_traffic():
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary.
 
     A figure is used only while the kernel source it was measured on is
-    unchanged (hash of the kernel file and the headers it includes);
-    otherwise it is None.
+    unchanged (hash of the kernel file, the headers it includes and, for the
+    MFMA kernels, the build script that sets their flags); otherwise it is
+    None.
     """
     current = {
-        "chunk_out": _source_hash(["mfma.hip", "mfma_tiles.h", "common.h"]),
-        "state_walk": _source_hash(["mfma.hip", "mfma_tiles.h", "common.h"]),
+        "chunk_out": _source_hash(["mfma_out.hip", "mfma_tiles.h", "common.h", "../build.py"]),
+        "state_walk": _source_hash(["mfma.hip", "mfma_tiles.h", "common.h", "../build.py"]),
         "decode_step": _source_hash(["decode.hip", "common.h"]),
     }
     out = {k: None for k in current}
@@ -330,6 +331,11 @@ def device_info():
     props = torch.cuda.get_device_properties(0)
     info = {"name": props.name, "arch": getattr(props, "gcnArchName", None), "hip": torch.version.hip,
             "torch": torch.__version__, "rocm_smi_clocks": None}
+    # Under a profiler (rocprofv3 preloads its tool library into every child,
+    # which then holds the GPU before rocm-smi's interpreter starts) the
+    # clocks are not read.
+    if any(k.startswith(("ROCPROF_", "ROCPROFILER_")) for k in os.environ):
+        return info
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
         if r.returncode == 0:
