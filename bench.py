@@ -19,7 +19,9 @@ bf16 chunk states it reads, O) over the launch time measured with HIP events,
 against 8 TB/s. The same object also gives the matrix-core view (algorithmic
 flops over time against the 2.5 PFLOP/s dense bf16 peak). `step_roofline`
 does the same for the whole step (both stages), `state_walk` for the first
-stage. `decode` carries the decode step's latency and its HBM roofline
+stage. `gated` times the same prefill with the gated epilogue
+swish(gate) * GroupNorm(O) (the output kernel then also reads the bf16 gate).
+`decode` carries the decode step's latency and its HBM roofline
 (134,610,944 algorithmic bytes per step against 8 TB/s);
 `decode_cache_defeating` repeats it at B=32, whose 256 MiB state does not fit
 the Infinity Cache. `small_config` times the parallel and chunkwise forms at
@@ -50,6 +52,7 @@ if ROOT not in sys.path:
 B, H, N, DK, DV, CHUNK = 8, 16, 8192, 256, 512, 512
 SEED = 1003
 DECODE_SEED = 1004
+GATE_SEED = 1006
 PEAK_BF16 = 2.5e15
 PEAK_HBM = 8.0e12
 FLOP_PER_TOKEN_HEAD = {64: 574_208, 128: 623_360, 256: 721_664, 512: 918_272}
@@ -115,6 +118,7 @@ def measured_traffic():
     """
     current = {
         "chunk_out": _source_hash(["mfma_out.hip", "mfma_tiles.h", "common.h", "../build.py"]),
+        "chunk_out_gated": _source_hash(["mfma_out.hip", "mfma_tiles.h", "common.h", "../build.py"]),
         "state_walk": _source_hash(["mfma.hip", "mfma_tiles.h", "common.h", "../build.py"]),
         "decode_step": _source_hash(["decode.hip", "common.h"]),
     }
@@ -375,6 +379,55 @@ def cpu_baseline(q, k, v, gamma, n_batch_rows=2):
     }
 
 
+def gated_prefill(ret, torch, dev, stream, qd, kd, vd, gamma, ws, state, out, gn, steps, warmup=5):
+    """The same prefill with the gated epilogue, swish(gate) * GroupNorm(O).
+
+    The gate ([B,H,N,dv] bf16, N(0, 4)) is drawn on the device from a seeded
+    generator. The output kernel then also reads the gate: 2 bytes per output
+    element more than the plain GroupNorm epilogue.
+    """
+    gen = torch.Generator(device=dev).manual_seed(GATE_SEED)
+    gate = (torch.randn(B, H, N, DV, generator=gen, device=dev) * 2.0).to(torch.bfloat16)
+
+    def step(events=None):
+        if events is not None:
+            events[0].record(stream)
+        ret.chunk_states(kd, vd, gamma, CHUNK, ws, state_out=state)
+        if events is not None:
+            events[1].record(stream)
+        ret.chunk_output(qd, kd, vd, gamma, CHUNK, ws, gn=gn, out=out, gate=gate)
+        if events is not None:
+            events[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    ms = ev[0][0].elapsed_time(ev[-1][2]) / steps
+    out_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    bytes_out = output_bytes(B, H, N, CHUNK) + B * H * N * DV * 2
+    del gate
+    return {
+        "workload": "the prefill above with the gated epilogue swish(gate) * GroupNorm(O), gate bf16 [B,H,N,dv]",
+        "steps": steps,
+        "ms_per_step": ms,
+        "tokens_per_s": B * N / (ms * 1e-3),
+        "output_launch_ms": out_ms,
+        "output_roofline": {
+            "bound": "hbm",
+            "algorithmic_bytes_per_launch": bytes_out,
+            "achieved": bytes_out / (out_ms * 1e-3) / 1e9,
+            "peak": PEAK_HBM / 1e9,
+            "unit": "GB/s",
+            "frac": bytes_out / (out_ms * 1e-3) / PEAK_HBM,
+            "traffic": measured_traffic()["chunk_out_gated"],
+        },
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -389,6 +442,7 @@ def main():
     ap.add_argument("--skip-long", action="store_true", help="skip the long-sequence flatness sweep")
     ap.add_argument("--skip-small", action="store_true", help="skip the B=2 H=8 N=2048 timings")
     ap.add_argument("--skip-decode-b32", action="store_true", help="skip the cache-defeating B=32 decode timing")
+    ap.add_argument("--skip-gated", action="store_true", help="skip the swish-gated prefill timing")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -456,6 +510,11 @@ def main():
     flops_walk = flops - flops_out
     bytes_out = output_bytes(B, H, N, CHUNK)
     bytes_walk = walk_bytes(B, H, N, CHUNK)
+
+    gated = None
+    if not args.skip_gated:
+        print(f"[bench] timing {args.steps} swish-gated prefill steps", file=sys.stderr, flush=True)
+        gated = gated_prefill(ret, torch, dev, stream, qd, kd, vd, gamma, ws, state, out, gn, args.steps)
 
     # Decode: single-token steps from the prefill's state.
     if args.skip_decode:
@@ -561,6 +620,7 @@ def main():
             "mfma_tflops": flops_walk / (walk_ms * 1e-3) / 1e12,
             "traffic": traffic["state_walk"],
         },
+        "gated": gated,
         "decode": {
             "steps": T,
             "us_per_step": us_step,

@@ -29,6 +29,16 @@
  *     for each (b, h, n) the mean and biased variance over that head's dv
  *     outputs, y = (o - mean) / sqrt(var + eps) * weight[h*dv + c] + bias[h*dv + c].
  *     weight and bias are device fp32 [H*dv] and may each be NULL (identity).
+ *   - gn->gate (optional, NULL = none) adds the swish gate of the gated MSR
+ *     block ("RetNet - Retentive Network ...", Key components, 4. block:
+ *     GroupNorm with swish gating; "RetNet入門" (news.ainew.jp), Multi-Scale
+ *     Retention (MSR): the normalised head outputs times the gated branch):
+ *     the stored output is y * swish(g) with swish(g) = g / (1 + exp(-g)),
+ *     where g is the gate's element at the same position. The gate is a device
+ *     buffer of the input's element type laid out like O ([B, H, N, dv]; one
+ *     token [B, H, dv] for the recurrent step), read only. It holds the gate
+ *     branch's pre-activation (its projection is the caller's). It must not
+ *     alias O.
  *   - stream is a hipStream_t (NULL = the default stream). All work is
  *     enqueued on it and the call returns without synchronising. RET_OK means
  *     "validated and launched"; a fault inside a kernel surfaces on the next
@@ -56,7 +66,7 @@
 extern "C" {
 #endif
 
-#define RETENTION_ABI_VERSION 1
+#define RETENTION_ABI_VERSION 2
 #define RETENTION_MAX_HEADS 256
 #define RETENTION_MAX_DK 256
 #define RETENTION_MAX_DV 1024
@@ -74,6 +84,7 @@ typedef struct retention_gn_t {
   float eps;            /* added to the variance; must be >= 0 and finite */
   const float* weight;  /* device fp32 [H*dv], or NULL for 1 */
   const float* bias;    /* device fp32 [H*dv], or NULL for 0 */
+  const void* gate;     /* device, O's type and layout, or NULL for no gate */
 } retention_gn_t;
 
 /* RETENTION_ABI_VERSION of the built library. */

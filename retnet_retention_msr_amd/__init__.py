@@ -67,8 +67,11 @@ def _gamma_array(gamma: GammaLike, H: int):
     return arr
 
 
-def _gn_struct(gn: Optional[GroupNorm], H: int, dv: int, device):
+def _gn_struct(gn: Optional[GroupNorm], H: int, dv: int, device, gate=None, like=None):
+    """The retention_gn_t for ``gn``; ``gate`` (optional) must match ``like`` (the output)."""
     if gn is None:
+        if gate is not None:
+            raise ValueError("a gate needs the GroupNorm epilogue (gn)")
         return None, ()
     keep = []
     ptrs = []
@@ -80,7 +83,16 @@ def _gn_struct(gn: Optional[GroupNorm], H: int, dv: int, device):
             raise ValueError("GroupNorm weight/bias must be contiguous float32 [H*dv] on the input's device")
         keep.append(t)
         ptrs.append(t.data_ptr())
-    s = _lib.GnStruct(float(gn.eps), ptrs[0], ptrs[1])
+    gate_ptr = None
+    if gate is not None:
+        if (not gate.is_cuda or gate.device != like.device or gate.dtype != like.dtype or not gate.is_contiguous()
+                or gate.numel() != like.numel()):
+            raise ValueError("gate must be a contiguous device tensor with the output's dtype and shape")
+        if gate.data_ptr() == like.data_ptr():
+            raise ValueError("gate must not alias the output")
+        keep.append(gate)
+        gate_ptr = gate.data_ptr()
+    s = _lib.GnStruct(float(gn.eps), ptrs[0], ptrs[1], gate_ptr)
     return ctypes.byref(s), (s, keep)
 
 
@@ -102,14 +114,18 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def parallel(q, k, v, gamma: GammaLike, gn: Optional[GroupNorm] = None, out=None):
-    """Parallel form O = (Q K^T * D) V per head (optionally GroupNorm-ed)."""
+def parallel(q, k, v, gamma: GammaLike, gn: Optional[GroupNorm] = None, out=None, gate=None):
+    """Parallel form O = (Q K^T * D) V per head (optionally GroupNorm-ed).
+
+    ``gate`` (optional, needs ``gn``): a tensor like the output; the result
+    becomes GroupNorm(O) * swish(gate).
+    """
     lib = _lib.load()
     B, H, N, dk, dv, dt = _check_qkv(q, k, v)
     if out is None:
         out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
     g = _gamma_array(gamma, H)
-    gn_p, _keep = _gn_struct(gn, H, dv, q.device)
+    gn_p, _keep = _gn_struct(gn, H, dv, q.device, gate, out)
     rc = lib.retention_parallel(q.data_ptr(), k.data_ptr(), v.data_ptr(), g, out.data_ptr(), B, H, N, dk, dv, dt,
                                 gn_p, _stream(q))
     if rc != 0:
@@ -123,11 +139,13 @@ def chunkwise_workspace_bytes(B, H, N, dk, dv, chunk, dtype=torch.bfloat16) -> i
 
 
 def chunkwise(q, k, v, gamma: GammaLike, chunk: int, state_in=None, state_out: Union[bool, torch.Tensor] = False,
-              gn: Optional[GroupNorm] = None, out=None, workspace=None):
+              gn: Optional[GroupNorm] = None, out=None, workspace=None, gate=None):
     """Chunkwise recurrent form. Returns (o, state_out or None).
 
     ``state_out``: False (not produced), True (allocate), or an fp32
-    [B,H,dk,dv] tensor to fill (it may be ``state_in`` itself).
+    [B,H,dk,dv] tensor to fill (it may be ``state_in`` itself). ``gate``
+    (optional, needs ``gn``): a tensor like the output; the result becomes
+    GroupNorm(O) * swish(gate).
     """
     lib = _lib.load()
     B, H, N, dk, dv, dt = _check_qkv(q, k, v)
@@ -147,7 +165,7 @@ def chunkwise(q, k, v, gamma: GammaLike, chunk: int, state_in=None, state_out: U
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     g = _gamma_array(gamma, H)
-    gn_p, _keep = _gn_struct(gn, H, dv, q.device)
+    gn_p, _keep = _gn_struct(gn, H, dv, q.device, gate, out)
     rc = lib.retention_chunkwise(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), g, out.data_ptr(), B, H, N, dk, dv, int(chunk), dt,
         state_in.data_ptr() if state_in is not None else None,
@@ -181,14 +199,17 @@ def chunk_states(k, v, gamma: GammaLike, chunk: int, workspace, state_in=None, s
 
 
 def chunk_output(q, k, v, gamma: GammaLike, chunk: int, workspace, has_state_in: bool = False,
-                 gn: Optional[GroupNorm] = None, out=None):
-    """Second stage of the chunkwise form: O from q, k, v and the chunk states in ``workspace``."""
+                 gn: Optional[GroupNorm] = None, out=None, gate=None):
+    """Second stage of the chunkwise form: O from q, k, v and the chunk states in ``workspace``.
+
+    ``gate`` as in ``chunkwise``.
+    """
     lib = _lib.load()
     B, H, N, dk, dv, dt = _check_qkv(q, k, v)
     if out is None:
         out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
     g = _gamma_array(gamma, H)
-    gn_p, _keep = _gn_struct(gn, H, dv, q.device)
+    gn_p, _keep = _gn_struct(gn, H, dv, q.device, gate, out)
     rc = lib.retention_chunk_output(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), g, out.data_ptr(), B, H, N, dk, dv, int(chunk), dt,
         1 if has_state_in else 0, gn_p, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -198,10 +219,12 @@ def chunk_output(q, k, v, gamma: GammaLike, chunk: int, workspace, has_state_in:
     return out
 
 
-def recurrent_step(q, k, v, gamma: GammaLike, state, gn: Optional[GroupNorm] = None, out=None):
+def recurrent_step(q, k, v, gamma: GammaLike, state, gn: Optional[GroupNorm] = None, out=None, gate=None):
     """One decode step: state <- gamma*state + k^T v (in place), returns o = q.state.
 
     q, k are [B,H,dk] (or [B,H,1,dk]); v is [B,H,dv] (or [B,H,1,dv]).
+    ``gate`` (optional, needs ``gn``): B*H*dv values of the output's dtype;
+    the result becomes GroupNorm(o) * swish(gate).
     """
     lib = _lib.load()
     for name, t in (("q", q), ("k", k), ("v", v), ("state", state)):
@@ -218,7 +241,7 @@ def recurrent_step(q, k, v, gamma: GammaLike, state, gn: Optional[GroupNorm] = N
     if out is None:
         out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
     g = _gamma_array(gamma, H)
-    gn_p, _keep = _gn_struct(gn, H, dv, q.device)
+    gn_p, _keep = _gn_struct(gn, H, dv, q.device, gate, out)
     rc = lib.retention_recurrent_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), g, state.data_ptr(),
                                       out.data_ptr(), B, H, dk, dv, dt, gn_p, _stream(q))
     if rc != 0:

@@ -28,10 +28,15 @@ EXPORTED = (
 )
 
 
-class GnStruct(ctypes.Structure):
-    """retention_gn_t: eps, device weight pointer, device bias pointer."""
+# RETENTION_ABI_VERSION of include/retention.h that the structures here mirror.
+ABI_VERSION = 2
 
-    _fields_ = [("eps", ctypes.c_float), ("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
+
+class GnStruct(ctypes.Structure):
+    """retention_gn_t: eps, device weight, bias and gate pointers."""
+
+    _fields_ = [("eps", ctypes.c_float), ("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("gate", ctypes.c_void_p)]
 
 
 _lib = None
@@ -67,6 +72,10 @@ def load():
     lib.retention_chunk_output.restype = i
     lib.retention_recurrent_step.argtypes = [vp, vp, vp, f_p, vp, vp, i, i, i, i, i, gn_p, vp]
     lib.retention_recurrent_step.restype = i
+    if lib.retention_abi_version() != ABI_VERSION:
+        raise RuntimeError(
+            f"{LIB_PATH} has ABI version {lib.retention_abi_version()}, this binding expects {ABI_VERSION}: rebuild it"
+        )
     _lib = lib
     return lib
 

@@ -52,12 +52,14 @@ int check_gn(const retention_gn_t* gn, GnArgs* out) {
   out->eps = 0.0f;
   out->weight = nullptr;
   out->bias = nullptr;
+  out->gate = nullptr;
   if (!gn) return RET_OK;
   if (!std::isfinite(gn->eps) || gn->eps < 0.0f) return RET_ERR_INVALID_ARG;
   out->enabled = 1;
   out->eps = gn->eps;
   out->weight = gn->weight;
   out->bias = gn->bias;
+  out->gate = gn->gate;
   return RET_OK;
 }
 

@@ -19,7 +19,16 @@ struct GnArgs {
   float eps;
   const float* weight;  // [H*dv] or nullptr
   const float* bias;    // [H*dv] or nullptr
+  const void* gate;     // like O (element type of the inputs), or nullptr
 };
+
+// swish(g) = g * sigmoid(g) = g / (1 + e^-g), the gate's activation: e^-g as
+// the hardware exp2 of -g * log2(e), then the hardware reciprocal (about one
+// ulp each). For g below about -88, e^-g is +inf, its reciprocal 0 and the
+// result -0, the limit; for large g the result is g.
+__device__ __forceinline__ float swish(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));

@@ -118,6 +118,7 @@ decode_step_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
       float y = (s_row[c] - mean) * rstd;
       if (gn.weight) y *= gn.weight[h * dv + c];
       if (gn.bias) y += gn.bias[h * dv + c];
+      if (gn.gate) y *= swish(Elem<T>::load(static_cast<const T*>(gn.gate), bh * dv + c));
       Elem<T>::store(o, bh * dv + c, y);
     }
   }

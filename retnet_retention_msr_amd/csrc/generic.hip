@@ -204,6 +204,7 @@ generic_chunk_out_kernel(const T* __restrict__ q, const T* __restrict__ k, const
       float y = (acc[j] - mean) * rstd;
       if (gn.weight && col < dv) y *= gn.weight[h * dv + col];
       if (gn.bias && col < dv) y += gn.bias[h * dv + col];
+      if (gn.gate && col < dv) y *= swish(Elem<T>::load(static_cast<const T*>(gn.gate), (bh * N + n) * dv + col));
       acc[j] = y;
     }
   }

@@ -93,7 +93,10 @@ __device__ __forceinline__ void wait_vm_keep() {
 // LDS reads of a step never wait for the copies in flight. The next block's
 // first copies and Q rows are requested before the current block's GroupNorm
 // and store, which use no buffer those copies write.
-template <int NVT, int WAVES>
+//
+// GATE: the GroupNorm is on and its output is multiplied by swish(gate) (a
+// separate instance, so the gate's registers do not weigh on the plain one).
+template <int NVT, int WAVES, bool GATE>
 __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, HeadDecay decay, GnArgs gn) {
   constexpr int DV = WAVES * 32 * NVT;
   constexpr int SW = 8 / WAVES;                    // 16 x 16 score tiles per wave (8 per key block)
@@ -524,6 +527,27 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
         bb[nt] = gn.bias ? gn.bias[cur.h * DV + vcol] : 0.f;
       }
     }
+    // Gate values (bf16 pairs) at exactly the positions this lane stores,
+    // also requested before the next block's copies. Rows past the block's
+    // last valid row read as zero through the descriptors' ranges.
+    constexpr bool gated = GATE;
+    const int voff = ((4 * (lane >> 5) + (lane & 1)) * DV + vcol0 + (l32 & ~1)) * 2;
+    uint32_t gv[2][4][NVT][2];
+    if constexpr (gated) {
+      const uint16_t* gblk = static_cast<const uint16_t*>(gn.gate) + (cur.bh * a.N + cur.q0) * static_cast<int64_t>(DV);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int row0 = qt * 32 + 8 * g;
+          const __amdgpu_buffer_rsrc_t r = make_rsrc(gblk + row0 * DV, min(max(oq - row0, 0), 8) * DV * 2);
+#pragma unroll
+          for (int nt = 0; nt < NVT; ++nt)
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp)
+              gv[qt][g][nt][hp] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + (2 * hp * DV + nt * 32) * 2, 0, 0);
+        }
+    }
     const int Ln = block_of(++it);
     if (Ln >= 0) {
       setup(Ln, cur);
@@ -595,36 +619,54 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
     }
 
     // Store: accumulators r and r+1 of a lane are rows rho and rho+1 of one
-    // column. Packed to bf16 pairs, one exchange with the neighbouring lane
-    // (DPP) and a byte permute give each lane two adjacent columns of one row
-    // (the even lane row rho, the odd lane row rho+1), written as one 4-byte
-    // store. Rows go out in groups of eight (qt*32 + 8g ..), each through a
-    // descriptor whose range ends at the block's last valid row, so the lane
-    // offsets are the same for every group.
+    // column. One exchange with the neighbouring lane (DPP) gives each lane
+    // two adjacent columns of one row (the even lane row rho, the odd lane row
+    // rho+1), written as one 4-byte store of a bf16 pair. Without a gate the
+    // pair is exchanged already packed (then a byte permute picks the halves);
+    // with a gate it is exchanged in fp32 and multiplied by swish of the gate
+    // pair at the same position before rounding. Rows go out in groups of
+    // eight (qt*32 + 8g ..), each through a descriptor whose range ends at the
+    // block's last valid row, so the lane offsets are the same for every group.
     {
       const bool odd = lane & 1;
-      const int voff = ((4 * (lane >> 5) + (odd ? 1 : 0)) * DV + vcol0 + (l32 & ~1)) * 2;
       // v_perm byte selectors over {neighbour (bytes 4-7), own (bytes 0-3)}:
       // even lanes take both low halves, odd lanes both high halves.
       const unsigned sel = odd ? 0x03020706u : 0x05040100u;
+      auto store_rows = [&](auto gate_tag) __attribute__((always_inline)) {
+        constexpr bool kGate = decltype(gate_tag)::value;
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+        for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int row0 = qt * 32 + 8 * g;
-          const __amdgpu_buffer_rsrc_t r = make_rsrc(oblk + row0 * DV, min(max(oq - row0, 0), 8) * DV * 2);
+          for (int g = 0; g < 4; ++g) {
+            const int row0 = qt * 32 + 8 * g;
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(oblk + row0 * DV, min(max(oq - row0, 0), 8) * DV * 2);
 #pragma unroll
-          for (int nt = 0; nt < NVT; ++nt)
+            for (int nt = 0; nt < NVT; ++nt)
 #pragma unroll
-            for (int hp = 0; hp < 2; ++hp) {
-              // accumulators 4g + 2hp (row row0 + 4*(lane/32) + 2hp) and the next row
-              const int rr = 4 * g + 2 * hp;
-              const unsigned own = pack_bf16x2(acc[qt][nt][rr], acc[qt][nt][rr + 1]);
-              const unsigned nbr = __builtin_amdgcn_update_dpp(0u, own, 0xB1, 0xf, 0xf, true);  // quad_perm [1,0,3,2]
-              const unsigned packed = __builtin_amdgcn_perm(nbr, own, sel);
-              __builtin_amdgcn_raw_buffer_store_b32(packed, r, voff + (2 * hp * DV + nt * 32) * 2, 0, 0);
-            }
-        }
+              for (int hp = 0; hp < 2; ++hp) {
+                // accumulators 4g + 2hp (row row0 + 4*(lane/32) + 2hp) and the next row
+                const int rr = 4 * g + 2 * hp;
+                unsigned packed;
+                if constexpr (kGate) {
+                  // the even lane sends its row rho+1 value, the odd lane its row rho value
+                  const float a0 = acc[qt][nt][rr], a1 = acc[qt][nt][rr + 1];
+                  const float send = odd ? a0 : a1;
+                  const float recv = __builtin_bit_cast(
+                      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xf, 0xf, true));
+                  const float lo = odd ? recv : a0, hi = odd ? a1 : recv;
+                  const uint32_t gp = gv[qt][g][nt][hp];
+                  packed = pack_bf16x2(lo * swish(__uint_as_float(gp << 16)),
+                                       hi * swish(__uint_as_float(gp & 0xffff0000u)));
+                } else {
+                  const unsigned own = pack_bf16x2(acc[qt][nt][rr], acc[qt][nt][rr + 1]);
+                  const unsigned nbr = __builtin_amdgcn_update_dpp(0u, own, 0xB1, 0xf, 0xf, true);  // quad_perm [1,0,3,2]
+                  packed = __builtin_amdgcn_perm(nbr, own, sel);
+                }
+                __builtin_amdgcn_raw_buffer_store_b32(packed, r, voff + (2 * hp * DV + nt * 32) * 2, 0, 0);
+              }
+          }
+      };
+      store_rows(std::integral_constant<bool, gated>{});
     }
 
     if (Ln < 0) break;
@@ -691,10 +733,14 @@ hipError_t launch_mfma_chunk_out(const uint16_t* q, const uint16_t* k, const uin
     kernel<<<grid, threads, 0, stream>>>(a, decay, gn);
     return hipGetLastError();
   };
+  const bool gated = gn.enabled && gn.gate;
   switch (d.dv) {
-    case 128: return launch(mfma_chunk_out_kernel<1, 4>, 256, 0);
-    case 256: return launch(mfma_chunk_out_kernel<1, 8>, 512, 1);
-    default: return launch(mfma_chunk_out_kernel<2, 8>, 512, 2);
+    case 128:
+      return gated ? launch(mfma_chunk_out_kernel<1, 4, true>, 256, 3) : launch(mfma_chunk_out_kernel<1, 4, false>, 256, 0);
+    case 256:
+      return gated ? launch(mfma_chunk_out_kernel<1, 8, true>, 512, 4) : launch(mfma_chunk_out_kernel<1, 8, false>, 512, 1);
+    default:
+      return gated ? launch(mfma_chunk_out_kernel<2, 8, true>, 512, 5) : launch(mfma_chunk_out_kernel<2, 8, false>, 512, 2);
   }
 }
 

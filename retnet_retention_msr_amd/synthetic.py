@@ -52,3 +52,9 @@ def make_gn_affine(H, dv, seed=0):
     w = 1.0 + 0.25 * _randn((H * dv,), gen)
     b = 0.1 * _randn((H * dv,), gen)
     return w, b
+
+
+def make_gate(shape, dtype=torch.bfloat16, seed=0, std=2.0):
+    """Gate pre-activations of the given shape (like the output), N(0, std^2), on the CPU."""
+    gen = torch.Generator().manual_seed(int(seed))
+    return _randn(tuple(shape), gen, std).to(dtype)

@@ -9,6 +9,7 @@ pointers below are never dereferenced.
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.retention_abi_version() == 1
+    assert lib.retention_abi_version() == _lib.ABI_VERSION == 2
     assert _lib.status_string(0) == "ok"
     assert _lib.status_string(-1) == "invalid argument"
     assert _lib.status_string(-2) == "unsupported arguments"
@@ -88,7 +89,7 @@ def test_parallel_rejects_null_gamma(lib):
 
 def test_groupnorm_eps_is_validated(lib):
     for eps in (-1e-5, float("nan"), float("inf")):
-        gn = _lib.GnStruct(eps, None, None)
+        gn = _lib.GnStruct(eps, None, None, None)
         assert _parallel(lib, gn=ctypes.byref(gn)) == _lib.RET_ERR_INVALID_ARG
 
 
@@ -154,3 +155,25 @@ def test_chunk_stage_entry_points_validate(lib):
                                       None) == -1
     assert lib.retention_chunk_output(FAKE, FAKE, FAKE, g, FAKE, 1, 2, 256, 64, 128, 64, 1, 0, None, None, 0,
                                       None) == -1
+
+
+def test_gn_struct_layout_matches_the_header(tmp_path):
+    """ctypes' retention_gn_t has the C compiler's size and field offsets."""
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stddef.h>\n#include <stdio.h>\n#include "retention.h"\n'
+        "int main(void) { printf(\"%zu %zu %zu %zu %zu\\n\", sizeof(retention_gn_t),"
+        " offsetof(retention_gn_t, eps), offsetof(retention_gn_t, weight),"
+        " offsetof(retention_gn_t, bias), offsetof(retention_gn_t, gate)); return 0; }\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    S = _lib.GnStruct
+    assert got == [ctypes.sizeof(S), S.eps.offset, S.weight.offset, S.bias.offset, S.gate.offset]
+
+
+def test_gate_needs_groupnorm():
+    import retnet_retention_msr_amd as ret
+
+    with pytest.raises(ValueError, match="needs the GroupNorm"):
+        ret._gn_struct(None, 2, 128, None, gate=object())

@@ -99,6 +99,26 @@ def test_6p7b_prefill_with_groupnorm_sampled(prefill_6p7b):
         _check(_f64(state[b : b + 1]), orc.state_after(kb, vb, g), f"state b={b}")
 
 
+def test_6p7b_prefill_gated_sampled(prefill_6p7b):
+    _announce("B=8 H=16 N=8192 chunk 512 + GroupNorm + swish gate: sampled rows")
+    q, k, v = prefill_6p7b
+    B, H, N, dk = q.shape
+    dv, C = v.shape[-1], 512
+    g = synthetic.head_gammas(H)
+    gate = synthetic.make_gate((B, H, N, dv), dtype=torch.bfloat16, seed=1006)
+    qd, kd, vd, gd = q.to(DEV), k.to(DEV), v.to(DEV), gate.to(DEV)
+    out = torch.empty(B, H, N, dv, dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(ret.chunkwise_workspace_bytes(B, H, N, dk, dv, C), dtype=torch.uint8, device=DEV)
+    ret.chunkwise(qd, kd, vd, g, C, gn=ret.GroupNorm(1e-5), out=out, workspace=ws, gate=gd)
+    torch.cuda.synchronize()
+    rows = _rows(N, C, seed=4)
+    for b in (0, B - 1):
+        qb, kb, vb = (_f64(t[b : b + 1]) for t in (q, k, v))
+        raw = orc.parallel_rows(qb, kb, vb, g, rows)
+        ref = orc.gated_group_norm(raw, _f64(gate[b : b + 1, :, rows]), eps=1e-5)
+        _check(_f64(out[b : b + 1, :, rows]), ref, f"gated o rows b={b}")
+
+
 def test_decode_step_full_shape():
     _announce("decode step on fp32 [8,16,256,512], 4 steps")
     B, H, dk, dv = 8, 16, 256, 512

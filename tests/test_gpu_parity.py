@@ -161,6 +161,57 @@ def test_bf16_groupnorm_epilogue(affine, form):
     _check(o, ref, 2e-2, "gn")
 
 
+# Gated epilogue, swish(gate) * GroupNorm(O): every MFMA output-kernel
+# instance (dv 128, 256, 512), a ragged last query block, state read-out and
+# affine GroupNorm; and the fp32 generic kernel.
+GATED_SHAPES = [
+    # B, H, N, dk, dv, chunk, dtype
+    (2, 3, 200, 64, 128, 64, torch.bfloat16),
+    (1, 4, 333, 128, 256, 128, torch.bfloat16),
+    (2, 2, 301, 256, 512, 256, torch.bfloat16),
+    (1, 2, 45, 24, 40, 16, torch.float32),
+]
+
+
+@pytest.mark.parametrize("B,H,N,dk,dv,C,dtype", GATED_SHAPES)
+@pytest.mark.parametrize("form", ["parallel", "chunkwise"])
+def test_gated_groupnorm_epilogue(B, H, N, dk, dv, C, dtype, form):
+    _announce(f"gated GroupNorm {form} {B}x{H}x{N} dk={dk} dv={dv} C={C} {dtype}")
+    q, k, v, g, S0 = _inputs(B, H, N, dk, dv, dtype, seed=N + dv, with_state=(form == "chunkwise"))
+    w, bvec = synthetic.make_gn_affine(H, dv, seed=N + 9)
+    gate = synthetic.make_gate((B, H, N, dv), dtype=dtype, seed=N + 11)
+    if form == "parallel":
+        raw = orc.parallel(q, k, v, g)
+    else:
+        raw = orc.chunkwise(q, k, v, g, C, state_in=S0)[0]
+    ref = orc.gated_group_norm(raw, gate, eps=1e-5, weight=w, bias=bvec)
+    qd, kd, vd, S0d, wd, bd, gd = _dev(q, k, v, S0, w, bvec, gate)
+    gn = ret.GroupNorm(1e-5, wd, bd)
+    if form == "parallel":
+        o = ret.parallel(qd, kd, vd, g, gn=gn, gate=gd)
+    else:
+        o = ret.chunkwise(qd, kd, vd, g, C, state_in=S0d, gn=gn, gate=gd)[0]
+    _check(o, ref, TOL[dtype], "gated")
+    # the ungated call on the same inputs still gives the plain GroupNorm
+    if form == "chunkwise":
+        o2 = ret.chunkwise(qd, kd, vd, g, C, state_in=S0d, gn=gn)[0]
+        _check(o2, orc.group_norm(raw, eps=1e-5, weight=w, bias=bvec), TOL[dtype], "ungated")
+
+
+def test_gated_large_gates_saturate():
+    """Gates far out on both sides: swish(g) = g for g >> 0 and 0 for g << 0."""
+    _announce("gated GroupNorm, saturating gates")
+    B, H, N, dk, dv, C = 1, 2, 130, 64, 128, 64
+    q, k, v, g, _ = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=5)
+    gate = synthetic.make_gate((B, H, N, dv), dtype=torch.float32, seed=6)
+    gate = (torch.sign(gate) * 100.0).to(torch.bfloat16)
+    ref = orc.gated_group_norm(orc.chunkwise(q, k, v, g, C)[0], gate, eps=1e-5)
+    qd, kd, vd, gd = _dev(q, k, v, gate)
+    o = ret.chunkwise(qd, kd, vd, g, C, gn=ret.GroupNorm(1e-5), gate=gd)[0]
+    _check(o, ref, 2e-2, "saturated")
+    assert torch.all(o[(gd < 0)] == 0)
+
+
 # Shapes with more 64-row query blocks than the output kernel runs workgroups
 # (one per CU), so each workgroup takes several blocks, from different heads,
 # chunk positions and a ragged tail, with state read-out and affine GroupNorm.
@@ -269,6 +320,28 @@ def test_decode_steps_match_oracle(dtype, gn_on, dv):
         o = ret.recurrent_step(qd[:, :, n].contiguous(), kd[:, :, n].contiguous(), vd[:, :, n].contiguous(), g, Sd,
                                gn=gn)
         _check(o, o_ref, tol, f"o step {n}")
+    _check(Sd, Sref, 1e-5, "state")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dv", [128, 100])
+def test_decode_gated_groupnorm(dtype, dv):
+    _announce(f"decode gated dtype={dtype} dv={dv}")
+    B, H, dk, steps = 2, 3, 64, 3
+    q, k, v = synthetic.make_qkv(B, H, steps, dk, dv, dtype=dtype, seed=31, qk_var=1.0)
+    g = synthetic.head_gammas(H)
+    S = synthetic.make_state(B, H, dk, dv, seed=32)
+    w, bvec = synthetic.make_gn_affine(H, dv, seed=33)
+    gate = synthetic.make_gate((B, H, steps, dv), dtype=dtype, seed=34)
+    Sd = S.to(DEV)
+    qd, kd, vd, wd, bd, gd = _dev(q, k, v, w, bvec, gate)
+    Sref = S.double().numpy()
+    for n in range(steps):
+        o_ref, Sref = orc.recurrent_step(q[:, :, n], k[:, :, n], v[:, :, n], g, Sref)
+        o_ref = orc.gated_group_norm(o_ref[:, :, None, :], gate[:, :, n : n + 1], 1e-5, w, bvec)[:, :, 0]
+        o = ret.recurrent_step(qd[:, :, n].contiguous(), kd[:, :, n].contiguous(), vd[:, :, n].contiguous(), g, Sd,
+                               gn=ret.GroupNorm(1e-5, wd, bd), gate=gd[:, :, n].contiguous())
+        _check(o, o_ref, TOL[dtype], f"o step {n}")
     _check(Sd, Sref, 1e-5, "state")
 
 
