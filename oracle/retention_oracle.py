@@ -14,8 +14,9 @@ Sources (the pages this follows; cited by tag below):
   [EN]  "What Is RetNet ? could it challenge the dominance of the Transformer ?"
         (medium.com, Publicis Sapient): "How is this dual representation
         achieved?" (the matrix D and the GroupNorm that follows it).
-  [AN]  "RetNet入門" (news.ainew.jp): Multi-Scale Retention (MSR) (the
-        normalised head outputs multiplied elementwise by a gated branch).
+  [SP]  "RetNet入門" (Spiral.AI blog digest, news.ainew.jp): Multi-Scale
+        Retention (MSR) (the normalised head outputs multiplied elementwise by
+        a gated branch).
 
 Conventions (readings where the pages are silent, all listed in the design doc):
   * positions n, m and the head index h are 0-based;
@@ -211,6 +212,57 @@ def state_after(k, v, gamma, state_in=None):
     return S
 
 
+def backward(q, k, v, gamma, d_o, state_in=None, d_state_out=None):
+    """Gradients of retention with respect to q, k, v and the starting state.
+
+    The forward map is the parallel form with a starting state S0 ([KR] Key
+    Equations, parallel form; the state term as in ``parallel``) together
+    with the state it leaves behind (``state_after``):
+        O   = (Q K^T * D) V + diag(xi) Q S0,         xi_n   = gamma^(n+1)
+        S_N = K^T diag(zeta) V + gamma^N S0,          zeta_m = gamma^(N-1-m)
+    The pages name training as the purpose of the parallel and chunkwise forms
+    but print no gradients; these are the derivatives of the two maps above,
+    given d_o = dL/dO and d_state_out = dL/dS_N (None = 0). With A = Q K^T * D
+    and dA = (d_o V^T) * D:
+        dV  = A^T d_o + diag(zeta) K dS_N
+        dQ  = dA K + diag(xi) d_o S0^T
+        dK  = dA^T Q + diag(zeta) V dS_N^T
+        dS0 = Q^T diag(xi) d_o + gamma^N dS_N
+    Returns (dq, dk, dv, d_state_in); d_state_in is None when state_in is None
+    and d_state_out is None.
+    """
+    q, k, v, d_o = _f64(q), _f64(k), _f64(v), _f64(d_o)
+    g = _f64(gamma)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    S0 = None if state_in is None else _f64(state_in)
+    dSN = None if d_state_out is None else _f64(d_state_out)
+    dq, dk_, dv_ = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    want_ds0 = S0 is not None or dSN is not None
+    dS0 = np.zeros((B, H, dk, dv)) if want_ds0 else None
+    for h in range(H):
+        D = decay_mask(N, g[h])
+        xi = np.power(g[h], np.arange(1, N + 1, dtype=np.float64))
+        zeta = np.power(g[h], np.arange(N - 1, -1, -1, dtype=np.float64))
+        for b in range(B):
+            Q, K, V, G = q[b, h], k[b, h], v[b, h], d_o[b, h]
+            A = (Q @ K.T) * D
+            dA = (G @ V.T) * D
+            dv_[b, h] = A.T @ G
+            dq[b, h] = dA @ K
+            dk_[b, h] = dA.T @ Q
+            if S0 is not None:
+                dq[b, h] += xi[:, None] * (G @ S0[b, h].T)
+            if dSN is not None:
+                dv_[b, h] += zeta[:, None] * (K @ dSN[b, h])
+                dk_[b, h] += zeta[:, None] * (V @ dSN[b, h].T)
+            if want_ds0:
+                dS0[b, h] = Q.T @ (xi[:, None] * G)
+                if dSN is not None:
+                    dS0[b, h] += (g[h] ** N) * dSN[b, h]
+    return dq, dk_, dv_, dS0
+
+
 def group_norm(o, eps=1e-5, weight=None, bias=None):
     """Per-head GroupNorm applied to retention outputs.
 
@@ -254,7 +306,7 @@ def swish(x):
 def gated_group_norm(o, gate, eps=1e-5, weight=None, bias=None):
     """The gated epilogue: swish(gate) * GroupNorm(o), elementwise.
 
-    [KR] Key components, 4. block (GroupNorm with swish gating); [AN]
+    [KR] Key components, 4. block (GroupNorm with swish gating); [SP]
     Multi-Scale Retention (MSR) (the normalised head outputs times the gated
     branch, before the output projection, which is not part of this). ``gate``
     is the gate branch's pre-activation for these outputs, in o's layout

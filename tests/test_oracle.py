@@ -418,3 +418,73 @@ def test_gated_group_norm_special_cases():
     gt = torch.from_numpy(gate).permute(0, 2, 1, 3).reshape(B * N, H * dv)
     ref = (torch.nn.functional.silu(gt) * gn).reshape(B, N, H, dv).permute(0, 2, 1, 3).numpy()
     np.testing.assert_allclose(orc.gated_group_norm(o, gate, 1e-5, w, bvec), ref, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Backward: gradients of O and of the final state
+# --------------------------------------------------------------------------
+
+
+def _loss(q, k, v, S0, gamma, W, U):
+    """L = sum(W * O) + sum(U * S_N) through the oracle's (pinned) forward maps."""
+    return float(np.sum(W * orc.parallel(q, k, v, gamma, state_in=S0))
+                 + np.sum(U * orc.state_after(k, v, gamma, state_in=S0)))
+
+
+def test_backward_matches_finite_differences():
+    B, H, N, dk, dv = 1, 2, 6, 3, 4
+    q, k, v = _inputs(B, H, N, dk, dv, seed=90)
+    S0 = _rand((B, H, dk, dv), seed=91)
+    W = _rand((B, H, N, dv), seed=92)
+    U = _rand((B, H, dk, dv), seed=93)
+    g = np.array([0.9, 0.55])
+    grads = orc.backward(q, k, v, g, W, state_in=S0, d_state_out=U)
+    eps = 1e-6
+    for x, gx in zip((q, k, v, S0), grads):
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args = [q, k, v, S0]
+            i = next(j for j, a in enumerate(args) if a is x)
+            args_p, args_m = list(args), list(args)
+            args_p[i], args_m[i] = xp, xm
+            fd[idx] = (_loss(*args_p, g, W, U) - _loss(*args_m, g, W, U)) / (2 * eps)
+        np.testing.assert_allclose(gx, fd, rtol=0, atol=1e-7)
+
+
+def test_backward_matches_torch_autograd_of_the_recurrence():
+    """Autograd through the token-by-token recurrence (update, then read out)."""
+    B, H, N, dk, dv = 2, 2, 9, 4, 3
+    q, k, v = _inputs(B, H, N, dk, dv, seed=94)
+    S0 = _rand((B, H, dk, dv), seed=95)
+    W = _rand((B, H, N, dv), seed=96)
+    U = _rand((B, H, dk, dv), seed=97)
+    g = np.array([0.8, 0.3])
+    tq, tk, tv, tS = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v, S0))
+    gam = torch.tensor(g, dtype=torch.float64)[None, :, None, None]
+    S = tS
+    outs = []
+    for n in range(N):
+        S = gam * S + tk[:, :, n, :, None] * tv[:, :, n, None, :]
+        outs.append(torch.einsum("bhk,bhkv->bhv", tq[:, :, n], S))
+    O = torch.stack(outs, dim=2)
+    L = (O * torch.from_numpy(W)).sum() + (S * torch.from_numpy(U)).sum()
+    L.backward()
+    ours = orc.backward(q, k, v, g, W, state_in=S0, d_state_out=U)
+    for got, ref in zip(ours, (tq.grad, tk.grad, tv.grad, tS.grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-11)
+
+
+def test_backward_without_state_terms():
+    """No S0 and no dS_N: dS0 is None, and the gradients equal those with zero tensors."""
+    q, k, v = _inputs(1, 1, 7, 3, 5, seed=98)
+    W = _rand((1, 1, 7, 5), seed=99)
+    g = np.array([0.7])
+    a = orc.backward(q, k, v, g, W)
+    b = orc.backward(q, k, v, g, W, state_in=np.zeros((1, 1, 3, 5)), d_state_out=np.zeros((1, 1, 3, 5)))
+    assert a[3] is None
+    for x, y in zip(a[:3], b[:3]):
+        np.testing.assert_allclose(x, y, rtol=0, atol=0)
+    np.testing.assert_allclose(b[3], orc.backward(q, k, v, g, W, state_in=np.zeros((1, 1, 3, 5)))[3], atol=0)
