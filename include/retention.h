@@ -174,6 +174,41 @@ int retention_recurrent_step(const void* q, const void* k, const void* v,
                              int B, int H, int dk, int dv, int dtype,
                              const retention_gn_t* gn, void* stream);
 
+/*
+ * Backward pass of retention: gradients with respect to q, k, v and the
+ * starting state, for training ("RetNet - Retentive Network ...", Key
+ * Equations: the parallel and chunkwise forms are the training forms; the
+ * pages print no gradients). The forward map is the chunkwise form above
+ * without GroupNorm or gate (a caller with those back-propagates through them
+ * first) together with the state it leaves:
+ *   O   = (Q K^T (*) D) V + diag(gamma^(n+1)) Q S0
+ *   S_N = K^T diag(gamma^(N-1-m)) V + gamma^N S0
+ * Given grad_o = dL/dO ([B, H, N, dv], the input type) and grad_state_out =
+ * dL/dS_N (fp32 [B, H, dk, dv], NULL = 0), it writes
+ *   grad_q = dA K + diag(gamma^(n+1)) grad_o S0^T        with A = Q K^T (*) D,
+ *   grad_k = dA^T Q + diag(gamma^(N-1-m)) V dS_N^T            dA = (grad_o V^T) (*) D
+ *   grad_v = A^T grad_o + diag(gamma^(N-1-m)) K dS_N
+ *   grad_state_in = Q^T diag(gamma^(n+1)) grad_o + gamma^N dS_N   (fp32; NULL: not written)
+ * grad_q, grad_k ([B, H, N, dk]) and grad_v ([B, H, N, dv]) have the input
+ * type and must not alias any input. state_in (fp32, NULL = zeros) is the S0
+ * of the forward call. Each gradient is evaluated as a retention of its own
+ * (grad_q forward in time; grad_k and grad_v over the token-reversed sequence)
+ * with the chunkwise kernels at the given chunk; a width above 256 is split
+ * into parts whose results are summed. workspace must hold
+ * retention_chunkwise_backward_workspace_bytes(...) bytes (contents on entry
+ * do not matter and are clobbered). Same status codes as the other entry
+ * points.
+ */
+size_t retention_chunkwise_backward_workspace_bytes(int B, int H, int N, int dk, int dv,
+                                                    int chunk, int dtype);
+
+int retention_chunkwise_backward(const void* q, const void* k, const void* v, const void* grad_o,
+                                 const float* gamma_host, void* grad_q, void* grad_k, void* grad_v,
+                                 int B, int H, int N, int dk, int dv, int chunk, int dtype,
+                                 const float* state_in, const float* grad_state_out,
+                                 float* grad_state_in, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,6 +27,8 @@ __all__ = [
     "chunk_output",
     "recurrent_step",
     "chunkwise_workspace_bytes",
+    "chunkwise_backward",
+    "chunkwise_backward_workspace_bytes",
     "RetentionError",
 ]
 
@@ -247,3 +249,49 @@ def recurrent_step(q, k, v, gamma: GammaLike, state, gn: Optional[GroupNorm] = N
     if rc != 0:
         raise RetentionError("retention_recurrent_step", rc)
     return out
+
+
+def chunkwise_backward_workspace_bytes(B, H, N, dk, dv, chunk, dtype=torch.bfloat16) -> int:
+    code = _lib.RET_BF16 if dtype == torch.bfloat16 else _lib.RET_F32
+    return int(_lib.load().retention_chunkwise_backward_workspace_bytes(B, H, N, dk, dv, int(chunk), code))
+
+
+def chunkwise_backward(q, k, v, grad_o, gamma: GammaLike, chunk: int, state_in=None, grad_state_out=None,
+                       grad_state_in: Union[bool, torch.Tensor] = False, workspace=None, grads=None):
+    """Gradients of the chunkwise form (no GroupNorm or gate) for dL/dO = grad_o.
+
+    Returns (grad_q, grad_k, grad_v, grad_state_in or None). ``grad_state_out``
+    is dL/dS_N (fp32 [B,H,dk,dv], None = 0); ``grad_state_in``: False (not
+    produced), True (allocate) or an fp32 [B,H,dk,dv] tensor to fill.
+    ``grads``: optional preallocated (grad_q, grad_k, grad_v).
+    """
+    lib = _lib.load()
+    B, H, N, dk, dv, dt = _check_qkv(q, k, v)
+    if not grad_o.is_cuda or not grad_o.is_contiguous() or grad_o.dtype != q.dtype or grad_o.shape != v.shape:
+        raise ValueError("grad_o must be a contiguous device tensor shaped and typed like v")
+    for name, t in (("state_in", state_in), ("grad_state_out", grad_state_out), ("grad_state_in", grad_state_in)):
+        if isinstance(t, torch.Tensor):
+            if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (B, H, dk, dv):
+                raise ValueError(f"{name} must be contiguous float32 [B,H,dk,dv]")
+    if grad_state_in is True:
+        grad_state_in = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    elif grad_state_in is False:
+        grad_state_in = None
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    gq, gk, gv = grads
+    nbytes = int(lib.retention_chunkwise_backward_workspace_bytes(B, H, N, dk, dv, int(chunk), dt))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    g = _gamma_array(gamma, H)
+    rc = lib.retention_chunkwise_backward(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), grad_o.data_ptr(), g, gq.data_ptr(), gk.data_ptr(), gv.data_ptr(),
+        B, H, N, dk, dv, int(chunk), dt,
+        state_in.data_ptr() if state_in is not None else None,
+        grad_state_out.data_ptr() if grad_state_out is not None else None,
+        grad_state_in.data_ptr() if grad_state_in is not None else None,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q))
+    if rc != 0:
+        raise RetentionError("retention_chunkwise_backward", rc)
+    return gq, gk, gv, grad_state_in
+

@@ -25,6 +25,8 @@ EXPORTED = (
     "retention_chunk_states",
     "retention_chunk_output",
     "retention_recurrent_step",
+    "retention_chunkwise_backward_workspace_bytes",
+    "retention_chunkwise_backward",
 )
 
 
@@ -72,6 +74,11 @@ def load():
     lib.retention_chunk_output.restype = i
     lib.retention_recurrent_step.argtypes = [vp, vp, vp, f_p, vp, vp, i, i, i, i, i, gn_p, vp]
     lib.retention_recurrent_step.restype = i
+    lib.retention_chunkwise_backward_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.retention_chunkwise_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.retention_chunkwise_backward.argtypes = [vp, vp, vp, vp, f_p, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, vp,
+                                                 vp, ctypes.c_size_t, vp]
+    lib.retention_chunkwise_backward.restype = i
     if lib.retention_abi_version() != ABI_VERSION:
         raise RuntimeError(
             f"{LIB_PATH} has ABI version {lib.retention_abi_version()}, this binding expects {ABI_VERSION}: rebuild it"

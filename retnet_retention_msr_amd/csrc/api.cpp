@@ -5,6 +5,7 @@
 // pure function of the sizes: it picks the MFMA kernels for bf16 shapes they
 // cover and the generic vector-ALU kernels otherwise, and it sizes the
 // chunkwise workspace.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -142,6 +143,68 @@ hipError_t launch_output(const ChunkPlan& p, const void* q, const void* k, const
                                        decay, g, s);
 }
 
+// Backward plan: operand copies, partial results, state transforms and the
+// workspace of the chunkwise calls, laid out one after another.
+constexpr int kPartWidth = 256;  // widest query/key dimension the MFMA kernels take
+
+struct BackwardPlan {
+  int nparts;  // parts of the dv-wide query/key dimension of the dQ and dK retentions
+  int part_w;
+  size_t qf, kf, dof, oa, dos, vs, dofs, vfs, qpart, kpart;  // byte offsets (token-row buffers)
+  size_t s_a, s_t, s_0t, s_nt;                               // fp32 state buffers
+  size_t cw;                                                 // chunkwise workspace
+  size_t cw_bytes;
+  size_t total;
+};
+
+BackwardPlan plan_backward(int B, int H, int N, int dk, int dv, int chunk, int dtype) {
+  BackwardPlan p{};
+  p.nparts = dv > kPartWidth ? (dv + kPartWidth - 1) / kPartWidth : 1;
+  p.part_w = dv > kPartWidth ? kPartWidth : dv;
+  const size_t es = dtype == RET_F32 ? 4 : 2;
+  const size_t tok = static_cast<size_t>(B) * H * N;
+  const size_t st = static_cast<size_t>(B) * H * dk * dv * sizeof(float);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  p.qf = take(tok * dk * es);
+  p.kf = take(tok * dk * es);
+  p.dof = take(tok * dv * es);
+  p.oa = take(tok * dv * es);
+  const bool split = p.nparts > 1;
+  p.dos = split ? take(tok * dv * es) : 0;
+  p.vs = split ? take(tok * dv * es) : 0;
+  p.dofs = split ? take(tok * dv * es) : 0;
+  p.vfs = take(tok * dv * es);
+  p.qpart = split ? take(static_cast<size_t>(p.nparts) * tok * dk * es) : 0;
+  p.kpart = take(static_cast<size_t>(p.nparts) * tok * dk * es);
+  p.s_a = take(st);
+  p.s_t = take(st);
+  p.s_0t = take(st);
+  p.s_nt = take(st);
+  size_t cw = plan_chunkwise(B, H, N, dk, dv, chunk, dtype).total;
+  for (int q = 0; q < p.nparts; ++q) {
+    const int w = std::min(p.part_w, dv - q * p.part_w);
+    cw = std::max(cw, plan_chunkwise(B, H, N, w, dk, chunk, dtype).total);
+  }
+  p.cw_bytes = cw;
+  p.cw = take(cw);
+  p.total = off;
+  return p;
+}
+
+// One retention (both chunkwise stages) for the backward pass: no GroupNorm.
+int run_retention(const void* q, const void* k, const void* v, void* o, const float* state_in, float* state_out,
+                  const Dims& d, int chunk, int dtype, const HeadDecay& decay, char* cw, hipStream_t s) {
+  const ChunkPlan p = plan_chunkwise(d.B, d.H, d.N, d.dk, d.dv, chunk, dtype);
+  GnArgs none{};
+  if (launch_states(p, k, v, state_in, state_out, cw, d, chunk, dtype, decay, s) != hipSuccess) return RET_ERR_HIP;
+  return status_of(launch_output(p, q, k, v, o, cw, state_in != nullptr, d, chunk, dtype, decay, none, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -248,6 +311,119 @@ int retention_recurrent_step(const void* q, const void* k, const void* v, const 
   check_gamma(gamma_host, H, &decay);
   return status_of(ret::launch_decode_step(dtype, q, k, v, state, o, B, H, dk, dv, decay, g,
                                            static_cast<hipStream_t>(stream)));
+}
+
+size_t retention_chunkwise_backward_workspace_bytes(int B, int H, int N, int dk, int dv, int chunk, int dtype) {
+  if (check_sizes(B, H, N, dk, dv, dtype) != RET_OK || chunk <= 0) return 0;
+  return plan_backward(B, H, N, dk, dv, chunk, dtype).total;
+}
+
+int retention_chunkwise_backward(const void* q, const void* k, const void* v, const void* grad_o,
+                                 const float* gamma_host, void* grad_q, void* grad_k, void* grad_v, int B, int H,
+                                 int N, int dk, int dv, int chunk, int dtype, const float* state_in,
+                                 const float* grad_state_out, float* grad_state_in, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !grad_o || !grad_q || !grad_k || !grad_v || chunk <= 0) return RET_ERR_INVALID_ARG;
+  int st = check_sizes(B, H, N, dk, dv, dtype);
+  if (st != RET_OK) return st;
+  st = check_gamma(gamma_host, H, nullptr);
+  if (st != RET_OK) return st;
+  const BackwardPlan p = plan_backward(B, H, N, dk, dv, chunk, dtype);
+  if (!workspace || workspace_bytes < p.total) return RET_ERR_INVALID_ARG;
+  HeadDecay decay;
+  check_gamma(gamma_host, H, &decay);
+  float inv_gamma[RETENTION_MAX_HEADS], fwd_gamma[RETENTION_MAX_HEADS];
+  for (int h = 0; h < H; ++h) {
+    fwd_gamma[h] = gamma_host[h];
+    inv_gamma[h] = static_cast<float>(1.0 / static_cast<double>(gamma_host[h]));
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const size_t es = dtype == RET_F32 ? 4 : 2;
+  const int64_t tok = static_cast<int64_t>(B) * H * N;
+  const Dims rows{B, H, N, 0, 0};
+  auto at = [&](size_t off) { return static_cast<void*>(ws + off); };
+  auto st_at = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  auto ok = [](hipError_t e) { return e == hipSuccess; };
+  char* cw = ws + p.cw;
+
+  // Token-reversed copies of Q, K and dO.
+  if (!ok(ret::launch_split_rows(dtype, q, at(p.qf), rows, dk, dk, 0, true, s))) return RET_ERR_HIP;
+  if (!ok(ret::launch_split_rows(dtype, k, at(p.kf), rows, dk, dk, 0, true, s))) return RET_ERR_HIP;
+  if (!ok(ret::launch_split_rows(dtype, grad_o, at(p.dof), rows, dv, dv, 0, true, s))) return RET_ERR_HIP;
+
+  // dV (and the state gradient): reverse-time retention with query K, key Q,
+  // value dO; the final-state gradient enters as its starting state divided
+  // by gamma (the reversed read-out weighs row m' by gamma^(m'+1), the term
+  // needs gamma^m').
+  float* s_a = nullptr;
+  if (grad_state_out) {
+    s_a = st_at(p.s_a);
+    if (!ok(ret::launch_state_prep(grad_state_out, s_a, B, H, dk, dv, false, dv, 0, inv_gamma, s))) return RET_ERR_HIP;
+  }
+  float* s_t = grad_state_in ? st_at(p.s_t) : nullptr;
+  st = run_retention(at(p.kf), at(p.qf), at(p.dof), at(p.oa), s_a, s_t, Dims{B, H, N, dk, dv}, chunk, dtype, decay,
+                     cw, s);
+  if (st != RET_OK) return st;
+  if (!ok(ret::launch_sum_parts(dtype, at(p.oa), grad_v, rows, dv, 1, 0, true, s))) return RET_ERR_HIP;
+  // Its final state T = sum_n gamma^n q_n^T dO_n + gamma^(N-1) dS_N; the state
+  // gradient is gamma T.
+  if (grad_state_in) {
+    if (!ok(ret::launch_state_prep(s_t, grad_state_in, B, H, dk, dv, false, dv, 0, fwd_gamma, s))) return RET_ERR_HIP;
+  }
+
+  // Operands of the dQ and dK retentions, their query/key width (dv) cut into
+  // parts of at most 256 columns.
+  const int P = p.nparts, pw = p.part_w;
+  const int64_t part_rows = tok * pw;  // elements between parts (every part but the last is pw wide)
+  const void* dos = grad_o;
+  const void* vs = v;
+  const void* dofs = at(p.dof);
+  if (P > 1) {
+    if (!ok(ret::launch_split_rows(dtype, grad_o, at(p.dos), rows, dv, pw, part_rows, false, s))) return RET_ERR_HIP;
+    if (!ok(ret::launch_split_rows(dtype, v, at(p.vs), rows, dv, pw, part_rows, false, s))) return RET_ERR_HIP;
+    if (!ok(ret::launch_split_rows(dtype, at(p.dof), at(p.dofs), rows, dv, pw, part_rows, false, s)))
+      return RET_ERR_HIP;
+    dos = at(p.dos);
+    vs = at(p.vs);
+    dofs = at(p.dofs);
+  }
+  if (!ok(ret::launch_split_rows(dtype, v, at(p.vfs), rows, dv, pw, part_rows, true, s))) return RET_ERR_HIP;
+  const int64_t st_part = static_cast<int64_t>(B) * H * pw * dk;  // fp32 elements between state parts
+  float* s_0t = nullptr;
+  if (state_in) {
+    s_0t = st_at(p.s_0t);
+    if (!ok(ret::launch_state_prep(state_in, s_0t, B, H, dk, dv, true, pw, st_part, nullptr, s))) return RET_ERR_HIP;
+  }
+  float* s_nt = nullptr;
+  if (grad_state_out) {
+    s_nt = st_at(p.s_nt);
+    if (!ok(ret::launch_state_prep(grad_state_out, s_nt, B, H, dk, dv, true, pw, st_part, inv_gamma, s)))
+      return RET_ERR_HIP;
+  }
+
+  auto part = [&](const void* base, int i) {
+    return static_cast<const void*>(static_cast<const char*>(base) + static_cast<size_t>(i) * part_rows * es);
+  };
+  const int64_t out_part = tok * dk;  // elements between partial results
+  for (int i = 0; i < P; ++i) {
+    const int w = std::min(pw, dv - i * pw);
+    const Dims dd{B, H, N, w, dk};
+    // dQ part: query dO, key V, value K, starting state S0^T (rows of the part).
+    void* oq = P > 1 ? static_cast<void*>(ws + p.qpart + static_cast<size_t>(i) * out_part * es) : grad_q;
+    st = run_retention(part(dos, i), part(vs, i), k, oq, s_0t ? s_0t + i * st_part : nullptr, nullptr, dd, chunk,
+                       dtype, decay, cw, s);
+    if (st != RET_OK) return st;
+    // dK part (reversed time): query V, key dO, value Q, starting state dS_N^T / gamma.
+    void* ok_ = static_cast<void*>(ws + p.kpart + static_cast<size_t>(i) * out_part * es);
+    st = run_retention(part(at(p.vfs), i), part(dofs, i), at(p.qf), ok_, s_nt ? s_nt + i * st_part : nullptr,
+                       nullptr, dd, chunk, dtype, decay, cw, s);
+    if (st != RET_OK) return st;
+  }
+  if (P > 1 && !ok(ret::launch_sum_parts(dtype, at(p.qpart), grad_q, rows, dk, P, out_part, false, s)))
+    return RET_ERR_HIP;
+  return status_of(ret::launch_sum_parts(dtype, at(p.kpart), grad_k, rows, dk, P, out_part, true, s));
 }
 
 }  // extern "C"

@@ -65,4 +65,20 @@ hipError_t launch_mfma_chunk_out(const uint16_t* q, const uint16_t* k, const uin
 // Whether the MFMA kernels implement these sizes.
 bool mfma_supports(int dk, int dv);
 
+// Backward-pass data movement (d.B, d.H, d.N are used; rows are tokens).
+// split_rows: src [B*H, N, D] -> parts of width part_w (the last may be
+// narrower), part p at dst + p * part_stride as [B*H, N, w_p], rows token-
+// reversed within each head when `flip`.
+hipError_t launch_split_rows(int dtype, const void* src, void* dst, const Dims& d, int D, int part_w,
+                             int64_t part_stride, bool flip, hipStream_t stream);
+// sum_parts: dst [B*H, N, W] = sum of nparts buffers [B*H, N, W] (part_stride
+// elements apart), read token-reversed when `flip`; fp32 sums.
+hipError_t launch_sum_parts(int dtype, const void* parts, void* dst, const Dims& d, int W, int nparts,
+                            int64_t part_stride, bool flip, hipStream_t stream);
+// state_prep: fp32 [B*H, R, C] times a per-head factor (head_factor: host
+// array of H floats, nullptr = 1), or its transpose split into parts of
+// part_w rows ([B*H, w_p, R] each, part_stride elements apart).
+hipError_t launch_state_prep(const float* src, float* dst, int B, int H, int R, int C, bool transpose, int part_w,
+                             int64_t part_stride, const float* head_factor, hipStream_t stream);
+
 }  // namespace ret

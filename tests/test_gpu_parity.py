@@ -411,3 +411,36 @@ def test_stage_entry_points_equal_chunkwise(dtype, dk, dv, C):
     ret.chunk_states(kd, vd, g, C, ws, state_in=S0d, state_out=S)
     o = ret.chunk_output(qd, kd, vd, g, C, ws, has_state_in=True, gn=gn)
     assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
+
+
+# ---------------------------------------------------------------------------
+# Backward pass: gradients against the oracle's (pinned) backward
+# ---------------------------------------------------------------------------
+BACKWARD_SHAPES = [
+    # B, H, N, dk, dv, chunk, dtype
+    (2, 2, 300, 64, 128, 64, torch.bfloat16),   # gradient retentions on MFMA (dV) and generic (dQ, dK)
+    (1, 2, 257, 128, 256, 128, torch.bfloat16),  # all on MFMA, one part
+    (1, 2, 200, 256, 512, 64, torch.bfloat16),   # all on MFMA, dv split into two 256-wide parts
+    (1, 2, 45, 24, 300, 16, torch.float32),      # generic, dv split 256 + 44
+]
+
+
+@pytest.mark.parametrize("B,H,N,dk,dv,C,dtype", BACKWARD_SHAPES)
+@pytest.mark.parametrize("with_state", [False, True])
+def test_chunkwise_backward_matches_oracle(B, H, N, dk, dv, C, dtype, with_state):
+    _announce(f"backward {B}x{H}x{N} dk={dk} dv={dv} C={C} {dtype} state={with_state}")
+    q, k, v, g, S0 = _inputs(B, H, N, dk, dv, dtype, seed=N + dk, with_state=with_state)
+    dO = synthetic.make_qkv(B, H, N, dk, dv, dtype=dtype, seed=N + 77)[2]
+    dSN = synthetic.make_state(B, H, dk, dv, seed=N + 78, std=0.5) if with_state else None
+    # (a zero starting state for the oracle when there is none, so that it also
+    # returns the state gradient, which the GPU computes regardless)
+    S0_ref = S0 if S0 is not None else torch.zeros(B, H, dk, dv)
+    ref = orc.backward(q, k, v, g, dO, state_in=S0_ref, d_state_out=dSN)
+    qd, kd, vd, dOd, S0d, dSNd = _dev(q, k, v, dO, S0, dSN)
+    gq, gk, gv, gs = ret.chunkwise_backward(qd, kd, vd, dOd, g, C, state_in=S0d, grad_state_out=dSNd,
+                                            grad_state_in=True)
+    tol = TOL[dtype]
+    _check(gq, ref[0], tol, "grad_q")
+    _check(gk, ref[1], tol, "grad_k")
+    _check(gv, ref[2], tol, "grad_v")
+    _check(gs, ref[3], tol, "grad_state_in")

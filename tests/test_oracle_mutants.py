@@ -100,3 +100,42 @@ def test_gate_mutants_are_caught(kind):
         y = orc.group_norm(orc.swish(gate) * o)
     assert np.max(np.abs(y - pin)) > 1e-6, kind
     np.testing.assert_allclose(orc.gated_group_norm(o, gate), pin, rtol=0, atol=1e-13)
+
+
+def _backward_mutant(q, k, v, g, G, U, kind):
+    """dQ, dK, dV with one planted slip (single head, no starting state)."""
+    Q, K, V, G, U = q[0, 0], k[0, 0], v[0, 0], G[0, 0], U[0, 0]
+    N = Q.shape[0]
+    D = orc.decay_mask(N, g)
+    zeta = g ** np.arange(N - 1, -1, -1, dtype=np.float64)
+    if kind == "zeta_reversed":
+        zeta = zeta[::-1]
+    A = (Q @ K.T) * D
+    dA = (G @ V.T) * (np.tril(np.ones((N, N))) if kind == "mask_without_decay" else D)
+    dq = dA @ K
+    dk = (dA @ Q if kind == "dA_not_transposed" else dA.T @ Q) + zeta[:, None] * (V @ U.T)
+    dv = A.T @ G + zeta[:, None] * (K @ U)
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("kind", ["mask_without_decay", "dA_not_transposed", "zeta_reversed"])
+def test_backward_mutants_are_caught(kind):
+    """The pin: autograd through the token recurrence (as in test_oracle)."""
+    import torch
+
+    q, k, v = _inputs(1, 1, 7, 3, 3, seed=13)
+    rng = np.random.default_rng(14)
+    G, U = rng.standard_normal((1, 1, 7, 3)), rng.standard_normal((1, 1, 3, 3))
+    g = 0.8
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    S = torch.zeros(1, 1, 3, 3, dtype=torch.float64)
+    outs = []
+    for n in range(7):
+        S = g * S + tk[:, :, n, :, None] * tv[:, :, n, None, :]
+        outs.append(torch.einsum("bhk,bhkv->bhv", tq[:, :, n], S))
+    ((torch.stack(outs, 2) * torch.from_numpy(G)).sum() + (S * torch.from_numpy(U)).sum()).backward()
+    ref = [t.grad.numpy()[0, 0] for t in (tq, tk, tv)]
+    got = _backward_mutant(q, k, v, g, G, U, kind)
+    assert max(np.max(np.abs(a - b)) for a, b in zip(got, ref)) > 1e-6, kind
+    ok = _backward_mutant(q, k, v, g, G, U, "none")
+    assert max(np.max(np.abs(a - b)) for a, b in zip(ok, ref)) < 1e-10
