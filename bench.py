@@ -21,6 +21,9 @@ flops over time against the 2.5 PFLOP/s dense bf16 peak). `step_roofline`
 does the same for the whole step (both stages), `state_walk` for the first
 stage. `gated` times the same prefill with the gated epilogue
 swish(gate) * GroupNorm(O) (the output kernel then also reads the bf16 gate).
+`backward` times the backward pass (dQ, dK, dV) of the same prefill, with
+the flops its decomposition executes against the bf16 MFMA peak and its
+irreducible bytes against HBM.
 `decode` carries the decode step's latency and its HBM roofline
 (134,610,944 algorithmic bytes per step against 8 TB/s);
 `decode_cache_defeating` repeats it at B=32, whose 256 MiB state does not fit
@@ -53,6 +56,7 @@ B, H, N, DK, DV, CHUNK = 8, 16, 8192, 256, 512, 512
 SEED = 1003
 DECODE_SEED = 1004
 GATE_SEED = 1006
+BACKWARD_SEED = 1007
 PEAK_BF16 = 2.5e15
 PEAK_HBM = 8.0e12
 FLOP_PER_TOKEN_HEAD = {64: 574_208, 128: 623_360, 256: 721_664, 512: 918_272}
@@ -379,6 +383,54 @@ def cpu_baseline(q, k, v, gamma, n_batch_rows=2):
     }
 
 
+def backward_flops(B, H, N, chunk, dk=DK, dv=DV, part=256):
+    """Flops the backward executes: one retention of the forward's size for dV,
+    and for dQ and dK one retention per part of the dv-wide query/key width
+    (parts of at most 256, value width dk), each counted like the forward."""
+    total = algorithmic_flops(B, H, N, chunk, dk, dv)
+    for c in range(0, dv, part if dv > part else dv):
+        w = min(part if dv > part else dv, dv - c)
+        total += 2 * algorithmic_flops(B, H, N, chunk, w, dk)
+    return total
+
+
+def backward_min_bytes(B, H, N, dk=DK, dv=DV):
+    """The backward's irreducible HBM traffic: bf16 Q, K, V and dO read, dQ, dK, dV written."""
+    return float(B * H * N * ((2 * dk + 2 * dv) + (2 * dk + dv)) * 2)
+
+
+def backward_pass(ret, torch, dev, stream, qd, kd, vd, gamma, steps, warmup=3):
+    """The backward pass of the same prefill (no states): dQ, dK, dV for a seeded dO."""
+    gen = torch.Generator(device=dev).manual_seed(BACKWARD_SEED)
+    dO = torch.randn(B, H, N, DV, generator=gen, device=dev).to(torch.bfloat16)
+    grads = (torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd))
+    ws = torch.empty(ret.chunkwise_backward_workspace_bytes(B, H, N, DK, DV, CHUNK), dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        ret.chunkwise_backward(qd, kd, vd, dO, gamma, CHUNK, workspace=ws, grads=grads)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        ret.chunkwise_backward(qd, kd, vd, dO, gamma, CHUNK, workspace=ws, grads=grads)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flop = backward_flops(B, H, N, CHUNK)
+    nbytes = backward_min_bytes(B, H, N)
+    del dO, grads, ws
+    return {
+        "workload": "backward of the prefill above without GroupNorm or states: dQ, dK, dV for bf16 dO ~ N(0,1)",
+        "steps": steps,
+        "ms": ms,
+        "tokens_per_s": B * N / (ms * 1e-3),
+        "executed_flop": flop,
+        "mfma_tflops": flop / (ms * 1e-3) / 1e12,
+        "mfma_frac": flop / (ms * 1e-3) / PEAK_BF16,
+        "min_bytes": nbytes,
+        "hbm_frac_of_min_bytes": nbytes / (ms * 1e-3) / PEAK_HBM,
+    }
+
+
 def gated_prefill(ret, torch, dev, stream, qd, kd, vd, gamma, ws, state, out, gn, steps, warmup=5):
     """The same prefill with the gated epilogue, swish(gate) * GroupNorm(O).
 
@@ -443,6 +495,7 @@ def main():
     ap.add_argument("--skip-small", action="store_true", help="skip the B=2 H=8 N=2048 timings")
     ap.add_argument("--skip-decode-b32", action="store_true", help="skip the cache-defeating B=32 decode timing")
     ap.add_argument("--skip-gated", action="store_true", help="skip the swish-gated prefill timing")
+    ap.add_argument("--skip-backward", action="store_true", help="skip the backward-pass timing")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -515,6 +568,11 @@ def main():
     if not args.skip_gated:
         print(f"[bench] timing {args.steps} swish-gated prefill steps", file=sys.stderr, flush=True)
         gated = gated_prefill(ret, torch, dev, stream, qd, kd, vd, gamma, ws, state, out, gn, args.steps)
+
+    backward = None
+    if not args.skip_backward:
+        print(f"[bench] timing {args.steps} backward passes", file=sys.stderr, flush=True)
+        backward = backward_pass(ret, torch, dev, stream, qd, kd, vd, gamma, args.steps)
 
     # Decode: single-token steps from the prefill's state.
     if args.skip_decode:
@@ -621,6 +679,7 @@ def main():
             "traffic": traffic["state_walk"],
         },
         "gated": gated,
+        "backward": backward,
         "decode": {
             "steps": T,
             "us_per_step": us_step,

@@ -6,6 +6,7 @@ package. It never imports the HIP library or its binding.
 
 from .retention_oracle import (  # noqa: F401
     backward,
+    backward_rows,
     chunkwise,
     decay_mask,
     gated_group_norm,

@@ -263,6 +263,44 @@ def backward(q, k, v, gamma, d_o, state_in=None, d_state_out=None):
     return dq, dk_, dv_, dS0
 
 
+def backward_rows(q, k, v, gamma, d_o, rows, state_in=None, d_state_out=None):
+    """Rows of the gradients of ``backward``, each row on its own (for sampled
+    checks on long sequences). Same maps and result as ``backward``, written
+    per token: for a row n of dQ and a row m of dK and dV,
+        dQ_n = sum_{m<=n} gamma^(n-m) (dO_n . v_m) k_m + gamma^(n+1) dO_n S0^T
+        dK_m = sum_{n>=m} gamma^(n-m) (dO_n . v_m) q_n + gamma^(N-1-m) v_m dS_N^T
+        dV_m = sum_{n>=m} gamma^(n-m) (q_n . k_m) dO_n + gamma^(N-1-m) k_m dS_N
+    Returns (dq, dk, dv) of shape [B, H, len(rows), d].
+    """
+    q, k, v, d_o = _f64(q), _f64(k), _f64(v), _f64(d_o)
+    g = _f64(gamma)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    rows = [int(r) for r in rows]
+    S0 = None if state_in is None else _f64(state_in)
+    dSN = None if d_state_out is None else _f64(d_state_out)
+    R = len(rows)
+    dq, dk_, dv_ = np.zeros((B, H, R, dk)), np.zeros((B, H, R, dk)), np.zeros((B, H, R, dv))
+    for h in range(H):
+        for b in range(B):
+            Q, K, V, G = q[b, h], k[b, h], v[b, h], d_o[b, h]
+            for i, n in enumerate(rows):
+                m = np.arange(n + 1)
+                w = np.power(g[h], (n - m).astype(np.float64)) * (V[: n + 1] @ G[n])
+                dq[b, h, i] = w @ K[: n + 1]
+                if S0 is not None:
+                    dq[b, h, i] += g[h] ** (n + 1) * (S0[b, h] @ G[n])
+                later = np.arange(n, N)
+                decay = np.power(g[h], (later - n).astype(np.float64))
+                dk_[b, h, i] = (decay * (G[n:] @ V[n])) @ Q[n:]
+                dv_[b, h, i] = (decay * (Q[n:] @ K[n])) @ G[n:]
+                if dSN is not None:
+                    z = g[h] ** (N - 1 - n)
+                    dk_[b, h, i] += z * (dSN[b, h] @ V[n])
+                    dv_[b, h, i] += z * (K[n] @ dSN[b, h])
+    return dq, dk_, dv_
+
+
 def group_norm(o, eps=1e-5, weight=None, bias=None):
     """Per-head GroupNorm applied to retention outputs.
 

@@ -119,6 +119,26 @@ def test_6p7b_prefill_gated_sampled(prefill_6p7b):
         _check(_f64(out[b : b + 1, :, rows]), ref, f"gated o rows b={b}")
 
 
+def test_6p7b_backward_sampled(prefill_6p7b):
+    """The backward pass at the 6.7B prefill shape, as the bench times it (no
+    states, chunk 512): sampled rows of dQ, dK and dV of two batch rows."""
+    _announce("B=8 H=16 N=8192 chunk 512 backward: sampled rows of dQ, dK, dV")
+    q, k, v = prefill_6p7b
+    B, H, N, dk = q.shape
+    dv, C = v.shape[-1], 512
+    g = synthetic.head_gammas(H)
+    dO = synthetic.make_qkv(B, H, N, dk, dv, dtype=torch.bfloat16, seed=1007)[2]
+    qd, kd, vd, dOd = q.to(DEV), k.to(DEV), v.to(DEV), dO.to(DEV)
+    gq, gk, gv, _ = ret.chunkwise_backward(qd, kd, vd, dOd, g, C)
+    torch.cuda.synchronize()
+    rows = _rows(N, C, seed=5, n_random=2)
+    for b in (0, B - 1):
+        ref = orc.backward_rows(_f64(q[b : b + 1]), _f64(k[b : b + 1]), _f64(v[b : b + 1]), g,
+                                _f64(dO[b : b + 1]), rows)
+        for name, got, r in zip(("dq", "dk", "dv"), (gq, gk, gv), ref):
+            _check(_f64(got[b : b + 1, :, rows]), r, f"{name} rows b={b}")
+
+
 def test_decode_step_full_shape():
     _announce("decode step on fp32 [8,16,256,512], 4 steps")
     B, H, dk, dv = 8, 16, 256, 512

@@ -488,3 +488,17 @@ def test_backward_without_state_terms():
     for x, y in zip(a[:3], b[:3]):
         np.testing.assert_allclose(x, y, rtol=0, atol=0)
     np.testing.assert_allclose(b[3], orc.backward(q, k, v, g, W, state_in=np.zeros((1, 1, 3, 5)))[3], atol=0)
+
+
+def test_backward_rows_equal_backward():
+    """The per-row gradients equal the matrix form's rows (first, last, middle)."""
+    q, k, v = _inputs(2, 2, 13, 3, 4, seed=100)
+    S0 = _rand((2, 2, 3, 4), seed=101)
+    W = _rand((2, 2, 13, 4), seed=102)
+    U = _rand((2, 2, 3, 4), seed=103)
+    g = np.array([0.85, 0.4])
+    full = orc.backward(q, k, v, g, W, state_in=S0, d_state_out=U)
+    rows = [0, 5, 12]
+    part = orc.backward_rows(q, k, v, g, W, rows, state_in=S0, d_state_out=U)
+    for a, b in zip(part, full[:3]):
+        np.testing.assert_allclose(a, b[:, :, rows], rtol=0, atol=1e-12)
