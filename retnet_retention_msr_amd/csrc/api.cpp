@@ -348,10 +348,24 @@ int retention_chunkwise_backward(const void* q, const void* k, const void* v, co
   auto ok = [](hipError_t e) { return e == hipSuccess; };
   char* cw = ws + p.cw;
 
-  // Token-reversed copies of Q, K and dO.
-  if (!ok(ret::launch_split_rows(dtype, q, at(p.qf), rows, dk, dk, 0, true, s))) return RET_ERR_HIP;
-  if (!ok(ret::launch_split_rows(dtype, k, at(p.kf), rows, dk, dk, 0, true, s))) return RET_ERR_HIP;
-  if (!ok(ret::launch_split_rows(dtype, grad_o, at(p.dof), rows, dv, dv, 0, true, s))) return RET_ERR_HIP;
+  // Operand copies, each source read once: Q and K token-reversed; dO
+  // token-reversed whole (the dV retention's value) and, when the dv-wide
+  // query/key width of the dQ and dK retentions is cut into parts of at most
+  // 256 columns, in parts as it is and token-reversed; V in parts reversed
+  // and, when cut, as it is.
+  const int P = p.nparts, pw = p.part_w;
+  const int64_t part_rows = tok * pw;  // elements between parts (every part but the last is pw wide)
+  {
+    const ret::SplitTarget tq[1] = {{at(p.qf), dk, 0, true}};
+    const ret::SplitTarget tk[1] = {{at(p.kf), dk, 0, true}};
+    const ret::SplitTarget to[3] = {{at(p.dof), dv, 0, true}, {at(p.dos), pw, part_rows, false},
+                                    {at(p.dofs), pw, part_rows, true}};
+    const ret::SplitTarget tv[2] = {{at(p.vfs), pw, part_rows, true}, {at(p.vs), pw, part_rows, false}};
+    if (!ok(ret::launch_split_rows(dtype, q, tq, 1, rows, dk, s))) return RET_ERR_HIP;
+    if (!ok(ret::launch_split_rows(dtype, k, tk, 1, rows, dk, s))) return RET_ERR_HIP;
+    if (!ok(ret::launch_split_rows(dtype, grad_o, to, P > 1 ? 3 : 1, rows, dv, s))) return RET_ERR_HIP;
+    if (!ok(ret::launch_split_rows(dtype, v, tv, P > 1 ? 2 : 1, rows, dv, s))) return RET_ERR_HIP;
+  }
 
   // dV (and the state gradient): reverse-time retention with query K, key Q,
   // value dO; the final-state gradient enters as its starting state divided
@@ -373,23 +387,10 @@ int retention_chunkwise_backward(const void* q, const void* k, const void* v, co
     if (!ok(ret::launch_state_prep(s_t, grad_state_in, B, H, dk, dv, false, dv, 0, fwd_gamma, s))) return RET_ERR_HIP;
   }
 
-  // Operands of the dQ and dK retentions, their query/key width (dv) cut into
-  // parts of at most 256 columns.
-  const int P = p.nparts, pw = p.part_w;
-  const int64_t part_rows = tok * pw;  // elements between parts (every part but the last is pw wide)
-  const void* dos = grad_o;
-  const void* vs = v;
-  const void* dofs = at(p.dof);
-  if (P > 1) {
-    if (!ok(ret::launch_split_rows(dtype, grad_o, at(p.dos), rows, dv, pw, part_rows, false, s))) return RET_ERR_HIP;
-    if (!ok(ret::launch_split_rows(dtype, v, at(p.vs), rows, dv, pw, part_rows, false, s))) return RET_ERR_HIP;
-    if (!ok(ret::launch_split_rows(dtype, at(p.dof), at(p.dofs), rows, dv, pw, part_rows, false, s)))
-      return RET_ERR_HIP;
-    dos = at(p.dos);
-    vs = at(p.vs);
-    dofs = at(p.dofs);
-  }
-  if (!ok(ret::launch_split_rows(dtype, v, at(p.vfs), rows, dv, pw, part_rows, true, s))) return RET_ERR_HIP;
+  // Operands of the dQ and dK retentions (copied above).
+  const void* dos = P > 1 ? at(p.dos) : grad_o;
+  const void* vs = P > 1 ? at(p.vs) : v;
+  const void* dofs = P > 1 ? at(p.dofs) : at(p.dof);
   const int64_t st_part = static_cast<int64_t>(B) * H * pw * dk;  // fp32 elements between state parts
   float* s_0t = nullptr;
   if (state_in) {

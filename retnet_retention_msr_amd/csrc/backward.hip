@@ -34,30 +34,52 @@ struct Vec16<float> {
   static constexpr int kElems = 4;
 };
 
-// dst part p (layout [BH, N, w_p], w_p = part_w except a narrower last part)
-// row r' <- columns [p*part_w, p*part_w + w_p) of src row r ([BH, N, D]),
-// with r' = r or its token reversal within the head. VEC: every width is a
-// multiple of 16 bytes, copied in 16-byte pieces.
+// Up to three destinations of one source row: part p of destination t
+// (layout [BH, N, w_p], w_p = part_w except a narrower last part) gets
+// columns [p*part_w, p*part_w + w_p) of src row r ([BH, N, D]) at row r or at
+// its token reversal within the head. One read of the source feeds them all.
+// VEC: every width is a multiple of 16 bytes, copied in 16-byte pieces.
+template <typename T>
+struct SplitDst {
+  T* base[3];
+  int part_w[3];
+  int64_t part_stride[3];
+  int flip[3];
+  int count;
+};
+
 template <typename T, bool VEC>
 __global__ void __launch_bounds__(kRowThreads)
-split_rows_kernel(const T* __restrict__ src, T* __restrict__ dst, int64_t rows, int N, int D, int part_w,
-                  int64_t part_stride, int flip) {
+split_rows_kernel(const T* __restrict__ src, SplitDst<T> dst, int64_t rows, int N, int D) {
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int lane = threadIdx.x & 63;
   const int64_t bh = row / N;
   const int n = static_cast<int>(row - bh * N);
-  const int nd = flip ? N - 1 - n : n;
   const T* s = src + row * D;
-  for (int c0 = 0, p = 0; c0 < D; c0 += part_w, ++p) {
-    const int w = min(part_w, D - c0);
-    T* d = dst + p * part_stride + (bh * N + nd) * static_cast<int64_t>(w);
-    if constexpr (VEC) {
-      constexpr int E = Vec16<T>::kElems;
-      for (int c = lane * E; c < w; c += 64 * E)
-        *reinterpret_cast<uint4*>(d + c) = *reinterpret_cast<const uint4*>(s + c0 + c);
-    } else {
-      for (int c = lane; c < w; c += 64) d[c] = s[c0 + c];
+  if constexpr (VEC) {
+    constexpr int E = Vec16<T>::kElems;
+    for (int c = lane * E; c < D; c += 64 * E) {
+      const uint4 x = *reinterpret_cast<const uint4*>(s + c);
+      for (int t = 0; t < dst.count; ++t) {
+        const int pw = dst.part_w[t];
+        const int p = c / pw, cc = c - p * pw;
+        const int w = min(pw, D - p * pw);
+        const int nd = dst.flip[t] ? N - 1 - n : n;
+        *reinterpret_cast<uint4*>(dst.base[t] + p * dst.part_stride[t] + (bh * N + nd) * static_cast<int64_t>(w) +
+                                  cc) = x;
+      }
+    }
+  } else {
+    for (int c = lane; c < D; c += 64) {
+      const T x = s[c];
+      for (int t = 0; t < dst.count; ++t) {
+        const int pw = dst.part_w[t];
+        const int p = c / pw, cc = c - p * pw;
+        const int w = min(pw, D - p * pw);
+        const int nd = dst.flip[t] ? N - 1 - n : n;
+        dst.base[t][p * dst.part_stride[t] + (bh * N + nd) * static_cast<int64_t>(w) + cc] = x;
+      }
     }
   }
 }
@@ -136,29 +158,35 @@ bool vec_ok(int esize, int D, int part_w, const void* a, const void* b) {
 
 }  // namespace
 
-hipError_t launch_split_rows(int dtype, const void* src, void* dst, const Dims& d, int D, int part_w,
-                             int64_t part_stride, bool flip, hipStream_t stream) {
+template <typename T>
+hipError_t split_typed(const void* src, const SplitTarget* targets, int ntargets, const Dims& d, int D,
+                       hipStream_t stream) {
   const int64_t rows = static_cast<int64_t>(d.B) * d.H * d.N;
-  if (rows == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-  const int f = flip ? 1 : 0;
-  if (dtype == 0) {
-    auto s = static_cast<const float*>(src);
-    auto o = static_cast<float*>(dst);
-    if (vec_ok(4, D, part_w, src, dst))
-      split_rows_kernel<float, true><<<grid, kRowThreads, 0, stream>>>(s, o, rows, d.N, D, part_w, part_stride, f);
-    else
-      split_rows_kernel<float, false><<<grid, kRowThreads, 0, stream>>>(s, o, rows, d.N, D, part_w, part_stride, f);
-  } else {
-    auto s = static_cast<const uint16_t*>(src);
-    auto o = static_cast<uint16_t*>(dst);
-    if (vec_ok(2, D, part_w, src, dst))
-      split_rows_kernel<uint16_t, true><<<grid, kRowThreads, 0, stream>>>(s, o, rows, d.N, D, part_w, part_stride, f);
-    else
-      split_rows_kernel<uint16_t, false><<<grid, kRowThreads, 0, stream>>>(s, o, rows, d.N, D, part_w, part_stride,
-                                                                           f);
+  if (rows == 0 || ntargets == 0) return hipSuccess;
+  SplitDst<T> dst{};
+  bool vec = (D * sizeof(T)) % 16 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0;
+  for (int t = 0; t < ntargets; ++t) {
+    dst.base[t] = static_cast<T*>(targets[t].dst);
+    dst.part_w[t] = targets[t].part_w;
+    dst.part_stride[t] = targets[t].part_stride;
+    dst.flip[t] = targets[t].flip ? 1 : 0;
+    vec = vec && (targets[t].part_w * sizeof(T)) % 16 == 0 && reinterpret_cast<uintptr_t>(targets[t].dst) % 16 == 0;
   }
+  dst.count = ntargets;
+  const dim3 grid(static_cast<unsigned>((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  const T* s = static_cast<const T*>(src);
+  if (vec)
+    split_rows_kernel<T, true><<<grid, kRowThreads, 0, stream>>>(s, dst, rows, d.N, D);
+  else
+    split_rows_kernel<T, false><<<grid, kRowThreads, 0, stream>>>(s, dst, rows, d.N, D);
   return hipGetLastError();
+}
+
+hipError_t launch_split_rows(int dtype, const void* src, const SplitTarget* targets, int ntargets, const Dims& d,
+                             int D, hipStream_t stream) {
+  if (ntargets < 0 || ntargets > 3) return hipErrorInvalidValue;
+  return dtype == 0 ? split_typed<float>(src, targets, ntargets, d, D, stream)
+                    : split_typed<uint16_t>(src, targets, ntargets, d, D, stream);
 }
 
 hipError_t launch_sum_parts(int dtype, const void* parts, void* dst, const Dims& d, int W, int nparts,

@@ -66,11 +66,18 @@ hipError_t launch_mfma_chunk_out(const uint16_t* q, const uint16_t* k, const uin
 bool mfma_supports(int dk, int dv);
 
 // Backward-pass data movement (d.B, d.H, d.N are used; rows are tokens).
-// split_rows: src [B*H, N, D] -> parts of width part_w (the last may be
-// narrower), part p at dst + p * part_stride as [B*H, N, w_p], rows token-
-// reversed within each head when `flip`.
-hipError_t launch_split_rows(int dtype, const void* src, void* dst, const Dims& d, int D, int part_w,
-                             int64_t part_stride, bool flip, hipStream_t stream);
+// split_rows: src [B*H, N, D] read once, written to up to three targets, each
+// cut into parts of width part_w (the last may be narrower), part p at
+// dst + p * part_stride elements as [B*H, N, w_p], rows token-reversed within
+// each head when `flip`.
+struct SplitTarget {
+  void* dst;
+  int part_w;
+  int64_t part_stride;
+  bool flip;
+};
+hipError_t launch_split_rows(int dtype, const void* src, const SplitTarget* targets, int ntargets, const Dims& d,
+                             int D, hipStream_t stream);
 // sum_parts: dst [B*H, N, W] = sum of nparts buffers [B*H, N, W] (part_stride
 // elements apart), read token-reversed when `flip`; fp32 sums.
 hipError_t launch_sum_parts(int dtype, const void* parts, void* dst, const Dims& d, int W, int nparts,
