@@ -187,7 +187,8 @@ __global__ void __launch_bounds__(kThreads) mfma_state_walk_kernel(WalkArgs a, H
   TileRegs<VPIECES, kThreads, kWalkVT> rv;
   // zeta_t = gamma^(L-1-t) = gamma^(L-1-t0) * gamma^(-r) for row r of a tile at t0;
   // it scales whichever of the K and V tiles is smaller. The gamma^(-r) factors
-  // of this thread's rows are fixed (r <= 63, so <= 7.4).
+  // of this thread's rows are fixed (r <= 63: at most 2^63 for gamma > 1/2;
+  // smaller decays take one exp2 per row instead).
   constexpr bool kScaleK = KT < kWalkVT;
   constexpr int ZP = kScaleK ? PIECES : VPIECES;
   float zrow[ZP];
@@ -221,10 +222,21 @@ __global__ void __launch_bounds__(kThreads) mfma_state_walk_kernel(WalkArgs a, H
     }
     __syncthreads();
     {
-      const float z0 = gpow(lg, static_cast<float>(L - 1 - t0));
       float z[ZP];
+      if (lg > -1.0f) {
+        const float z0 = gpow(lg, static_cast<float>(L - 1 - t0));
 #pragma unroll
-      for (int m = 0; m < ZP; ++m) z[m] = z0 * zrow[m];
+        for (int m = 0; m < ZP; ++m) z[m] = z0 * zrow[m];
+      } else {
+        // gamma <= 1/2: gamma^(-r) may leave the float range; one exp2 per row
+        // (rows past the chunk end are zero and take exponent 0).
+#pragma unroll
+        for (int m = 0; m < ZP; ++m) {
+          const int row = kScaleK ? TileRegs<PIECES, kThreads, KT>::row_of(m)
+                                  : TileRegs<VPIECES, kThreads, kWalkVT>::row_of(m);
+          z[m] = gpow(lg, static_cast<float>(max(L - 1 - t0 - row, 0)));
+        }
+      }
       if constexpr (kScaleK) {
         rk.store_scaled(sK, kPitchWK, z);
         rv.store(sV, kWalkPitch);
@@ -371,7 +383,8 @@ __global__ void __launch_bounds__(kWalk2Threads) mfma_state_walk2_kernel(WalkArg
   TileRegs<KP, NT, DK> rk;
   TileRegs<VP, NT, VT> rv;
   // zeta_t = gamma^(L-1-t) = gamma^(L-1-t0) * gamma^(-r) for row r of a block
-  // at t0; the gamma^(-r) factors of this thread's V rows are fixed.
+  // at t0; the gamma^(-r) factors of this thread's V rows are fixed (at most
+  // 2^63 for gamma > 1/2; smaller decays take one exp2 per row instead).
   float zrow[VP];
 #pragma unroll
   for (int m = 0; m < VP; ++m) zrow[m] = gpow(lg, -static_cast<float>(TileRegs<VP, NT, VT>::row_of(m)));
@@ -405,10 +418,18 @@ __global__ void __launch_bounds__(kWalk2Threads) mfma_state_walk2_kernel(WalkArg
   };
   auto put = [&](int c, int t0, int b) {
     const int L = min(a.chunk, a.N - c * a.chunk);
-    const float z0 = gpow(lg, static_cast<float>(L - 1 - t0));
     float z[VP];
+    if (lg > -1.0f) {
+      const float z0 = gpow(lg, static_cast<float>(L - 1 - t0));
 #pragma unroll
-    for (int m = 0; m < VP; ++m) z[m] = z0 * zrow[m];
+      for (int m = 0; m < VP; ++m) z[m] = z0 * zrow[m];
+    } else {
+      // gamma <= 1/2: gamma^(-r) may leave the float range; one exp2 per row
+      // (rows past the chunk end are zero and take exponent 0).
+#pragma unroll
+      for (int m = 0; m < VP; ++m)
+        z[m] = gpow(lg, static_cast<float>(max(L - 1 - t0 - TileRegs<VP, NT, VT>::row_of(m), 0)));
+    }
     rk.store(sK[b], PK);
     // V rows scaled by zeta into their swizzled places.
 #pragma unroll

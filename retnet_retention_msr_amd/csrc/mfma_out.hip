@@ -363,7 +363,11 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
 #pragma unroll
         for (int s = 0; s < 8; ++s) kfr[j][s] = ld8(kt + kread[j][s & 3] + 128 * (s >> 2));
     };
-    // Decay, mask and store the scores of key block kb (S^T tiles in sacc).
+    // Decay, mask and store the scores of key block kb (S^T tiles in sacc):
+    // the block factor times the lane factor, or, for heads with gamma <= 1/2
+    // (never on the 1 - 2^(-5-h) schedule), one exp2 per score, since the lane
+    // factor (down to gamma^-35) would leave the float range.
+    const bool split_decay = cur.lg > -1.0f;
     auto score_out = [&](int kb, const floatx4 (&sacc)[SW], uint16_t* pdst) __attribute__((always_inline)) {
       const int dq = cur.q0 - (cur.cs + kb * kTile);
       const float fblock = gpow(cur.lg, static_cast<float>(dq));
@@ -375,8 +379,14 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
         const int ql = qt * 16 + l16;
         const int tl = tt * 16 + 4 * (lane >> 4);
         float x[4];
+        if (split_decay) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = ql - tl - r >= -dq ? sacc[j][r] * (fblock * flane[j][r]) : 0.f;
+          for (int r = 0; r < 4; ++r) x[r] = ql - tl - r >= -dq ? sacc[j][r] * (fblock * flane[j][r]) : 0.f;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            x[r] = ql - tl - r >= -dq ? sacc[j][r] * gpow(cur.lg, static_cast<float>(dq + ql - tl - r)) : 0.f;
+        }
         uint2 w;
         w.x = pack_bf16x2(x[0], x[1]);
         w.y = pack_bf16x2(x[2], x[3]);

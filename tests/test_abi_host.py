@@ -177,3 +177,34 @@ def test_gate_needs_groupnorm():
 
     with pytest.raises(ValueError, match="needs the GroupNorm"):
         ret._gn_struct(None, 2, 128, None, gate=object())
+
+
+def _backward(lib, gq=FAKE, ws=FAKE, ws_bytes=1 << 40, chunk=64, gamma=None, B=1, H=2, N=256, dk=64, dv=128,
+              dtype=1):
+    g = _gamma(gamma or [0.9] * H)
+    return lib.retention_chunkwise_backward(FAKE, FAKE, FAKE, FAKE, g, gq, FAKE, FAKE, B, H, N, dk, dv, chunk, dtype,
+                                            None, None, None, ws, ws_bytes, None)
+
+
+def test_backward_rejects_invalid_arguments(lib):
+    need = lib.retention_chunkwise_backward_workspace_bytes(1, 2, 256, 64, 128, 64, 1)
+    assert need > 0
+    assert _backward(lib, gq=None) == -1
+    assert _backward(lib, ws=None) == -1
+    assert _backward(lib, ws_bytes=need - 1) == -1
+    assert _backward(lib, chunk=0) == -1
+    assert _backward(lib, gamma=[0.9, 1.0]) == -1
+    assert _backward(lib, N=0) == -1
+    assert _backward(lib, dtype=2) == -1
+    assert _backward(lib, H=257, gamma=[0.9] * 257) == -2
+
+
+def test_backward_workspace_bytes(lib):
+    ws = lib.retention_chunkwise_backward_workspace_bytes
+    # It holds at least the reversed Q, K, dO and V copies and the forward-size chunk workspace.
+    B, H, N, dk, dv = 8, 16, 8192, 256, 512
+    tok = B * H * N
+    assert ws(B, H, N, dk, dv, 512, 1) >= (2 * tok * dk + 2 * tok * dv) * 2 + \
+        lib.retention_chunkwise_workspace_bytes(B, H, N, dk, dv, 512, 1)
+    assert ws(0, H, N, dk, dv, 512, 1) == 0
+    assert ws(B, H, N, dk, dv, 0, 1) == 0

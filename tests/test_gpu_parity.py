@@ -444,3 +444,58 @@ def test_chunkwise_backward_matches_oracle(B, H, N, dk, dv, C, dtype, with_state
     _check(gk, ref[1], tol, "grad_k")
     _check(gv, ref[2], tol, "grad_v")
     _check(gs, ref[3], tol, "grad_state_in")
+
+
+# ---------------------------------------------------------------------------
+# Edge cases: a single token, a chunk longer than the sequence, the largest
+# head count and value width the ABI takes, decays near 0 and near 1
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("N,C", [(1, 64), (5, 64), (63, 512)])
+def test_short_sequences(dtype, N, C):
+    _announce(f"short sequence N={N} C={C} {dtype}")
+    B, H, dk, dv = 2, 2, 64, 128
+    q, k, v, g, S0 = _inputs(B, H, N, dk, dv, dtype, seed=300 + N, with_state=True)
+    ref, Sref = orc.chunkwise(q, k, v, g, C, state_in=S0)
+    qd, kd, vd, S0d = _dev(q, k, v, S0)
+    o, S = ret.chunkwise(qd, kd, vd, g, C, state_in=S0d, state_out=True)
+    _check(o, ref, TOL[dtype], "o")
+    _check(S, Sref, TOL[dtype], "state")
+    _check(ret.parallel(qd, kd, vd, g), orc.parallel(q, k, v, g), TOL[dtype], "parallel")
+    gq, gk, gv, gs = ret.chunkwise_backward(qd, kd, vd, vd, g, C, state_in=S0d, grad_state_in=True)
+    bref = orc.backward(q, k, v, g, v, state_in=S0)
+    for name, got, r in zip(("dq", "dk", "dv", "ds0"), (gq, gk, gv, gs), bref):
+        _check(got, r, TOL[dtype], name)
+
+
+def test_max_heads_and_wide_values():
+    """256 heads (the ABI maximum; the decays are spread over [0.05, 0.999],
+    since the 1 - 2^(-5-h) schedule rounds to 1 in fp32 from h = 19 on) and
+    dv = 1024 (the widest value row, on the generic path)."""
+    _announce("H=256 and dv=1024")
+    B, H, N, dk, dv, C = 1, 256, 70, 32, 128, 64
+    q, k, v, _, S0 = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=400, with_state=True)
+    g = torch.linspace(0.05, 0.999, H)
+    ref = orc.chunkwise(q, k, v, g, C, state_in=S0)[0]
+    qd, kd, vd, S0d = _dev(q, k, v, S0)
+    _check(ret.chunkwise(qd, kd, vd, g, C, state_in=S0d)[0], ref, 2e-2, "H=256")
+    B, H, N, dk, dv = 1, 2, 90, 64, 1024
+    q, k, v, g, _ = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=401)
+    qd, kd, vd = _dev(q, k, v)
+    gn = ret.GroupNorm(1e-5)
+    _check(ret.chunkwise(qd, kd, vd, g, 32, gn=gn)[0], orc.group_norm(orc.chunkwise(q, k, v, g, 32)[0]), 2e-2,
+           "dv=1024")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_extreme_decays(dtype):
+    """gamma near 0 (each token sees almost only itself) and near 1 (almost no decay)."""
+    _announce(f"extreme decays {dtype}")
+    B, H, N, dk, dv, C = 1, 2, 300, 64, 128, 64
+    q, k, v, _, S0 = _inputs(B, H, N, dk, dv, dtype, seed=500, with_state=True)
+    g = torch.tensor([1e-6, 1.0 - 2.0 ** -20])
+    ref, Sref = orc.chunkwise(q, k, v, g, C, state_in=S0)
+    qd, kd, vd, S0d = _dev(q, k, v, S0)
+    o, S = ret.chunkwise(qd, kd, vd, g, C, state_in=S0d, state_out=True)
+    _check(o, ref, TOL[dtype], "o")
+    _check(S, Sref, TOL[dtype], "state")
