@@ -323,6 +323,28 @@ def test_decode_steps_match_oracle(dtype, gn_on, dv):
     _check(Sd, Sref, 1e-5, "state")
 
 
+@pytest.mark.parametrize("dk", [128, 256])
+@pytest.mark.parametrize("gn_on", [False, True])
+def test_decode_batched_rows(dk, gn_on):
+    """dk = 128 and 256 take the path that loads all of a thread's state rows first."""
+    _announce(f"decode dk={dk} gn={gn_on}")
+    B, H, dv, steps = 2, 3, 192, 3
+    q, k, v = synthetic.make_qkv(B, H, steps, dk, dv, dtype=torch.bfloat16, seed=41, qk_var=1.0)
+    g = synthetic.head_gammas(H)
+    S = synthetic.make_state(B, H, dk, dv, seed=42)
+    Sd = S.to(DEV)
+    qd, kd, vd = _dev(q, k, v)
+    Sref = S.double().numpy()
+    for n in range(steps):
+        o_ref, Sref = orc.recurrent_step(q[:, :, n], k[:, :, n], v[:, :, n], g, Sref)
+        if gn_on:
+            o_ref = orc.group_norm(o_ref[:, :, None, :], 1e-5)[:, :, 0]
+        o = ret.recurrent_step(qd[:, :, n].contiguous(), kd[:, :, n].contiguous(), vd[:, :, n].contiguous(), g, Sd,
+                               gn=ret.GroupNorm(1e-5) if gn_on else None)
+        _check(o, o_ref, 2e-2, f"o step {n}")
+    _check(Sd, Sref, 1e-5, "state")
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("dv", [128, 100])
 def test_decode_gated_groupnorm(dtype, dv):
