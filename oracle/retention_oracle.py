@@ -18,7 +18,7 @@ Sources (the pages this follows; cited by tag below):
         Retention (MSR) (the normalised head outputs multiplied elementwise by
         a gated branch).
 
-Conventions (readings where the pages are silent, all listed in the design doc):
+Conventions (readings where the pages are silent):
   * positions n, m and the head index h are 0-based;
   * shapes: q, k are [B, H, N, dk]; v is [B, H, N, dv]; a state is
     [B, H, dk, dv]; gamma is [H];
@@ -164,7 +164,7 @@ def chunkwise(q, k, v, gamma, chunk, state_in=None):
     with xi_j = gamma^(j+1), zeta_j = gamma^(L-1-j), R_{-1} = state_in (or 0).
     The carry printed on the page lacks the in-chunk factor zeta; taken
     literally it would break the equality with the recurrence that the same
-    page asserts, so zeta is included (reading recorded in the design doc).
+    page asserts, so zeta is included.
     Returns (o [B, H, N, dv], R_last).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
