@@ -133,14 +133,14 @@ hipError_t launch_states(const ChunkPlan& p, const void* k, const void* v, const
 
 hipError_t launch_output(const ChunkPlan& p, const void* q, const void* k, const void* v, void* o, const char* ws,
                          bool state0, const Dims& d, int chunk, int dtype, const HeadDecay& decay, const GnArgs& g,
-                         hipStream_t s) {
+                         hipStream_t s, bool accumulate = false) {
   if (p.mfma) {
     return ret::launch_mfma_chunk_out(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                       static_cast<const uint16_t*>(v), reinterpret_cast<const uint16_t*>(ws), state0,
-                                      static_cast<uint16_t*>(o), d, chunk, decay, g, s);
+                                      static_cast<uint16_t*>(o), d, chunk, decay, g, accumulate, s);
   }
   return ret::launch_generic_chunk_out(dtype, q, k, v, reinterpret_cast<const float*>(ws), state0, o, d, chunk,
-                                       decay, g, s);
+                                       decay, g, accumulate, s);
 }
 
 // Backward plan: operand copies, partial results, state transforms and the
@@ -150,7 +150,7 @@ constexpr int kPartWidth = 256;  // widest query/key dimension the MFMA kernels 
 struct BackwardPlan {
   int nparts;  // parts of the dv-wide query/key dimension of the dQ and dK retentions
   int part_w;
-  size_t qf, kf, dof, oa, dos, vs, dofs, vfs, qpart, kpart;  // byte offsets (token-row buffers)
+  size_t qf, kf, dof, oa, dos, vs, dofs, vfs, kpart;  // byte offsets (token-row buffers)
   size_t s_a, s_t, s_0t, s_nt;                               // fp32 state buffers
   size_t cw;                                                 // chunkwise workspace
   size_t cw_bytes;
@@ -179,8 +179,7 @@ BackwardPlan plan_backward(int B, int H, int N, int dk, int dv, int chunk, int d
   p.vs = split ? take(tok * dv * es) : 0;
   p.dofs = split ? take(tok * dv * es) : 0;
   p.vfs = take(tok * dv * es);
-  p.qpart = split ? take(static_cast<size_t>(p.nparts) * tok * dk * es) : 0;
-  p.kpart = take(static_cast<size_t>(p.nparts) * tok * dk * es);
+  p.kpart = take(tok * dk * es);
   p.s_a = take(st);
   p.s_t = take(st);
   p.s_0t = take(st);
@@ -198,11 +197,12 @@ BackwardPlan plan_backward(int B, int H, int N, int dk, int dv, int chunk, int d
 
 // One retention (both chunkwise stages) for the backward pass: no GroupNorm.
 int run_retention(const void* q, const void* k, const void* v, void* o, const float* state_in, float* state_out,
-                  const Dims& d, int chunk, int dtype, const HeadDecay& decay, char* cw, hipStream_t s) {
+                  const Dims& d, int chunk, int dtype, const HeadDecay& decay, char* cw, hipStream_t s,
+                  bool accumulate = false) {
   const ChunkPlan p = plan_chunkwise(d.B, d.H, d.N, d.dk, d.dv, chunk, dtype);
   GnArgs none{};
   if (launch_states(p, k, v, state_in, state_out, cw, d, chunk, dtype, decay, s) != hipSuccess) return RET_ERR_HIP;
-  return status_of(launch_output(p, q, k, v, o, cw, state_in != nullptr, d, chunk, dtype, decay, none, s));
+  return status_of(launch_output(p, q, k, v, o, cw, state_in != nullptr, d, chunk, dtype, decay, none, s, accumulate));
 }
 
 }  // namespace
@@ -239,9 +239,9 @@ int retention_parallel(const void* q, const void* k, const void* v, const float*
   if (dtype == RET_BF16 && ret::mfma_supports(dk, dv)) {
     return status_of(ret::launch_mfma_chunk_out(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                                 static_cast<const uint16_t*>(v), nullptr, false,
-                                                static_cast<uint16_t*>(o), d, N, decay, g, s));
+                                                static_cast<uint16_t*>(o), d, N, decay, g, false, s));
   }
-  return status_of(ret::launch_generic_chunk_out(dtype, q, k, v, nullptr, false, o, d, N, decay, g, s));
+  return status_of(ret::launch_generic_chunk_out(dtype, q, k, v, nullptr, false, o, d, N, decay, g, false, s));
 }
 
 size_t retention_chunkwise_workspace_bytes(int B, int H, int N, int dk, int dv, int chunk, int dtype) {
@@ -407,24 +407,21 @@ int retention_chunkwise_backward(const void* q, const void* k, const void* v, co
   auto part = [&](const void* base, int i) {
     return static_cast<const void*>(static_cast<const char*>(base) + static_cast<size_t>(i) * part_rows * es);
   };
-  const int64_t out_part = tok * dk;  // elements between partial results
+  // The parts' results are summed in place: the first part writes, the later
+  // ones add (in fp32, before rounding) to what is there.
   for (int i = 0; i < P; ++i) {
     const int w = std::min(pw, dv - i * pw);
     const Dims dd{B, H, N, w, dk};
     // dQ part: query dO, key V, value K, starting state S0^T (rows of the part).
-    void* oq = P > 1 ? static_cast<void*>(ws + p.qpart + static_cast<size_t>(i) * out_part * es) : grad_q;
-    st = run_retention(part(dos, i), part(vs, i), k, oq, s_0t ? s_0t + i * st_part : nullptr, nullptr, dd, chunk,
-                       dtype, decay, cw, s);
+    st = run_retention(part(dos, i), part(vs, i), k, grad_q, s_0t ? s_0t + i * st_part : nullptr, nullptr, dd, chunk,
+                       dtype, decay, cw, s, i > 0);
     if (st != RET_OK) return st;
     // dK part (reversed time): query V, key dO, value Q, starting state dS_N^T / gamma.
-    void* ok_ = static_cast<void*>(ws + p.kpart + static_cast<size_t>(i) * out_part * es);
-    st = run_retention(part(at(p.vfs), i), part(dofs, i), at(p.qf), ok_, s_nt ? s_nt + i * st_part : nullptr,
-                       nullptr, dd, chunk, dtype, decay, cw, s);
+    st = run_retention(part(at(p.vfs), i), part(dofs, i), at(p.qf), at(p.kpart), s_nt ? s_nt + i * st_part : nullptr,
+                       nullptr, dd, chunk, dtype, decay, cw, s, i > 0);
     if (st != RET_OK) return st;
   }
-  if (P > 1 && !ok(ret::launch_sum_parts(dtype, at(p.qpart), grad_q, rows, dk, P, out_part, false, s)))
-    return RET_ERR_HIP;
-  return status_of(ret::launch_sum_parts(dtype, at(p.kpart), grad_k, rows, dk, P, out_part, true, s));
+  return status_of(ret::launch_sum_parts(dtype, at(p.kpart), grad_k, rows, dk, 1, 0, true, s));
 }
 
 }  // extern "C"

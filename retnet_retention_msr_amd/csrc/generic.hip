@@ -119,7 +119,8 @@ template <typename T>
 __global__ void __launch_bounds__(kThreads)
 generic_chunk_out_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                          const float* __restrict__ chunk_states, int state_for_chunk0, T* __restrict__ o, int H,
-                         int N, int dk, int dv, int chunk, int nchunks, HeadDecay decay, GnArgs gn) {
+                         int N, int dk, int dv, int chunk, int nchunks, HeadDecay decay, GnArgs gn,
+                         int accumulate) {
   __shared__ float s_q[256];
   __shared__ float s_w[kThreads];
   __shared__ float s_red[4];
@@ -211,7 +212,10 @@ generic_chunk_out_kernel(const T* __restrict__ q, const T* __restrict__ k, const
 #pragma unroll
   for (int j = 0; j < kOutColsPerThread; ++j) {
     const int col = tid + kThreads * j;
-    if (col < dv) Elem<T>::store(o, (bh * N + n) * dv + col, acc[j]);
+    if (col < dv) {
+      const int64_t at = (bh * N + n) * dv + col;
+      Elem<T>::store(o, at, accumulate ? acc[j] + Elem<T>::load(o, at) : acc[j]);
+    }
   }
 }
 
@@ -236,18 +240,20 @@ hipError_t launch_generic_state_walk(int dtype, const void* k, const void* v, co
 
 hipError_t launch_generic_chunk_out(int dtype, const void* q, const void* k, const void* v,
                                     const float* chunk_states, bool state_for_chunk0, void* o, const Dims& d,
-                                    int chunk, const HeadDecay& decay, const GnArgs& gn, hipStream_t stream) {
+                                    int chunk, const HeadDecay& decay, const GnArgs& gn, bool accumulate,
+                                    hipStream_t stream) {
   const int nchunks = (d.N + chunk - 1) / chunk;
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(d.B) * d.H * d.N));
+  const int acc = accumulate ? 1 : 0;
   if (dtype == 0) {
     generic_chunk_out_kernel<float><<<grid, kThreads, 0, stream>>>(
         static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), chunk_states,
-        state_for_chunk0 ? 1 : 0, static_cast<float*>(o), d.H, d.N, d.dk, d.dv, chunk, nchunks, decay, gn);
+        state_for_chunk0 ? 1 : 0, static_cast<float*>(o), d.H, d.N, d.dk, d.dv, chunk, nchunks, decay, gn, acc);
   } else {
     generic_chunk_out_kernel<uint16_t><<<grid, kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
         chunk_states, state_for_chunk0 ? 1 : 0, static_cast<uint16_t*>(o), d.H, d.N, d.dk, d.dv, chunk, nchunks,
-        decay, gn);
+        decay, gn, acc);
   }
   return hipGetLastError();
 }

@@ -31,10 +31,12 @@ hipError_t launch_generic_state_walk(int dtype, const void* k, const void* v, co
 // Generic (VALU) output rows: intra-chunk causal part plus, when chunk_states
 // is non-null, the cross-chunk read-out of the state before the row's chunk.
 // With chunk >= N and no states this is the parallel form.
+// `accumulate`: add the values already in o (partial results summed over
+// launches) instead of overwriting them.
 hipError_t launch_generic_chunk_out(int dtype, const void* q, const void* k, const void* v,
                                     const float* chunk_states, bool state_for_chunk0, void* o,
                                     const Dims& d, int chunk, const HeadDecay& decay, const GnArgs& gn,
-                                    hipStream_t stream);
+                                    bool accumulate, hipStream_t stream);
 
 // bf16 MFMA chunk-state walk: writes the bf16 state before every chunk in a
 // [B*H][nchunks][dv][dk] (dk fastest) layout, and the fp32 final state.
@@ -60,7 +62,7 @@ int walk_tiles_per_head(int64_t heads, int dk, int dv);
 hipError_t launch_mfma_chunk_out(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const uint16_t* chunk_states, bool state_for_chunk0, uint16_t* o,
                                  const Dims& d, int chunk, const HeadDecay& decay, const GnArgs& gn,
-                                 hipStream_t stream);
+                                 bool accumulate, hipStream_t stream);
 
 // Whether the MFMA kernels implement these sizes.
 bool mfma_supports(int dk, int dv);

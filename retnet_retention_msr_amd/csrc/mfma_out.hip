@@ -94,9 +94,11 @@ __device__ __forceinline__ void wait_vm_keep() {
 // first copies and Q rows are requested before the current block's GroupNorm
 // and store, which use no buffer those copies write.
 //
-// GATE: the GroupNorm is on and its output is multiplied by swish(gate) (a
-// separate instance, so the gate's registers do not weigh on the plain one).
-template <int NVT, int WAVES, bool GATE>
+// EPI (a separate instance each, so the extra registers do not weigh on the
+// plain one): 0 stores the result; 1 multiplies it (after the GroupNorm) by
+// swish(gate); 2 adds the bf16 values already in O (partial results of one
+// product accumulated over several launches, in fp32 before rounding).
+template <int NVT, int WAVES, int EPI>
 __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, HeadDecay decay, GnArgs gn) {
   constexpr int DV = WAVES * 32 * NVT;
   constexpr int SW = 8 / WAVES;                    // 16 x 16 score tiles per wave (8 per key block)
@@ -537,14 +539,16 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
         bb[nt] = gn.bias ? gn.bias[cur.h * DV + vcol] : 0.f;
       }
     }
-    // Gate values (bf16 pairs) at exactly the positions this lane stores,
-    // also requested before the next block's copies. Rows past the block's
-    // last valid row read as zero through the descriptors' ranges.
-    constexpr bool gated = GATE;
+    // Gate values, or the values already in O, as bf16 pairs at exactly the
+    // positions this lane stores, also requested before the next block's
+    // copies. Rows past the block's last valid row read as zero through the
+    // descriptors' ranges.
+    constexpr bool gated = EPI != 0;
     const int voff = ((4 * (lane >> 5) + (lane & 1)) * DV + vcol0 + (l32 & ~1)) * 2;
     uint32_t gv[2][4][NVT][2];
     if constexpr (gated) {
-      const uint16_t* gblk = static_cast<const uint16_t*>(gn.gate) + (cur.bh * a.N + cur.q0) * static_cast<int64_t>(DV);
+      const uint16_t* gbase = EPI == 1 ? static_cast<const uint16_t*>(gn.gate) : a.o;
+      const uint16_t* gblk = gbase + (cur.bh * a.N + cur.q0) * static_cast<int64_t>(DV);
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
@@ -642,8 +646,8 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
       // v_perm byte selectors over {neighbour (bytes 4-7), own (bytes 0-3)}:
       // even lanes take both low halves, odd lanes both high halves.
       const unsigned sel = odd ? 0x03020706u : 0x05040100u;
-      auto store_rows = [&](auto gate_tag) __attribute__((always_inline)) {
-        constexpr bool kGate = decltype(gate_tag)::value;
+      auto store_rows = [&](auto epi_tag) __attribute__((always_inline)) {
+        constexpr int kEpi = decltype(epi_tag)::value;
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
@@ -657,7 +661,7 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
                 // accumulators 4g + 2hp (row row0 + 4*(lane/32) + 2hp) and the next row
                 const int rr = 4 * g + 2 * hp;
                 unsigned packed;
-                if constexpr (kGate) {
+                if constexpr (kEpi != 0) {
                   // the even lane sends its row rho+1 value, the odd lane its row rho value
                   const float a0 = acc[qt][nt][rr], a1 = acc[qt][nt][rr + 1];
                   const float send = odd ? a0 : a1;
@@ -665,8 +669,12 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
                       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xf, 0xf, true));
                   const float lo = odd ? recv : a0, hi = odd ? a1 : recv;
                   const uint32_t gp = gv[qt][g][nt][hp];
-                  packed = pack_bf16x2(lo * swish(__uint_as_float(gp << 16)),
-                                       hi * swish(__uint_as_float(gp & 0xffff0000u)));
+                  const float g_lo = __uint_as_float(gp << 16), g_hi = __uint_as_float(gp & 0xffff0000u);
+                  if constexpr (kEpi == 1) {
+                    packed = pack_bf16x2(lo * swish(g_lo), hi * swish(g_hi));
+                  } else {
+                    packed = pack_bf16x2(lo + g_lo, hi + g_hi);
+                  }
                 } else {
                   const unsigned own = pack_bf16x2(acc[qt][nt][rr], acc[qt][nt][rr + 1]);
                   const unsigned nbr = __builtin_amdgcn_update_dpp(0u, own, 0xB1, 0xf, 0xf, true);  // quad_perm [1,0,3,2]
@@ -676,7 +684,7 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_chunk_out_kernel(OutArgs a, H
               }
           }
       };
-      store_rows(std::integral_constant<bool, gated>{});
+      store_rows(std::integral_constant<int, EPI>{});
     }
 
     if (Ln < 0) break;
@@ -715,7 +723,8 @@ hipError_t resident_workgroups(const void* kernel, int threads, int which, int* 
 
 hipError_t launch_mfma_chunk_out(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const uint16_t* chunk_states, bool state_for_chunk0, uint16_t* o, const Dims& d,
-                                 int chunk, const HeadDecay& decay, const GnArgs& gn, hipStream_t stream) {
+                                 int chunk, const HeadDecay& decay, const GnArgs& gn, bool accumulate,
+                                 hipStream_t stream) {
   OutArgs a;
   a.q = q;
   a.k = k;
@@ -743,14 +752,20 @@ hipError_t launch_mfma_chunk_out(const uint16_t* q, const uint16_t* k, const uin
     kernel<<<grid, threads, 0, stream>>>(a, decay, gn);
     return hipGetLastError();
   };
-  const bool gated = gn.enabled && gn.gate;
+  const int epi = (gn.enabled && gn.gate) ? 1 : (accumulate ? 2 : 0);
   switch (d.dv) {
     case 128:
-      return gated ? launch(mfma_chunk_out_kernel<1, 4, true>, 256, 3) : launch(mfma_chunk_out_kernel<1, 4, false>, 256, 0);
+      return epi == 1   ? launch(mfma_chunk_out_kernel<1, 4, 1>, 256, 3)
+             : epi == 2 ? launch(mfma_chunk_out_kernel<1, 4, 2>, 256, 6)
+                        : launch(mfma_chunk_out_kernel<1, 4, 0>, 256, 0);
     case 256:
-      return gated ? launch(mfma_chunk_out_kernel<1, 8, true>, 512, 4) : launch(mfma_chunk_out_kernel<1, 8, false>, 512, 1);
+      return epi == 1   ? launch(mfma_chunk_out_kernel<1, 8, 1>, 512, 4)
+             : epi == 2 ? launch(mfma_chunk_out_kernel<1, 8, 2>, 512, 7)
+                        : launch(mfma_chunk_out_kernel<1, 8, 0>, 512, 1);
     default:
-      return gated ? launch(mfma_chunk_out_kernel<2, 8, true>, 512, 5) : launch(mfma_chunk_out_kernel<2, 8, false>, 512, 2);
+      return epi == 1   ? launch(mfma_chunk_out_kernel<2, 8, 1>, 512, 5)
+             : epi == 2 ? launch(mfma_chunk_out_kernel<2, 8, 2>, 512, 8)
+                        : launch(mfma_chunk_out_kernel<2, 8, 0>, 512, 2);
   }
 }
 

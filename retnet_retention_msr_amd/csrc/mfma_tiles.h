@@ -173,7 +173,7 @@ struct OutArgs {
 // Workgroups of `kernel` (launched with `threads` threads) resident on the
 // current device at once: CUs times workgroups per CU, cached per device and
 // kernel slot `which` (0 .. kResidentSlots-1).
-constexpr int kResidentSlots = 8;
+constexpr int kResidentSlots = 12;
 hipError_t resident_workgroups(const void* kernel, int threads, int which, int* out);
 
 }  // namespace ret
