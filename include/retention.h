@@ -44,8 +44,11 @@
  *     "validated and launched"; a fault inside a kernel surfaces on the next
  *     synchronising HIP call of the caller.
  *   - Ownership: the caller owns every buffer. The library allocates no
- *     device memory and keeps no mutable global state; calls on different
- *     streams do not interfere except through buffers the caller shares.
+ *     device memory. Its only mutable global state is a per-device cache of
+ *     occupancy figures (how many workgroups of a kernel fit the GPU at
+ *     once), filled on first use through atomic stores and never changed
+ *     afterwards; calls on different streams do not interfere except through
+ *     buffers the caller shares.
  *   - O must not alias Q, K or V. No entry point throws; all report status.
  *
  * Status codes:
@@ -55,7 +58,8 @@
  *   what the kernels implement (for example H > RETENTION_MAX_HEADS or dk
  *   above RETENTION_MAX_DK); RET_ERR_HIP (-3): the HIP runtime reported an
  *   error for a launch. Invalid or unsupported arguments are detected before
- *   any HIP call is made.
+ *   any HIP call is made. A chunk length at or above N means one chunk (all
+ *   such lengths give the same result).
  */
 #ifndef RETENTION_H
 #define RETENTION_H
@@ -194,7 +198,10 @@ int retention_recurrent_step(const void* q, const void* k, const void* v,
  * of the forward call. Each gradient is evaluated as a retention of its own
  * (grad_q forward in time; grad_k and grad_v over the token-reversed sequence)
  * with the chunkwise kernels at the given chunk; a width above 256 is split
- * into parts whose results are summed. workspace must hold
+ * into parts whose results are summed. With grad_state_out given, every
+ * gamma must be a normal float (>= FLT_MIN, about 1.2e-38): the final-state
+ * gradient is divided by gamma on its way in, and RET_ERR_UNSUPPORTED is
+ * returned otherwise. workspace must hold
  * retention_chunkwise_backward_workspace_bytes(...) bytes (contents on entry
  * do not matter and are clobbered). Same status codes as the other entry
  * points.

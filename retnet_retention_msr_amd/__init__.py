@@ -98,18 +98,78 @@ def _gn_struct(gn: Optional[GroupNorm], H: int, dv: int, device, gate=None, like
     return ctypes.byref(s), (s, keep)
 
 
+def _require(t, name, shape, dtype, device):
+    """Raise ValueError unless ``t`` is a contiguous tensor of exactly this shape
+    and dtype on ``device``. Every pointer handed to the C ABI passes through
+    here (or _check_qkv) first: the library cannot tell a host pointer or a
+    short buffer from a valid one."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device} (the inputs' device), not {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, not {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _require_workspace(ws, name, nbytes, device):
+    """A device byte buffer of at least ``nbytes`` bytes (contiguous)."""
+    if not isinstance(ws, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if ws.device != device:
+        raise ValueError(f"{name} must be on {device} (the inputs' device), not {ws.device}")
+    if not ws.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    have = ws.numel() * ws.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes, {nbytes} are needed")
+    return ws
+
+
+def _no_overlap(out, name, *inputs):
+    """``out`` must not share memory with any of ``inputs``."""
+    lo = out.data_ptr()
+    hi = lo + out.numel() * out.element_size()
+    for t in inputs:
+        if t is None:
+            continue
+        a = t.data_ptr()
+        b = a + t.numel() * t.element_size()
+        if lo < b and a < hi:
+            raise ValueError(f"{name} must not overlap an input")
+
+
 def _check_qkv(q, k, v):
     for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a tensor")
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share a dtype")
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError("expected q, k [B,H,N,dk] and v [B,H,N,dv]")
     B, H, N, dk = q.shape
     return B, H, N, dk, v.shape[3], _dtype_code(q)
+
+
+def _output(out, q, shape):
+    """The output tensor: allocated like q when None, else checked and kept apart from the inputs."""
+    if out is None:
+        return torch.empty(shape, dtype=q.dtype, device=q.device)
+    return _require(out, "out", shape, q.dtype, q.device)
+
+
+def _state(t, name, B, H, dk, dv, device):
+    return None if t is None else _require(t, name, (B, H, dk, dv), torch.float32, device)
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -122,12 +182,12 @@ def parallel(q, k, v, gamma: GammaLike, gn: Optional[GroupNorm] = None, out=None
     ``gate`` (optional, needs ``gn``): a tensor like the output; the result
     becomes GroupNorm(O) * swish(gate).
     """
-    lib = _lib.load()
     B, H, N, dk, dv, dt = _check_qkv(q, k, v)
-    if out is None:
-        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    out = _output(out, q, (B, H, N, dv))
+    _no_overlap(out, "out", q, k, v)
     g = _gamma_array(gamma, H)
     gn_p, _keep = _gn_struct(gn, H, dv, q.device, gate, out)
+    lib = _lib.load()
     rc = lib.retention_parallel(q.data_ptr(), k.data_ptr(), v.data_ptr(), g, out.data_ptr(), B, H, N, dk, dv, dt,
                                 gn_p, _stream(q))
     if rc != 0:
@@ -149,21 +209,22 @@ def chunkwise(q, k, v, gamma: GammaLike, chunk: int, state_in=None, state_out: U
     (optional, needs ``gn``): a tensor like the output; the result becomes
     GroupNorm(O) * swish(gate).
     """
-    lib = _lib.load()
     B, H, N, dk, dv, dt = _check_qkv(q, k, v)
-    if out is None:
-        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
-    for name, s in (("state_in", state_in), ("state_out", state_out)):
-        if isinstance(s, torch.Tensor):
-            if s.dtype != torch.float32 or not s.is_contiguous() or tuple(s.shape) != (B, H, dk, dv):
-                raise ValueError(f"{name} must be contiguous float32 [B,H,dk,dv]")
+    out = _output(out, q, (B, H, N, dv))
+    _no_overlap(out, "out", q, k, v)
+    state_in = _state(state_in, "state_in", B, H, dk, dv, q.device)
     if state_out is True:
         state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
-    elif state_out is False:
+    elif state_out is False or state_out is None:
         state_out = None
+    else:
+        _state(state_out, "state_out", B, H, dk, dv, q.device)
+    lib = _lib.load()
     nbytes = int(lib.retention_chunkwise_workspace_bytes(B, H, N, dk, dv, int(chunk), dt))
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    elif workspace is not None:
+        _require_workspace(workspace, "workspace", nbytes, q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     g = _gamma_array(gamma, H)
@@ -184,11 +245,12 @@ def chunk_states(k, v, gamma: GammaLike, chunk: int, workspace, state_in=None, s
     ``workspace`` is a device uint8 tensor of at least chunkwise_workspace_bytes(...)
     bytes; ``state_out`` (optional fp32 [B,H,dk,dv]) receives the final state.
     """
-    lib = _lib.load()
     B, H, N, dk, dv, dt = _check_qkv(k, k, v)
-    for name, t in (("state_in", state_in), ("state_out", state_out)):
-        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (B, H, dk, dv)):
-            raise ValueError(f"{name} must be contiguous float32 [B,H,dk,dv]")
+    state_in = _state(state_in, "state_in", B, H, dk, dv, k.device)
+    state_out = _state(state_out, "state_out", B, H, dk, dv, k.device)
+    lib = _lib.load()
+    _require_workspace(workspace, "workspace",
+                       int(lib.retention_chunkwise_workspace_bytes(B, H, N, dk, dv, int(chunk), dt)), k.device)
     g = _gamma_array(gamma, H)
     rc = lib.retention_chunk_states(
         k.data_ptr(), v.data_ptr(), g, B, H, N, dk, dv, int(chunk), dt,
@@ -206,10 +268,12 @@ def chunk_output(q, k, v, gamma: GammaLike, chunk: int, workspace, has_state_in:
 
     ``gate`` as in ``chunkwise``.
     """
-    lib = _lib.load()
     B, H, N, dk, dv, dt = _check_qkv(q, k, v)
-    if out is None:
-        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    out = _output(out, q, (B, H, N, dv))
+    _no_overlap(out, "out", q, k, v, workspace)
+    lib = _lib.load()
+    _require_workspace(workspace, "workspace",
+                       int(lib.retention_chunkwise_workspace_bytes(B, H, N, dk, dv, int(chunk), dt)), q.device)
     g = _gamma_array(gamma, H)
     gn_p, _keep = _gn_struct(gn, H, dv, q.device, gate, out)
     rc = lib.retention_chunk_output(
@@ -228,10 +292,11 @@ def recurrent_step(q, k, v, gamma: GammaLike, state, gn: Optional[GroupNorm] = N
     ``gate`` (optional, needs ``gn``): B*H*dv values of the output's dtype;
     the result becomes GroupNorm(o) * swish(gate).
     """
-    lib = _lib.load()
     for name, t in (("q", q), ("k", k), ("v", v), ("state", state)):
-        if not t.is_cuda or not t.is_contiguous():
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous device tensor")
+        if t.device != state.device:
+            raise ValueError(f"{name} must be on the state's device {state.device}")
     if state.dtype != torch.float32 or state.dim() != 4:
         raise ValueError("state must be float32 [B,H,dk,dv]")
     B, H, dk, dv = state.shape
@@ -242,6 +307,12 @@ def recurrent_step(q, k, v, gamma: GammaLike, state, gn: Optional[GroupNorm] = N
     dt = _dtype_code(q)
     if out is None:
         out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    elif not isinstance(out, torch.Tensor) or out.numel() != B * H * dv:
+        raise ValueError(f"out must hold B*H*dv = {B * H * dv} elements")
+    else:
+        _require(out, "out", tuple(out.shape), q.dtype, q.device)
+    _no_overlap(out, "out", q, k, v, state)
+    lib = _lib.load()
     g = _gamma_array(gamma, H)
     gn_p, _keep = _gn_struct(gn, H, dv, q.device, gate, out)
     rc = lib.retention_recurrent_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), g, state.data_ptr(),
@@ -265,24 +336,30 @@ def chunkwise_backward(q, k, v, grad_o, gamma: GammaLike, chunk: int, state_in=N
     produced), True (allocate) or an fp32 [B,H,dk,dv] tensor to fill.
     ``grads``: optional preallocated (grad_q, grad_k, grad_v).
     """
-    lib = _lib.load()
     B, H, N, dk, dv, dt = _check_qkv(q, k, v)
-    if not grad_o.is_cuda or not grad_o.is_contiguous() or grad_o.dtype != q.dtype or grad_o.shape != v.shape:
-        raise ValueError("grad_o must be a contiguous device tensor shaped and typed like v")
-    for name, t in (("state_in", state_in), ("grad_state_out", grad_state_out), ("grad_state_in", grad_state_in)):
-        if isinstance(t, torch.Tensor):
-            if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (B, H, dk, dv):
-                raise ValueError(f"{name} must be contiguous float32 [B,H,dk,dv]")
+    _require(grad_o, "grad_o", tuple(v.shape), q.dtype, q.device)
+    state_in = _state(state_in, "state_in", B, H, dk, dv, q.device)
+    grad_state_out = _state(grad_state_out, "grad_state_out", B, H, dk, dv, q.device)
     if grad_state_in is True:
         grad_state_in = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
-    elif grad_state_in is False:
+    elif grad_state_in is False or grad_state_in is None:
         grad_state_in = None
+    else:
+        _state(grad_state_in, "grad_state_in", B, H, dk, dv, q.device)
     if grads is None:
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    if len(grads) != 3:
+        raise ValueError("grads must be (grad_q, grad_k, grad_v)")
     gq, gk, gv = grads
+    for name, t, shape in (("grad_q", gq, q.shape), ("grad_k", gk, k.shape), ("grad_v", gv, v.shape)):
+        _require(t, name, tuple(shape), q.dtype, q.device)
+        _no_overlap(t, name, q, k, v, grad_o, state_in, grad_state_out)
+    lib = _lib.load()
     nbytes = int(lib.retention_chunkwise_backward_workspace_bytes(B, H, N, dk, dv, int(chunk), dt))
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _require_workspace(workspace, "workspace", nbytes, q.device)
     g = _gamma_array(gamma, H)
     rc = lib.retention_chunkwise_backward(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), grad_o.data_ptr(), g, gq.data_ptr(), gk.data_ptr(), gv.data_ptr(),

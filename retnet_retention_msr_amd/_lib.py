@@ -54,7 +54,14 @@ def load():
             f"{LIB_PATH} is missing: build it with `python -m retnet_retention_msr_amd.build` "
             "(there is no fallback path)"
         )
-    lib = ctypes.CDLL(LIB_PATH)
+    _lib = open_library(LIB_PATH)
+    return _lib
+
+
+def open_library(path):
+    """ctypes handle of a library at ``path`` that implements include/retention.h,
+    with every entry point's argument and result types declared."""
+    lib = ctypes.CDLL(path)
     vp, i, f_p, gn_p = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(GnStruct)
     lib.retention_abi_version.argtypes = []
     lib.retention_abi_version.restype = i
@@ -81,9 +88,8 @@ def load():
     lib.retention_chunkwise_backward.restype = i
     if lib.retention_abi_version() != ABI_VERSION:
         raise RuntimeError(
-            f"{LIB_PATH} has ABI version {lib.retention_abi_version()}, this binding expects {ABI_VERSION}: rebuild it"
+            f"{path} has ABI version {lib.retention_abi_version()}, this binding expects {ABI_VERSION}: rebuild it"
         )
-    _lib = lib
     return lib
 
 

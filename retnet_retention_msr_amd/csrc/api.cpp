@@ -6,6 +6,8 @@
 // cover and the generic vector-ALU kernels otherwise, and it sizes the
 // chunkwise workspace.
 #include <algorithm>
+#include <cfloat>
+#include <climits>
 #include <cmath>
 #include <cstdint>
 
@@ -66,6 +68,17 @@ int check_gn(const retention_gn_t* gn, GnArgs* out) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? RET_OK : RET_ERR_HIP; }
 
+// A chunk at least as long as the sequence is one chunk: every such length
+// gives the same result. It is brought down to the sequence length rounded up
+// to a multiple of the MFMA block height (so the MFMA kernels stay eligible),
+// which keeps every later product of a chunk index and the chunk length
+// within int range.
+int effective_chunk(int N, int chunk) {
+  if (chunk <= N) return chunk;
+  const int64_t up = (static_cast<int64_t>(N) + kMfmaRows - 1) / kMfmaRows * kMfmaRows;
+  return static_cast<int>(std::min<int64_t>(chunk, up <= INT_MAX ? up : N));
+}
+
 // Chunkwise execution plan.
 struct ChunkPlan {
   bool mfma;
@@ -80,7 +93,7 @@ struct ChunkPlan {
 ChunkPlan plan_chunkwise(int B, int H, int N, int dk, int dv, int chunk, int dtype) {
   ChunkPlan p{};
   p.mfma = dtype == RET_BF16 && ret::mfma_supports(dk, dv) && chunk % kMfmaRows == 0;
-  p.nchunks = (N + chunk - 1) / chunk;
+  p.nchunks = static_cast<int>((static_cast<int64_t>(N) + chunk - 1) / chunk);
   const size_t heads = static_cast<size_t>(B) * H;
   const size_t dkdv = static_cast<size_t>(dk) * dv;
   if (p.mfma) {
@@ -103,17 +116,18 @@ ChunkPlan plan_chunkwise(int B, int H, int N, int dk, int dv, int chunk, int dty
 }
 
 // Shared validation of the chunkwise entry points (no HIP calls).
-int check_chunkwise(const float* gamma_host, int B, int H, int N, int dk, int dv, int chunk, int dtype,
+int check_chunkwise(const float* gamma_host, int B, int H, int N, int dk, int dv, int* chunk, int dtype,
                     const retention_gn_t* gn, const void* workspace, size_t workspace_bytes, GnArgs* g,
                     ChunkPlan* plan, HeadDecay* decay) {
-  if (chunk <= 0) return RET_ERR_INVALID_ARG;
+  if (*chunk <= 0) return RET_ERR_INVALID_ARG;
   int st = check_sizes(B, H, N, dk, dv, dtype);
   if (st != RET_OK) return st;
+  *chunk = effective_chunk(N, *chunk);
   st = check_gamma(gamma_host, H, nullptr);
   if (st != RET_OK) return st;
   st = check_gn(gn, g);
   if (st != RET_OK) return st;
-  *plan = plan_chunkwise(B, H, N, dk, dv, chunk, dtype);
+  *plan = plan_chunkwise(B, H, N, dk, dv, *chunk, dtype);
   if (plan->total > 0 && (!workspace || workspace_bytes < plan->total)) return RET_ERR_INVALID_ARG;
   check_gamma(gamma_host, H, decay);
   return RET_OK;
@@ -246,7 +260,7 @@ int retention_parallel(const void* q, const void* k, const void* v, const float*
 
 size_t retention_chunkwise_workspace_bytes(int B, int H, int N, int dk, int dv, int chunk, int dtype) {
   if (check_sizes(B, H, N, dk, dv, dtype) != RET_OK || chunk <= 0) return 0;
-  return plan_chunkwise(B, H, N, dk, dv, chunk, dtype).total;
+  return plan_chunkwise(B, H, N, dk, dv, effective_chunk(N, chunk), dtype).total;
 }
 
 int retention_chunkwise(const void* q, const void* k, const void* v, const float* gamma_host, void* o, int B, int H,
@@ -256,7 +270,7 @@ int retention_chunkwise(const void* q, const void* k, const void* v, const float
   GnArgs g;
   ChunkPlan p;
   HeadDecay decay;
-  const int st = check_chunkwise(gamma_host, B, H, N, dk, dv, chunk, dtype, gn, workspace, workspace_bytes, &g, &p,
+  const int st = check_chunkwise(gamma_host, B, H, N, dk, dv, &chunk, dtype, gn, workspace, workspace_bytes, &g, &p,
                                  &decay);
   if (st != RET_OK) return st;
   const Dims d{B, H, N, dk, dv};
@@ -273,7 +287,7 @@ int retention_chunk_states(const void* k, const void* v, const float* gamma_host
   GnArgs g;
   ChunkPlan p;
   HeadDecay decay;
-  const int st = check_chunkwise(gamma_host, B, H, N, dk, dv, chunk, dtype, nullptr, workspace, workspace_bytes, &g,
+  const int st = check_chunkwise(gamma_host, B, H, N, dk, dv, &chunk, dtype, nullptr, workspace, workspace_bytes, &g,
                                  &p, &decay);
   if (st != RET_OK) return st;
   const Dims d{B, H, N, dk, dv};
@@ -288,7 +302,7 @@ int retention_chunk_output(const void* q, const void* k, const void* v, const fl
   GnArgs g;
   ChunkPlan p;
   HeadDecay decay;
-  const int st = check_chunkwise(gamma_host, B, H, N, dk, dv, chunk, dtype, gn, workspace, workspace_bytes, &g, &p,
+  const int st = check_chunkwise(gamma_host, B, H, N, dk, dv, &chunk, dtype, gn, workspace, workspace_bytes, &g, &p,
                                  &decay);
   if (st != RET_OK) return st;
   const Dims d{B, H, N, dk, dv};
@@ -315,7 +329,7 @@ int retention_recurrent_step(const void* q, const void* k, const void* v, const 
 
 size_t retention_chunkwise_backward_workspace_bytes(int B, int H, int N, int dk, int dv, int chunk, int dtype) {
   if (check_sizes(B, H, N, dk, dv, dtype) != RET_OK || chunk <= 0) return 0;
-  return plan_backward(B, H, N, dk, dv, chunk, dtype).total;
+  return plan_backward(B, H, N, dk, dv, effective_chunk(N, chunk), dtype).total;
 }
 
 int retention_chunkwise_backward(const void* q, const void* k, const void* v, const void* grad_o,
@@ -328,6 +342,13 @@ int retention_chunkwise_backward(const void* q, const void* k, const void* v, co
   if (st != RET_OK) return st;
   st = check_gamma(gamma_host, H, nullptr);
   if (st != RET_OK) return st;
+  // The final-state gradient enters the reverse-time retentions divided by
+  // gamma; for a subnormal gamma that quotient overflows float.
+  if (grad_state_out) {
+    for (int h = 0; h < H; ++h)
+      if (gamma_host[h] < FLT_MIN) return RET_ERR_UNSUPPORTED;
+  }
+  chunk = effective_chunk(N, chunk);
   const BackwardPlan p = plan_backward(B, H, N, dk, dv, chunk, dtype);
   if (!workspace || workspace_bytes < p.total) return RET_ERR_INVALID_ARG;
   HeadDecay decay;

@@ -1,26 +1,13 @@
-// Device-side helpers shared by the retention kernels (gfx950 only).
+// Device-side helpers shared by the retention kernels (gfx950 only). The
+// host-visible argument structures they use are declared in kernels.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 namespace ret {
-
-constexpr int kMaxHeads = 256;
-
-// log2(gamma_h) per head, computed on the host in double precision and
-// rounded once to float. A decay power gamma^e is formed as exp2(e * log2g).
-struct HeadDecay {
-  float log2g[kMaxHeads];
-};
-
-struct GnArgs {
-  int enabled;
-  float eps;
-  const float* weight;  // [H*dv] or nullptr
-  const float* bias;    // [H*dv] or nullptr
-  const void* gate;     // like O (element type of the inputs), or nullptr
-};
 
 // swish(g) = g * sigmoid(g) = g / (1 + e^-g), the gate's activation: e^-g as
 // the hardware exp2 of -g * log2(e), then the hardware reciprocal (about one

@@ -10,6 +10,7 @@
 // contiguous bytes per row), keeps 4 column partial sums of q . S per lane, and
 // the 16 row groups are reduced through LDS at the end. With GroupNorm the
 // workgroup walks all column slabs of its head so it sees the whole row.
+#include "common.h"
 #include "kernels.h"
 
 namespace ret {

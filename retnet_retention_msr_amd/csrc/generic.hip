@@ -13,6 +13,7 @@
 //
 // With one chunk spanning the sequence and no state the output kernel is the
 // parallel form. These kernels favour simplicity over speed.
+#include "common.h"
 #include "kernels.h"
 
 namespace ret {

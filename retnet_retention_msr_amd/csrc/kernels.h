@@ -1,15 +1,32 @@
-// Host-side launchers of the retention kernels. Each returns the HIP status of
-// the launch (hipGetLastError after enqueueing); arguments were validated by
-// the C ABI before these are called.
+// Host-side launchers of the retention kernels and the planning functions of
+// the C ABI. Each launcher returns the HIP status of the launch
+// (hipGetLastError after enqueueing); arguments were validated by the C ABI
+// before these are called. This header is plain host C++ (HIP runtime API
+// types only), so the validation and planning code that includes it also
+// builds with a host compiler alone.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
-#include "common.h"
-
 namespace ret {
+
+constexpr int kMaxHeads = 256;
+
+// log2(gamma_h) per head, computed on the host in double precision and
+// rounded once to float. A decay power gamma^e is formed as exp2(e * log2g).
+struct HeadDecay {
+  float log2g[kMaxHeads];
+};
+
+struct GnArgs {
+  int enabled;
+  float eps;
+  const float* weight;  // [H*dv] or nullptr
+  const float* bias;    // [H*dv] or nullptr
+  const void* gate;     // like O (element type of the inputs), or nullptr
+};
 
 // Sizes shared by the launchers.
 struct Dims {
@@ -55,6 +72,11 @@ hipError_t launch_mfma_state_walk(const uint16_t* k, const uint16_t* v, const fl
 int walk_k_tiles(int dk);
 bool walk_wide(int64_t heads, int dk, int dv);
 int walk_tiles_per_head(int64_t heads, int dk, int dv);
+// The full-dk walk form covers these dk.
+bool walk_full_dk(int dk);
+// Whether a segmented walk runs once from zero plus the fix-up pass (true) or
+// twice (segment end states first, then every segment from its true start).
+bool walk_fixup_segments(int chunk, int dk, int dv);
 
 // bf16 MFMA output: per 64-row query block, intra-chunk causal product plus the
 // read-out of the bf16 chunk state (when chunk_states is non-null), then the

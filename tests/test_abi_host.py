@@ -2,8 +2,15 @@
 
 The library must load, export every function include/retention.h declares,
 and reject invalid or unsupported arguments before making any HIP call. Only
-argument combinations that fail validation are passed here; the fake device
-pointers below are never dereferenced.
+argument combinations that fail validation are passed to the real library;
+the fake device pointers below are never dereferenced.
+
+With RETENTION_ABI_TEST_LIB naming the host-only build of the validation and
+planning code (tests/host_shim: the launchers replaced by stubs that record
+the call and touch nothing; test_abi_sanitized.py builds it with the address
+and undefined-behaviour sanitizers and runs this file against it), the same
+checks run there, plus valid-argument calls that go through planning to the
+stub launchers.
 """
 
 import ctypes
@@ -18,11 +25,18 @@ from retnet_retention_msr_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "retention.h")
 
-FAKE = 0x10000  # never dereferenced: every call below fails validation first
+FAKE = 0x10000  # never dereferenced: every call below fails validation first (or reaches a stub launcher)
+
+SHIM = os.environ.get("RETENTION_ABI_TEST_LIB")
+shim_only = pytest.mark.skipif(not SHIM, reason="valid-argument calls only run against the host shim")
 
 
 @pytest.fixture(scope="module")
 def lib():
+    if SHIM:
+        lib = _lib.open_library(SHIM)
+        lib.retention_shim_launches.restype = ctypes.c_int
+        return lib
     return _lib.load()
 
 
@@ -208,3 +222,67 @@ def test_backward_workspace_bytes(lib):
         lib.retention_chunkwise_workspace_bytes(B, H, N, dk, dv, 512, 1)
     assert ws(0, H, N, dk, dv, 512, 1) == 0
     assert ws(B, H, N, dk, dv, 0, 1) == 0
+
+
+def test_backward_rejects_subnormal_gamma_with_a_final_state_gradient(lib):
+    """dL/dS_N enters divided by gamma: a subnormal gamma would overflow that quotient."""
+    need = lib.retention_chunkwise_backward_workspace_bytes(1, 2, 256, 64, 128, 64, 1)
+    g = _gamma([1e-39, 0.9])
+    assert lib.retention_chunkwise_backward(FAKE, FAKE, FAKE, FAKE, g, FAKE, FAKE, FAKE, 1, 2, 256, 64, 128, 64, 1,
+                                            None, FAKE, None, FAKE, need, None) == _lib.RET_ERR_UNSUPPORTED
+
+
+def test_huge_chunk_plans_like_one_chunk(lib):
+    """A chunk at or above N is one chunk: the workspace equals that of the smallest such chunk."""
+    ws = lib.retention_chunkwise_workspace_bytes
+    one = ws(1, 2, 1000, 64, 128, 1024, 1)
+    assert one > 0
+    assert ws(1, 2, 1000, 64, 128, 2**31 - 1, 1) == one
+    assert ws(1, 2, 1000, 64, 128, 2**31 - 64, 1) == one
+    assert lib.retention_chunkwise_backward_workspace_bytes(1, 2, 1000, 64, 128, 2**31 - 1, 1) == \
+        lib.retention_chunkwise_backward_workspace_bytes(1, 2, 1000, 64, 128, 1024, 1)
+
+
+def _launches(lib):
+    return lib.retention_shim_launches()
+
+
+@shim_only
+@pytest.mark.parametrize("shape", [
+    (8, 16, 8192, 256, 512, 512, 1),   # the 6.7B-shaped prefill
+    (1, 16, 65536, 256, 512, 64, 1),   # one long sequence, small chunks (segmented walk, two passes)
+    (1, 16, 65536, 256, 512, 512, 1),  # segmented walk with the fix-up pass
+    (2, 8, 2048, 256, 512, 256, 1),
+    (1, 1, 64, 16, 16, 16, 0),         # fp32 generic path
+    (1, 3, 77, 48, 96, 2**31 - 1, 1),  # generic bf16 shape, chunk near INT_MAX
+    (2, 4, 1000, 128, 256, 2**31 - 64, 1),
+])
+def test_valid_chunkwise_calls_reach_the_launchers(lib, shape):
+    B, H, N, dk, dv, chunk, dtype = shape
+    need = lib.retention_chunkwise_workspace_bytes(B, H, N, dk, dv, chunk, dtype)
+    g = _gamma([1 - 2.0 ** (-5 - h) for h in range(H)])
+    before = _launches(lib)
+    assert lib.retention_chunkwise(FAKE, FAKE, FAKE, g, FAKE, B, H, N, dk, dv, chunk, dtype, None, FAKE, None,
+                                   FAKE if need else None, need, None) == 0
+    gn = _lib.GnStruct(1e-5, None, None, None)
+    assert lib.retention_chunkwise(FAKE, FAKE, FAKE, g, FAKE, B, H, N, dk, dv, chunk, dtype, FAKE, FAKE,
+                                   ctypes.byref(gn), FAKE if need else None, need, None) == 0
+    assert lib.retention_parallel(FAKE, FAKE, FAKE, g, FAKE, B, H, N, dk, dv, dtype, ctypes.byref(gn), None) == 0
+    assert _launches(lib) > before
+
+
+@shim_only
+@pytest.mark.parametrize("shape", [
+    (8, 16, 8192, 256, 512, 512, 1),
+    (1, 2, 300, 64, 320, 64, 1),   # dv above the 256-column part width: two parts
+    (1, 1, 64, 16, 16, 16, 0),
+])
+def test_valid_backward_and_decode_calls_reach_the_launchers(lib, shape):
+    B, H, N, dk, dv, chunk, dtype = shape
+    need = lib.retention_chunkwise_backward_workspace_bytes(B, H, N, dk, dv, chunk, dtype)
+    g = _gamma([1 - 2.0 ** (-5 - h) for h in range(H)])
+    before = _launches(lib)
+    assert lib.retention_chunkwise_backward(FAKE, FAKE, FAKE, FAKE, g, FAKE, FAKE, FAKE, B, H, N, dk, dv, chunk,
+                                            dtype, FAKE, FAKE, FAKE, FAKE, need, None) == 0
+    assert lib.retention_recurrent_step(FAKE, FAKE, FAKE, g, FAKE, FAKE, B, H, dk, dv, dtype, None, None) == 0
+    assert _launches(lib) > before
