@@ -77,20 +77,42 @@ def output_flops(B, H, N, chunk, dk=DK, dv=DV):
     return float((chunk + 1) * (dk + dv) + 2 * dk * dv) * B * H * N
 
 
-def output_bytes(B, H, N, chunk, dk=DK, dv=DV, state_in=False):
-    """HBM bytes the output stage must move: bf16 Q, K, V and O, plus the bf16
-    state carried into every chunk that has one (all but the first without
-    state_in)."""
+def method_bytes(B, H, N, dk=DK, dv=DV):
+    """HBM bytes the method itself must move: bf16 Q, K, V read once and O
+    written once, (2*dk + 2*dv) * 2 bytes per token-head (3,072 at dk 256,
+    dv 512; 3.221e9 B for B8 H16 N8192). Whatever a design moves beyond this
+    (states written and read back, operands read twice) is reported apart, as
+    design bytes."""
+    return float(B * H * N * (2 * dk + 2 * dv) * 2)
+
+
+def chunk_state_bytes(B, H, N, chunk, dk=DK, dv=DV, state_in=False):
+    """The bf16 state carried into every chunk that has one, as the two-stage
+    design writes it once (state stage) and reads it once (output stage)."""
     nchunks = -(-N // chunk)
     states = nchunks if state_in else nchunks - 1
-    return float(B * H * N * (2 * dk + 2 * dv) * 2 + B * H * states * dk * dv * 2)
+    return float(B * H * states * dk * dv * 2)
 
 
-def walk_bytes(B, H, N, chunk, dk=DK, dv=DV):
-    """HBM bytes of the state stage: bf16 K and V read, the bf16 state of every
-    chunk written, the fp32 final state written."""
+def two_stage_design_bytes(B, H, N, chunk, dk=DK, dv=DV):
+    """Bytes the two-stage design moves per forward: method bytes, plus K and V
+    read a second time by the state stage, plus the bf16 chunk states written
+    by the state stage (every chunk) and read by the output stage (all but the
+    first), plus the fp32 final state."""
     nchunks = -(-N // chunk)
-    return float(B * H * N * (dk + dv) * 2 + B * H * nchunks * dk * dv * 2 + B * H * dk * dv * 4)
+    return (method_bytes(B, H, N, dk, dv) + float(B * H * N * (dk + dv) * 2)
+            + float(B * H * nchunks * dk * dv * 2) + chunk_state_bytes(B, H, N, chunk, dk, dv)
+            + float(B * H * dk * dv * 4))
+
+
+def roofline_fracs(flop, nbytes, seconds):
+    """Fractions of the binding roof min(MFMA peak, AI * HBM peak), of HBM
+    bandwidth and of the MFMA peak, for method flops and bytes over a time."""
+    roof = min(PEAK_BF16, flop / nbytes * PEAK_HBM)
+    return {"binding_roof": "mfma" if roof == PEAK_BF16 else "hbm",
+            "binding_roof_frac": flop / seconds / roof,
+            "hbm_frac": nbytes / seconds / PEAK_HBM,
+            "mfma_frac": flop / seconds / PEAK_BF16}
 
 
 def decode_bytes(B, H, dk=DK, dv=DV):
@@ -195,13 +217,10 @@ def long_sequence_sweep(ret, synthetic, dev, min_reps=5, warm_s=0.05, timed_s=0.
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
         flop = algorithmic_flops(1, H_, n, chunk)
-        byts = output_bytes(1, H_, n, chunk) + walk_bytes(1, H_, n, chunk)
-        # The binding roof of the whole forward: min(MFMA peak, AI * HBM peak).
-        roof = min(PEAK_BF16, flop / byts * PEAK_HBM)
+        byts = method_bytes(1, H_, n)
         return {"N": n, "chunk": chunk, "ms": ms, "reps": reps, "tokens_per_s": n / (ms * 1e-3),
-                "algorithmic_flop": flop, "algorithmic_bytes": byts,
-                "binding_roof": "mfma" if roof == PEAK_BF16 else "hbm",
-                "binding_roof_frac": flop / (ms * 1e-3) / roof}
+                "algorithmic_flop": flop, "method_bytes": byts,
+                **roofline_fracs(flop, byts, ms * 1e-3)}
 
     by_length = [run(n, 512) for n in LONG_LENGTHS]
     by_chunk = [run(max(LONG_LENGTHS), c) for c in LONG_CHUNKS]
@@ -250,17 +269,15 @@ def small_config(ret, synthetic, dev, reps=200, warm_s=0.05):
     res = {"workload": "B=2 H=8 N=2048 dk=256 dv=512 bf16, no GroupNorm", "reps": reps}
     # parallel: N(N+1)/2 score entries per head, each 2*dk + 2*dv flop; bytes Q, K, V, O.
     par_flop = float(b * h * n * (n + 1) * (DK + DV))
-    par_bytes = float(b * h * n * (2 * DK + 2 * DV) * 2)
+    par_bytes = method_bytes(b, h, n)
     us = timed(lambda: ret.parallel(qd, kd, vd, gamma, out=out))
-    roof = min(PEAK_BF16, par_flop / par_bytes * PEAK_HBM)
     res["parallel"] = {"us": us, "tokens_per_s": b * n / (us * 1e-6), "algorithmic_flop": par_flop,
-                       "binding_roof_frac": par_flop / (us * 1e-6) / roof}
+                       "method_bytes": par_bytes, **roofline_fracs(par_flop, par_bytes, us * 1e-6)}
     ch_flop = algorithmic_flops(b, h, n, c)
-    ch_bytes = output_bytes(b, h, n, c) + walk_bytes(b, h, n, c)
+    ch_bytes = method_bytes(b, h, n)
     us = timed(lambda: ret.chunkwise(qd, kd, vd, gamma, c, out=out, workspace=ws))
-    roof = min(PEAK_BF16, ch_flop / ch_bytes * PEAK_HBM)
     res["chunkwise"] = {"us": us, "chunk": c, "tokens_per_s": b * n / (us * 1e-6), "algorithmic_flop": ch_flop,
-                        "algorithmic_bytes": ch_bytes, "binding_roof_frac": ch_flop / (us * 1e-6) / roof}
+                        "method_bytes": ch_bytes, **roofline_fracs(ch_flop, ch_bytes, us * 1e-6)}
     return res
 
 
@@ -460,7 +477,8 @@ def gated_prefill(ret, torch, dev, stream, qd, kd, vd, gamma, ws, state, out, gn
     torch.cuda.synchronize()
     ms = ev[0][0].elapsed_time(ev[-1][2]) / steps
     out_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
-    bytes_out = output_bytes(B, H, N, CHUNK) + B * H * N * DV * 2
+    # Method bytes of the gated output: Q, K, V, O plus the gate read once.
+    bytes_out = method_bytes(B, H, N) + B * H * N * DV * 2
     del gate
     return {
         "workload": "the prefill above with the gated epilogue swish(gate) * GroupNorm(O), gate bf16 [B,H,N,dv]",
@@ -470,7 +488,7 @@ def gated_prefill(ret, torch, dev, stream, qd, kd, vd, gamma, ws, state, out, gn
         "output_launch_ms": out_ms,
         "output_roofline": {
             "bound": "hbm",
-            "algorithmic_bytes_per_launch": bytes_out,
+            "method_bytes_per_launch": bytes_out,
             "achieved": bytes_out / (out_ms * 1e-3) / 1e9,
             "peak": PEAK_HBM / 1e9,
             "unit": "GB/s",
@@ -541,28 +559,16 @@ def main():
             events[2].record(stream)
 
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    print(f"[bench] timing {args.steps} prefill steps", file=sys.stderr, flush=True)
-    t_wall = time.perf_counter()
-    for i in range(args.steps):
-        step(ev[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    ms = ev[0][0].elapsed_time(ev[-1][2]) / args.steps
-    per_step = sorted(e[0].elapsed_time(e[2]) for e in ev)
-    ms_median, ms_min = per_step[len(per_step) // 2], per_step[0]
-    walk_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    out_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
-    tokens_per_s = B * N / (ms * 1e-3)
-    flops = algorithmic_flops(B, H, N, CHUNK)
-    achieved = flops / (ms * 1e-3)
-    flops_out = output_flops(B, H, N, CHUNK)
-    flops_walk = flops - flops_out
-    bytes_out = output_bytes(B, H, N, CHUNK)
-    bytes_walk = walk_bytes(B, H, N, CHUNK)
+
+    # The CPU oracle first, while the GPU has nothing to do; then the other
+    # GPU measurements; the headline prefill last, so that its warm-up and
+    # timed steps run at the clocks the GPU holds under sustained load (from
+    # idle, the first tens of milliseconds of this load run slower).
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(q, k, v, gamma, args.cpu_batch_rows)
+        cpu["other_cases"] = cpu_extra(synthetic, gamma)
 
     gated = None
     if not args.skip_gated:
@@ -575,6 +581,8 @@ def main():
         backward = backward_pass(ret, torch, dev, stream, qd, kd, vd, gamma, args.steps)
 
     # Decode: single-token steps from the prefill's state.
+    step()
+    torch.cuda.synchronize()
     if args.skip_decode:
         args.decode_steps = 0
     print(f"[bench] timing {args.decode_steps} decode steps", file=sys.stderr, flush=True)
@@ -597,6 +605,7 @@ def main():
     us_step = d0.elapsed_time(d1) * 1e3 / T if T else float("nan")
     dbytes = decode_bytes(B, H)
     dgbps = dbytes / (us_step * 1e-6) / 1e9
+    del dq, dk_, dvv, dstate
 
     decode_b32 = None
     if not args.skip_decode and not args.skip_decode_b32:
@@ -608,16 +617,40 @@ def main():
         print("[bench] B=2 H=8 N=2048 parallel and chunkwise", file=sys.stderr, flush=True)
         small = small_config(ret, synthetic, dev)
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(q, k, v, gamma, args.cpu_batch_rows)
-        cpu["other_cases"] = cpu_extra(synthetic, gamma)
-
     long_seq = None
     if not args.skip_long:
         print("[bench] long-sequence sweep", file=sys.stderr, flush=True)
         long_seq = long_sequence_sweep(ret, synthetic, dev)
+
+    # The headline: W untimed steps, then exactly K timed steps between two
+    # synchronisations, HIP events on the launch stream around every stage.
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} prefill steps", file=sys.stderr, flush=True)
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = ev[0][0].elapsed_time(ev[-1][2]) / args.steps
+    per_step = sorted(e[0].elapsed_time(e[2]) for e in ev)
+    ms_median, ms_min = per_step[len(per_step) // 2], per_step[0]
+    walk_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    out_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    tokens_per_s = B * N / (ms * 1e-3)
+    flops = algorithmic_flops(B, H, N, CHUNK)
+    achieved = flops / (ms * 1e-3)
+    flops_out = output_flops(B, H, N, CHUNK)
+    flops_walk = flops - flops_out
+    mbytes = method_bytes(B, H, N)
+    # What the two stages move by design: the output stage reads Q, K, V and
+    # the bf16 chunk states and writes O; the state stage reads K and V again
+    # and writes the chunk states and the final state.
+    design_out = mbytes + chunk_state_bytes(B, H, N, CHUNK)
+    design_step = two_stage_design_bytes(B, H, N, CHUNK)
+    design_walk = design_step - design_out
 
     traffic = measured_traffic()
     line = {
@@ -640,41 +673,50 @@ def main():
             "B": B, "H": H, "N": N, "dk": DK, "dv": DV, "chunk": CHUNK,
             "gamma": "1 - 2^(-5-h)", "parallelism": "single GPU",
         },
+        # The dominant kernel is the output stage. Its fractions count the
+        # method's bytes (Q, K, V read, O written) and the output stage's share
+        # of the method's flops; the arithmetic intensity of the whole forward
+        # (299 flop/B) and of this stage (214 flop/B) are both below the ridge
+        # (312.5 flop/B), so the binding roof is HBM.
         "roofline": {
             "bound": "hbm",
-            "achieved": bytes_out / (out_ms * 1e-3) / 1e9,
+            "achieved": mbytes / (out_ms * 1e-3) / 1e9,
             "peak": PEAK_HBM / 1e9,
             "unit": "GB/s",
-            "frac": bytes_out / (out_ms * 1e-3) / PEAK_HBM,
+            "frac": mbytes / (out_ms * 1e-3) / PEAK_HBM,
             "traffic": traffic["chunk_out"],
             "kernel": "mfma_chunk_out_kernel (retention_chunk_output: intra-chunk products, read-out, GroupNorm)",
-            "algorithmic_bytes_per_launch": bytes_out,
-            "algorithmic_flop_per_launch": flops_out,
-            "arithmetic_intensity_flop_per_byte": flops_out / bytes_out,
+            "method_bytes_per_launch": mbytes,
+            "method_flop_per_launch": flops_out,
+            "arithmetic_intensity_flop_per_byte": flops_out / mbytes,
             "ridge_flop_per_byte": PEAK_BF16 / PEAK_HBM,
+            "design_bytes_per_launch": design_out,
+            "design_over_method": design_out / mbytes,
+            "traffic_over_method": traffic["chunk_out"] / mbytes if traffic["chunk_out"] else None,
             "mfma_tflops": flops_out / (out_ms * 1e-3) / 1e12,
             "mfma_frac": flops_out / (out_ms * 1e-3) / PEAK_BF16,
             "launch_ms": out_ms,
         },
         "step_roofline": {
             "bound": "hbm",
-            "achieved": (bytes_out + bytes_walk) / (ms * 1e-3) / 1e9,
+            "achieved": mbytes / (ms * 1e-3) / 1e9,
             "peak": PEAK_HBM / 1e9,
             "unit": "GB/s",
-            "frac": (bytes_out + bytes_walk) / (ms * 1e-3) / PEAK_HBM,
-            "algorithmic_bytes_per_step": bytes_out + bytes_walk,
-            "algorithmic_flop_per_step": flops,
+            "frac": mbytes / (ms * 1e-3) / PEAK_HBM,
+            "method_bytes_per_step": mbytes,
+            "method_flop_per_step": flops,
+            "arithmetic_intensity_flop_per_byte": flops / mbytes,
+            "design_bytes_per_step": design_step,
+            "design_over_method": design_step / mbytes,
             "mfma_tflops": achieved / 1e12,
             "mfma_frac": achieved / PEAK_BF16,
         },
         "state_walk": {
             "kernel": "mfma_state_walk2_kernel (retention_chunk_states: chunk-state carry)",
             "launch_ms": walk_ms,
-            "bound": "hbm",
-            "algorithmic_bytes_per_launch": bytes_walk,
-            "achieved_gbps": bytes_walk / (walk_ms * 1e-3) / 1e9,
-            "frac": bytes_walk / (walk_ms * 1e-3) / PEAK_HBM,
-            "algorithmic_flop_per_launch": flops_walk,
+            "design_bytes_per_launch": design_walk,
+            "design_gbps": design_walk / (walk_ms * 1e-3) / 1e9,
+            "method_flop_per_launch": flops_walk,
             "mfma_tflops": flops_walk / (walk_ms * 1e-3) / 1e12,
             "traffic": traffic["state_walk"],
         },

@@ -39,14 +39,39 @@ def test_measured_traffic_is_keyed_by_kernel_source():
         assert v is None or v > 0
 
 
-def test_output_and_walk_bytes():
-    # Output stage: bf16 Q, K (dk) and V, O (dv) per token-head, plus the bf16
-    # dk x dv state of every chunk but the first (no state_in).
-    per_tok = (2 * 256 + 2 * 512) * 2
-    states = 8 * 16 * 15 * 256 * 512 * 2
-    assert bench.output_bytes(8, 16, 8192, 512) == 8 * 16 * 8192 * per_tok + states
-    assert bench.output_bytes(8, 16, 8192, 512, state_in=True) == 8 * 16 * 8192 * per_tok + states * 16 // 15
-    # State stage: K, V read; the bf16 state of all 16 chunks and the fp32 final state written.
-    assert bench.walk_bytes(8, 16, 8192, 512) == 8 * 16 * 8192 * 768 * 2 + 8 * 16 * 16 * 256 * 512 * 2 + 8 * 16 * 256 * 512 * 4
-    # Both stages sit below the ridge point of 2.5 PFLOP/s over 8 TB/s.
-    assert bench.output_flops(8, 16, 8192, 512) / bench.output_bytes(8, 16, 8192, 512) < bench.PEAK_BF16 / bench.PEAK_HBM
+def test_method_bytes_flops_and_intensity_at_the_prefill():
+    # Q, K, V read once and O written once: (2*256 + 2*512) * 2 = 3,072 bytes per token-head.
+    assert bench.method_bytes(1, 1, 1) == 3072
+    assert bench.method_bytes(8, 16, 8192) == 3072 * 8 * 16 * 8192 == 3_221_225_472
+    flop = bench.algorithmic_flops(8, 16, 8192, 512)
+    assert round(flop / 1e9, 1) == 962.9  # 9.629e11 flop per forward
+    assert round(flop / bench.method_bytes(8, 16, 8192)) == 299  # flop/B, below the 312.5 ridge
+    assert flop / bench.method_bytes(8, 16, 8192) < bench.PEAK_BF16 / bench.PEAK_HBM
+    # The output stage's share: 656,128 flop per token-head at chunk 512.
+    assert bench.output_flops(1, 1, 1, 512) == 656_128
+
+
+def test_roofline_fractions_use_the_binding_roof():
+    # At chunk 512 the forward is HBM-bound (AI 299): the binding-roof fraction equals the HBM fraction.
+    flop, nbytes = bench.algorithmic_flops(8, 16, 8192, 512), bench.method_bytes(8, 16, 8192)
+    f = bench.roofline_fracs(flop, nbytes, 1e-3)
+    assert f["binding_roof"] == "hbm"
+    assert abs(f["binding_roof_frac"] - f["hbm_frac"]) < 1e-12
+    assert abs(f["hbm_frac"] - nbytes / 1e-3 / 8e12) < 1e-12
+    assert abs(f["mfma_frac"] - flop / 1e-3 / 2.5e15) < 1e-12
+    # One row of 16 heads, 65,536 tokens at chunk 64: AI 187 flop/B; 20.4 M tokens/s reads about 0.13.
+    flop64, bytes64 = bench.algorithmic_flops(1, 16, 65536, 64), bench.method_bytes(1, 16, 65536)
+    assert round(flop64 / bytes64) == 187
+    t = 65536 / 20.4e6
+    assert abs(bench.roofline_fracs(flop64, bytes64, t)["binding_roof_frac"] - 0.128) < 0.005
+
+
+def test_two_stage_design_bytes():
+    # Method bytes, K and V again, the bf16 state of all 16 chunks written and
+    # of 15 read back, and the fp32 final state.
+    B, H, N = 8, 16, 8192
+    st = 256 * 512 * 2
+    expect = 3072 * B * H * N + 768 * 2 * B * H * N + B * H * (16 + 15) * st + B * H * 256 * 512 * 4
+    assert bench.two_stage_design_bytes(B, H, N, 512) == expect
+    assert bench.chunk_state_bytes(B, H, N, 512) == B * H * 15 * st
+    assert bench.chunk_state_bytes(B, H, N, 512, state_in=True) == B * H * 16 * st
