@@ -74,6 +74,8 @@ extern "C" {
 #define RETENTION_MAX_HEADS 256
 #define RETENTION_MAX_DK 256
 #define RETENTION_MAX_DV 1024
+/* Workspace bytes retention_chunkwise_noalloc can provide from its own scratch. */
+#define RETENTION_NOALLOC_MAX_WORKSPACE_BYTES ((size_t)64 << 20)
 
 enum retention_dtype { RET_F32 = 0, RET_BF16 = 1 };
 
@@ -135,6 +137,26 @@ int retention_chunkwise(const void* q, const void* k, const void* v,
                         const float* state_in, float* state_out,
                         const retention_gn_t* gn,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * retention_chunkwise for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, results and status codes as
+ * retention_chunkwise, without the workspace: the library takes it from a
+ * device array of its own (RETENTION_NOALLOC_MAX_WORKSPACE_BYTES, 64 MiB per
+ * GPU, held from the library's load until the process ends; its address is
+ * looked up once per device on the first call there). Calls whose
+ * retention_chunkwise_workspace_bytes(...) exceeds that size return
+ * RET_ERR_UNSUPPORTED. The call allocates nothing. All calls on one GPU share
+ * that GPU's array: calls that overlap in time on one GPU (different streams
+ * not ordered by the caller) race and give undefined results; the contents
+ * one call leaves are never read by the next.
+ */
+int retention_chunkwise_noalloc(const void* q, const void* k, const void* v,
+                                const float* gamma_host, void* o,
+                                int B, int H, int N, int dk, int dv, int chunk, int dtype,
+                                const float* state_in, float* state_out,
+                                const retention_gn_t* gn, void* stream);
 
 /*
  * The two stages of retention_chunkwise, for callers that want the chunk

@@ -23,6 +23,7 @@ __all__ = [
     "GroupNorm",
     "parallel",
     "chunkwise",
+    "chunkwise_noalloc",
     "chunk_states",
     "chunk_output",
     "recurrent_step",
@@ -237,6 +238,33 @@ def chunkwise(q, k, v, gamma: GammaLike, chunk: int, state_in=None, state_out: U
     if rc != 0:
         raise RetentionError("retention_chunkwise", rc)
     return out, state_out
+
+
+def chunkwise_noalloc(q, k, v, gamma: GammaLike, chunk: int, out, state_in=None, state_out=None,
+                      gn: Optional[GroupNorm] = None, gate=None):
+    """retention_chunkwise_noalloc: the chunkwise form with the library's own
+    device scratch as workspace, for callers that cannot allocate (nothing is
+    allocated here either: ``out`` and ``state_out``, if wanted, are the
+    caller's). Returns ``out``. Raises RetentionError (RET_ERR_UNSUPPORTED)
+    when the sizes need more workspace than the scratch holds
+    (NOALLOC_MAX_WORKSPACE_BYTES). Calls that overlap in time on one GPU race
+    on the shared scratch.
+    """
+    B, H, N, dk, dv, dt = _check_qkv(q, k, v)
+    _require(out, "out", (B, H, N, dv), q.dtype, q.device)
+    _no_overlap(out, "out", q, k, v)
+    state_in = _state(state_in, "state_in", B, H, dk, dv, q.device)
+    state_out = _state(state_out, "state_out", B, H, dk, dv, q.device)
+    g = _gamma_array(gamma, H)
+    gn_p, _keep = _gn_struct(gn, H, dv, q.device, gate, out)
+    lib = _lib.load()
+    rc = lib.retention_chunkwise_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), g, out.data_ptr(), B, H, N, dk, dv, int(chunk), dt,
+        state_in.data_ptr() if state_in is not None else None,
+        state_out.data_ptr() if state_out is not None else None, gn_p, _stream(q))
+    if rc != 0:
+        raise RetentionError("retention_chunkwise_noalloc", rc)
+    return out
 
 
 def chunk_states(k, v, gamma: GammaLike, chunk: int, workspace, state_in=None, state_out=None):

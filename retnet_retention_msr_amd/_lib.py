@@ -14,6 +14,8 @@ RET_OK = 0
 RET_ERR_INVALID_ARG = -1
 RET_ERR_UNSUPPORTED = -2
 RET_ERR_HIP = -3
+# RETENTION_NOALLOC_MAX_WORKSPACE_BYTES of include/retention.h.
+NOALLOC_MAX_WORKSPACE_BYTES = 64 << 20
 
 # Every symbol include/retention.h declares.
 EXPORTED = (
@@ -22,6 +24,7 @@ EXPORTED = (
     "retention_parallel",
     "retention_chunkwise_workspace_bytes",
     "retention_chunkwise",
+    "retention_chunkwise_noalloc",
     "retention_chunk_states",
     "retention_chunk_output",
     "retention_recurrent_step",
@@ -74,6 +77,8 @@ def open_library(path):
     lib.retention_chunkwise.argtypes = [vp, vp, vp, f_p, vp, i, i, i, i, i, i, i, vp, vp, gn_p, vp,
                                         ctypes.c_size_t, vp]
     lib.retention_chunkwise.restype = i
+    lib.retention_chunkwise_noalloc.argtypes = [vp, vp, vp, f_p, vp, i, i, i, i, i, i, i, vp, vp, gn_p, vp]
+    lib.retention_chunkwise_noalloc.restype = i
     lib.retention_chunk_states.argtypes = [vp, vp, f_p, i, i, i, i, i, i, i, vp, vp, vp, ctypes.c_size_t, vp]
     lib.retention_chunk_states.restype = i
     lib.retention_chunk_output.argtypes = [vp, vp, vp, f_p, vp, i, i, i, i, i, i, i, i, gn_p, vp,

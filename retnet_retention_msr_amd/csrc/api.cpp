@@ -20,6 +20,8 @@ using ret::Dims;
 using ret::GnArgs;
 using ret::HeadDecay;
 
+static_assert(ret::kScratchBytes == RETENTION_NOALLOC_MAX_WORKSPACE_BYTES, "scratch size");
+
 constexpr size_t kAlign = 256;
 constexpr int kMfmaRows = 64;            // MFMA kernels need chunk % 64 == 0
 constexpr int64_t kWalkTargetBlocks = 512;  // segment the walk below this many workgroups
@@ -278,6 +280,27 @@ int retention_chunkwise(const void* q, const void* k, const void* v, const float
   char* ws = static_cast<char*>(workspace);
   if (launch_states(p, k, v, state_in, state_out, ws, d, chunk, dtype, decay, s) != hipSuccess) return RET_ERR_HIP;
   return status_of(launch_output(p, q, k, v, o, ws, state_in != nullptr, d, chunk, dtype, decay, g, s));
+}
+
+int retention_chunkwise_noalloc(const void* q, const void* k, const void* v, const float* gamma_host, void* o, int B,
+                                int H, int N, int dk, int dv, int chunk, int dtype, const float* state_in,
+                                float* state_out, const retention_gn_t* gn, void* stream) {
+  // Everything is validated before the scratch address is looked up (the
+  // first HIP call), exactly as retention_chunkwise validates before launching.
+  if (!q || !k || !v || !o || chunk <= 0) return RET_ERR_INVALID_ARG;
+  int st = check_sizes(B, H, N, dk, dv, dtype);
+  if (st != RET_OK) return st;
+  st = check_gamma(gamma_host, H, nullptr);
+  if (st != RET_OK) return st;
+  GnArgs g;
+  st = check_gn(gn, &g);
+  if (st != RET_OK) return st;
+  const ChunkPlan p = plan_chunkwise(B, H, N, dk, dv, effective_chunk(N, chunk), dtype);
+  if (p.total > ret::kScratchBytes) return RET_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if (p.total > 0 && ret::scratch_pointer(&ws) != hipSuccess) return RET_ERR_HIP;
+  return retention_chunkwise(q, k, v, gamma_host, o, B, H, N, dk, dv, chunk, dtype, state_in, state_out, gn, ws,
+                             ws ? ret::kScratchBytes : 0, stream);
 }
 
 int retention_chunk_states(const void* k, const void* v, const float* gamma_host, int B, int H, int N, int dk,

@@ -89,6 +89,14 @@ hipError_t launch_mfma_chunk_out(const uint16_t* q, const uint16_t* k, const uin
 // Whether the MFMA kernels implement these sizes.
 bool mfma_supports(int dk, int dv);
 
+// Bytes of the library-owned device scratch (scratch.hip) that the
+// allocation-free chunkwise entry point uses instead of a caller workspace.
+constexpr size_t kScratchBytes = size_t{64} << 20;
+
+// Device address of this GPU's copy of the scratch (the current device's),
+// looked up with hipGetSymbolAddress on the first call per device and kept.
+hipError_t scratch_pointer(void** out);
+
 // Backward-pass data movement (d.B, d.H, d.N are used; rows are tokens).
 // split_rows: src [B*H, N, D] read once, written to up to three targets, each
 // cut into parts of width part_w (the last may be narrower), part p at
