@@ -105,6 +105,26 @@ def two_stage_design_bytes(B, H, N, chunk, dk=DK, dv=DV):
             + float(B * H * dk * dv * 4))
 
 
+def single_pass_design_bytes(B, H, N, dk=DK, dv=DV):
+    """Bytes the single-pass kernel's workgroups request: each (head, 256-column
+    v tile) reads Q and K whole and its V columns, and writes its O columns and
+    its columns of the final fp32 state. Q and K are requested once per v tile
+    (the v tiles of a head share an XCD, so the repeat is meant to hit L2)."""
+    nvt = dv // 256
+    return float(B * H * N * (nvt * 2 * dk + 2 * dv) * 2 + B * H * dk * dv * 4)
+
+
+def single_pass_executed_flops(B, H, N, chunk, dk=DK, dv=DV):
+    """Flops the single-pass kernel executes: the method's, with the scores of
+    every 64-row query block against whole 32-key blocks up to its end
+    (computed by each of the dv/256 v tiles) and the products with V over whole
+    blocks, for N a multiple of the chunk and the chunk a multiple of 64."""
+    nvt = dv // 256
+    per_chunk_keys = sum(64 * (qb * 64 + 64) for qb in range(chunk // 64))
+    per_token = per_chunk_keys / chunk
+    return float(B * H * N * (per_token * 2 * dk * nvt + per_token * 2 * dv + 4 * dk * dv))
+
+
 def roofline_fracs(flop, nbytes, seconds):
     """Fractions of the binding roof min(MFMA peak, AI * HBM peak), of HBM
     bandwidth and of the MFMA peak, for method flops and bytes over a time."""
@@ -143,6 +163,7 @@ def measured_traffic():
     None.
     """
     current = {
+        "fused": _source_hash(["fused.hip", "mfma_tiles.h", "common.h", "../build.py"]),
         "chunk_out": _source_hash(["mfma_out.hip", "mfma_tiles.h", "common.h", "../build.py"]),
         "chunk_out_gated": _source_hash(["mfma_out.hip", "mfma_tiles.h", "common.h", "../build.py"]),
         "state_walk": _source_hash(["mfma.hip", "mfma_tiles.h", "common.h", "../build.py"]),
@@ -448,6 +469,52 @@ def backward_pass(ret, torch, dev, stream, qd, kd, vd, gamma, steps, warmup=3):
     }
 
 
+SINGLE_PASS_CHUNKS = (64, 128)
+
+
+def single_pass_prefill(ret, torch, dev, stream, qd, kd, vd, gamma, state, out, gn, steps, warmup=10):
+    """The headline shape at the chunk lengths that plan the single-pass
+    kernel (retention_chunkwise, one launch after a small zeroing kernel).
+    The chunk length changes only the blocking of the same retention (every
+    chunk length gives the same outputs up to rounding) and the method's flop
+    count; these are not the headline configuration, whose chunk is 512."""
+    B, H, N = qd.shape[0], qd.shape[1], qd.shape[2]
+    res = {}
+    for C in SINGLE_PASS_CHUNKS:
+        ws = torch.empty(max(ret.chunkwise_workspace_bytes(B, H, N, DK, DV, C), 1), dtype=torch.uint8, device=dev)
+        assert ret.chunkwise_workspace_bytes(B, H, N, DK, DV, C) == B * H * (DV // 256) * 2048, "not the single pass"
+
+        def step():
+            ret.chunkwise(qd, kd, vd, gamma, C, state_out=state, gn=gn, out=out, workspace=ws)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        flop = algorithmic_flops(B, H, N, C)
+        mbytes = method_bytes(B, H, N)
+        res[f"chunk_{C}"] = {
+            "ms_per_step": ms,
+            "tokens_per_s": B * N / (ms * 1e-3),
+            "hbm_frac_of_method_bytes": mbytes / (ms * 1e-3) / PEAK_HBM,
+            "method_flop": flop,
+            "mfma_frac_of_method_flop": flop / (ms * 1e-3) / PEAK_BF16,
+            "executed_flop": single_pass_executed_flops(B, H, N, C),
+            "design_bytes": single_pass_design_bytes(B, H, N),
+        }
+        del ws
+    res["kernel"] = "fused_chunk_kernel (retention_chunkwise at chunk 64 and 128: read-out, intra-chunk products, " \
+                    "state update, GroupNorm and state out in one launch)"
+    res["traffic_chunk_64"] = measured_traffic()["fused"]
+    return res
+
+
 def gated_prefill(ret, torch, dev, stream, qd, kd, vd, gamma, ws, state, out, gn, steps, warmup=5):
     """The same prefill with the gated epilogue, swish(gate) * GroupNorm(O).
 
@@ -514,6 +581,8 @@ def main():
     ap.add_argument("--skip-decode-b32", action="store_true", help="skip the cache-defeating B=32 decode timing")
     ap.add_argument("--skip-gated", action="store_true", help="skip the swish-gated prefill timing")
     ap.add_argument("--skip-backward", action="store_true", help="skip the backward-pass timing")
+    ap.add_argument("--skip-single-pass", action="store_true",
+                    help="skip the single-pass kernel timings at chunks 64 and 128")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -574,6 +643,11 @@ def main():
     if not args.skip_gated:
         print(f"[bench] timing {args.steps} swish-gated prefill steps", file=sys.stderr, flush=True)
         gated = gated_prefill(ret, torch, dev, stream, qd, kd, vd, gamma, ws, state, out, gn, args.steps)
+
+    single_pass = None
+    if not args.skip_single_pass:
+        print(f"[bench] timing the single-pass kernel at chunks {SINGLE_PASS_CHUNKS}", file=sys.stderr, flush=True)
+        single_pass = single_pass_prefill(ret, torch, dev, stream, qd, kd, vd, gamma, state, out, gn, args.steps)
 
     backward = None
     if not args.skip_backward:
@@ -721,6 +795,7 @@ def main():
             "traffic": traffic["state_walk"],
         },
         "gated": gated,
+        "single_pass": single_pass,
         "backward": backward,
         "decode": {
             "steps": T,

@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define RETENTION_ABI_VERSION 2
+#define RETENTION_ABI_VERSION 3
 #define RETENTION_MAX_HEADS 256
 #define RETENTION_MAX_DK 256
 #define RETENTION_MAX_DV 1024
@@ -112,10 +112,23 @@ int retention_parallel(const void* q, const void* k, const void* v,
 
 /*
  * Bytes of device workspace retention_chunkwise needs for these sizes
- * (a pure function of its arguments; 0 for invalid sizes).
+ * (a pure function of its arguments; 0 for invalid sizes). Where the
+ * single-pass kernel applies (bf16, dk 128 or 256, dv a multiple of 256 up to
+ * 1024, chunk 64 or 128 after clamping to N, and at least 192 (head,
+ * 256-column v tile) pairs) this is only the GroupNorm exchange: 2 KiB per
+ * (head, 256-column v tile). Otherwise it holds a state per chunk (the
+ * two-stage path, retention_chunk_stages_workspace_bytes).
  */
 size_t retention_chunkwise_workspace_bytes(int B, int H, int N, int dk, int dv,
                                            int chunk, int dtype);
+
+/*
+ * Bytes of device workspace the two stage entry points below need: the bf16
+ * (fp32 for fp32 inputs) state carried into every chunk, plus segment end
+ * states when the walk is cut into segments.
+ */
+size_t retention_chunk_stages_workspace_bytes(int B, int H, int N, int dk, int dv,
+                                              int chunk, int dtype);
 
 /*
  * Chunkwise recurrent form ("RetNet - Retentive Network ...", Key Equations,
@@ -173,8 +186,8 @@ int retention_chunkwise_noalloc(const void* q, const void* k, const void* v,
  * chunk and dtype; has_state_in must be non-zero exactly when that call had a
  * state_in. Applies the optional GroupNorm.
  *
- * The workspace (at least retention_chunkwise_workspace_bytes(...) bytes) is
- * opaque; its contents are only meaningful between these two calls.
+ * The workspace (at least retention_chunk_stages_workspace_bytes(...) bytes)
+ * is opaque; its contents are only meaningful between these two calls.
  */
 int retention_chunk_states(const void* k, const void* v, const float* gamma_host,
                            int B, int H, int N, int dk, int dv, int chunk, int dtype,

@@ -28,6 +28,7 @@ __all__ = [
     "chunk_output",
     "recurrent_step",
     "chunkwise_workspace_bytes",
+    "chunk_stages_workspace_bytes",
     "chunkwise_backward",
     "chunkwise_backward_workspace_bytes",
     "RetentionError",
@@ -201,6 +202,12 @@ def chunkwise_workspace_bytes(B, H, N, dk, dv, chunk, dtype=torch.bfloat16) -> i
     return int(_lib.load().retention_chunkwise_workspace_bytes(B, H, N, dk, dv, int(chunk), code))
 
 
+def chunk_stages_workspace_bytes(B, H, N, dk, dv, chunk, dtype=torch.bfloat16) -> int:
+    """Workspace bytes of chunk_states / chunk_output (the state of every chunk)."""
+    code = _lib.RET_BF16 if dtype == torch.bfloat16 else _lib.RET_F32
+    return int(_lib.load().retention_chunk_stages_workspace_bytes(B, H, N, dk, dv, int(chunk), code))
+
+
 def chunkwise(q, k, v, gamma: GammaLike, chunk: int, state_in=None, state_out: Union[bool, torch.Tensor] = False,
               gn: Optional[GroupNorm] = None, out=None, workspace=None, gate=None):
     """Chunkwise recurrent form. Returns (o, state_out or None).
@@ -270,7 +277,7 @@ def chunkwise_noalloc(q, k, v, gamma: GammaLike, chunk: int, out, state_in=None,
 def chunk_states(k, v, gamma: GammaLike, chunk: int, workspace, state_in=None, state_out=None):
     """First stage of the chunkwise form: the state carried into every chunk, kept in ``workspace``.
 
-    ``workspace`` is a device uint8 tensor of at least chunkwise_workspace_bytes(...)
+    ``workspace`` is a device uint8 tensor of at least chunk_stages_workspace_bytes(...)
     bytes; ``state_out`` (optional fp32 [B,H,dk,dv]) receives the final state.
     """
     B, H, N, dk, dv, dt = _check_qkv(k, k, v)
@@ -278,7 +285,7 @@ def chunk_states(k, v, gamma: GammaLike, chunk: int, workspace, state_in=None, s
     state_out = _state(state_out, "state_out", B, H, dk, dv, k.device)
     lib = _lib.load()
     _require_workspace(workspace, "workspace",
-                       int(lib.retention_chunkwise_workspace_bytes(B, H, N, dk, dv, int(chunk), dt)), k.device)
+                       int(lib.retention_chunk_stages_workspace_bytes(B, H, N, dk, dv, int(chunk), dt)), k.device)
     g = _gamma_array(gamma, H)
     rc = lib.retention_chunk_states(
         k.data_ptr(), v.data_ptr(), g, B, H, N, dk, dv, int(chunk), dt,
@@ -301,7 +308,7 @@ def chunk_output(q, k, v, gamma: GammaLike, chunk: int, workspace, has_state_in:
     _no_overlap(out, "out", q, k, v, workspace)
     lib = _lib.load()
     _require_workspace(workspace, "workspace",
-                       int(lib.retention_chunkwise_workspace_bytes(B, H, N, dk, dv, int(chunk), dt)), q.device)
+                       int(lib.retention_chunk_stages_workspace_bytes(B, H, N, dk, dv, int(chunk), dt)), q.device)
     g = _gamma_array(gamma, H)
     gn_p, _keep = _gn_struct(gn, H, dv, q.device, gate, out)
     rc = lib.retention_chunk_output(

@@ -23,6 +23,7 @@ EXPORTED = (
     "retention_status_string",
     "retention_parallel",
     "retention_chunkwise_workspace_bytes",
+    "retention_chunk_stages_workspace_bytes",
     "retention_chunkwise",
     "retention_chunkwise_noalloc",
     "retention_chunk_states",
@@ -34,7 +35,7 @@ EXPORTED = (
 
 
 # RETENTION_ABI_VERSION of include/retention.h that the structures here mirror.
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class GnStruct(ctypes.Structure):
@@ -74,6 +75,8 @@ def open_library(path):
     lib.retention_parallel.restype = i
     lib.retention_chunkwise_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.retention_chunkwise_workspace_bytes.restype = ctypes.c_size_t
+    lib.retention_chunk_stages_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.retention_chunk_stages_workspace_bytes.restype = ctypes.c_size_t
     lib.retention_chunkwise.argtypes = [vp, vp, vp, f_p, vp, i, i, i, i, i, i, i, vp, vp, gn_p, vp,
                                         ctypes.c_size_t, vp]
     lib.retention_chunkwise.restype = i

@@ -25,6 +25,14 @@ static_assert(ret::kScratchBytes == RETENTION_NOALLOC_MAX_WORKSPACE_BYTES, "scra
 constexpr size_t kAlign = 256;
 constexpr int kMfmaRows = 64;            // MFMA kernels need chunk % 64 == 0
 constexpr int64_t kWalkTargetBlocks = 512;  // segment the walk below this many workgroups
+// The single-pass kernel runs one workgroup per (head, 256-column v tile);
+// below this many of them the two-stage path, which parallelises over query
+// blocks, keeps more of the GPU busy.
+constexpr int64_t kFusedMinUnits = 192;
+// Above this chunk length the single pass re-reads each chunk's keys and
+// values once per 64-row query block (its state takes the registers a
+// longer block would need) and measures slower than the two stages.
+constexpr int kFusedMaxChunk = 128;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -81,8 +89,10 @@ int effective_chunk(int N, int chunk) {
   return static_cast<int>(std::min<int64_t>(chunk, up <= INT_MAX ? up : N));
 }
 
-// Chunkwise execution plan.
+// Chunkwise execution plan: the single-pass kernel (fused), or the two stages
+// (state walk, then output) on the MFMA or the generic kernels.
 struct ChunkPlan {
+  bool fused;
   bool mfma;
   int nchunks;
   int chunks_per_seg;
@@ -92,8 +102,21 @@ struct ChunkPlan {
   size_t total;
 };
 
-ChunkPlan plan_chunkwise(int B, int H, int N, int dk, int dv, int chunk, int dtype) {
+bool use_fused(int B, int H, int dk, int dv, int chunk, int dtype) {
+  return dtype == RET_BF16 && chunk <= kFusedMaxChunk && ret::fused_supports(dk, dv, chunk) &&
+         static_cast<int64_t>(B) * H * (dv / 256) >= kFusedMinUnits;
+}
+
+// `stages`: plan the two stages even where the single-pass kernel applies
+// (the explicit stage entry points).
+ChunkPlan plan_chunkwise(int B, int H, int N, int dk, int dv, int chunk, int dtype, bool stages = false) {
   ChunkPlan p{};
+  if (!stages && use_fused(B, H, dk, dv, chunk, dtype)) {
+    p.fused = true;
+    p.nchunks = static_cast<int>((static_cast<int64_t>(N) + chunk - 1) / chunk);
+    p.total = ret::fused_workspace_bytes(static_cast<int64_t>(B) * H, dv);
+    return p;
+  }
   p.mfma = dtype == RET_BF16 && ret::mfma_supports(dk, dv) && chunk % kMfmaRows == 0;
   p.nchunks = static_cast<int>((static_cast<int64_t>(N) + chunk - 1) / chunk);
   const size_t heads = static_cast<size_t>(B) * H;
@@ -120,7 +143,7 @@ ChunkPlan plan_chunkwise(int B, int H, int N, int dk, int dv, int chunk, int dty
 // Shared validation of the chunkwise entry points (no HIP calls).
 int check_chunkwise(const float* gamma_host, int B, int H, int N, int dk, int dv, int* chunk, int dtype,
                     const retention_gn_t* gn, const void* workspace, size_t workspace_bytes, GnArgs* g,
-                    ChunkPlan* plan, HeadDecay* decay) {
+                    ChunkPlan* plan, HeadDecay* decay, bool stages = false) {
   if (*chunk <= 0) return RET_ERR_INVALID_ARG;
   int st = check_sizes(B, H, N, dk, dv, dtype);
   if (st != RET_OK) return st;
@@ -129,7 +152,7 @@ int check_chunkwise(const float* gamma_host, int B, int H, int N, int dk, int dv
   if (st != RET_OK) return st;
   st = check_gn(gn, g);
   if (st != RET_OK) return st;
-  *plan = plan_chunkwise(B, H, N, dk, dv, *chunk, dtype);
+  *plan = plan_chunkwise(B, H, N, dk, dv, *chunk, dtype, stages);
   if (plan->total > 0 && (!workspace || workspace_bytes < plan->total)) return RET_ERR_INVALID_ARG;
   check_gamma(gamma_host, H, decay);
   return RET_OK;
@@ -211,14 +234,26 @@ BackwardPlan plan_backward(int B, int H, int N, int dk, int dv, int chunk, int d
   return p;
 }
 
-// One retention (both chunkwise stages) for the backward pass: no GroupNorm.
+// One chunkwise retention as planned: the single-pass kernel, or both stages.
+int run_chunkwise(const ChunkPlan& p, const void* q, const void* k, const void* v, void* o, const float* state_in,
+                  float* state_out, const Dims& d, int chunk, int dtype, const HeadDecay& decay, const GnArgs& g,
+                  char* ws, hipStream_t s, bool accumulate = false) {
+  if (p.fused) {
+    return status_of(ret::launch_fused_chunkwise(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                                 static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), state_in,
+                                                 state_out, ws, d, chunk, decay, g, accumulate, s));
+  }
+  if (launch_states(p, k, v, state_in, state_out, ws, d, chunk, dtype, decay, s) != hipSuccess) return RET_ERR_HIP;
+  return status_of(launch_output(p, q, k, v, o, ws, state_in != nullptr, d, chunk, dtype, decay, g, s, accumulate));
+}
+
+// One retention for the backward pass: no GroupNorm.
 int run_retention(const void* q, const void* k, const void* v, void* o, const float* state_in, float* state_out,
                   const Dims& d, int chunk, int dtype, const HeadDecay& decay, char* cw, hipStream_t s,
                   bool accumulate = false) {
   const ChunkPlan p = plan_chunkwise(d.B, d.H, d.N, d.dk, d.dv, chunk, dtype);
   GnArgs none{};
-  if (launch_states(p, k, v, state_in, state_out, cw, d, chunk, dtype, decay, s) != hipSuccess) return RET_ERR_HIP;
-  return status_of(launch_output(p, q, k, v, o, cw, state_in != nullptr, d, chunk, dtype, decay, none, s, accumulate));
+  return run_chunkwise(p, q, k, v, o, state_in, state_out, d, chunk, dtype, decay, none, cw, s, accumulate);
 }
 
 }  // namespace
@@ -265,6 +300,11 @@ size_t retention_chunkwise_workspace_bytes(int B, int H, int N, int dk, int dv, 
   return plan_chunkwise(B, H, N, dk, dv, effective_chunk(N, chunk), dtype).total;
 }
 
+size_t retention_chunk_stages_workspace_bytes(int B, int H, int N, int dk, int dv, int chunk, int dtype) {
+  if (check_sizes(B, H, N, dk, dv, dtype) != RET_OK || chunk <= 0) return 0;
+  return plan_chunkwise(B, H, N, dk, dv, effective_chunk(N, chunk), dtype, true).total;
+}
+
 int retention_chunkwise(const void* q, const void* k, const void* v, const float* gamma_host, void* o, int B, int H,
                         int N, int dk, int dv, int chunk, int dtype, const float* state_in, float* state_out,
                         const retention_gn_t* gn, void* workspace, size_t workspace_bytes, void* stream) {
@@ -276,10 +316,8 @@ int retention_chunkwise(const void* q, const void* k, const void* v, const float
                                  &decay);
   if (st != RET_OK) return st;
   const Dims d{B, H, N, dk, dv};
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  if (launch_states(p, k, v, state_in, state_out, ws, d, chunk, dtype, decay, s) != hipSuccess) return RET_ERR_HIP;
-  return status_of(launch_output(p, q, k, v, o, ws, state_in != nullptr, d, chunk, dtype, decay, g, s));
+  return run_chunkwise(p, q, k, v, o, state_in, state_out, d, chunk, dtype, decay, g, static_cast<char*>(workspace),
+                       static_cast<hipStream_t>(stream));
 }
 
 int retention_chunkwise_noalloc(const void* q, const void* k, const void* v, const float* gamma_host, void* o, int B,
@@ -311,7 +349,7 @@ int retention_chunk_states(const void* k, const void* v, const float* gamma_host
   ChunkPlan p;
   HeadDecay decay;
   const int st = check_chunkwise(gamma_host, B, H, N, dk, dv, &chunk, dtype, nullptr, workspace, workspace_bytes, &g,
-                                 &p, &decay);
+                                 &p, &decay, true);
   if (st != RET_OK) return st;
   const Dims d{B, H, N, dk, dv};
   return status_of(launch_states(p, k, v, state_in, state_out, static_cast<char*>(workspace), d, chunk, dtype, decay,
@@ -326,7 +364,7 @@ int retention_chunk_output(const void* q, const void* k, const void* v, const fl
   ChunkPlan p;
   HeadDecay decay;
   const int st = check_chunkwise(gamma_host, B, H, N, dk, dv, &chunk, dtype, gn, workspace, workspace_bytes, &g, &p,
-                                 &decay);
+                                 &decay, true);
   if (st != RET_OK) return st;
   const Dims d{B, H, N, dk, dv};
   return status_of(launch_output(p, q, k, v, o, static_cast<const char*>(workspace), has_state_in != 0, d, chunk,

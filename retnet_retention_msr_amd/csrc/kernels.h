@@ -89,6 +89,17 @@ hipError_t launch_mfma_chunk_out(const uint16_t* q, const uint16_t* k, const uin
 // Whether the MFMA kernels implement these sizes.
 bool mfma_supports(int dk, int dv);
 
+// Single-pass chunkwise kernel (fused.hip): one workgroup per (head, 256-column
+// v tile) walks the chunks with its state slab in registers; GroupNorm
+// statistics are exchanged between the v tiles of a head through a small
+// workspace (fused_workspace_bytes). Covers dk 128 and 256, dv a multiple of
+// 256 up to 1024, chunk a multiple of 64.
+bool fused_supports(int dk, int dv, int chunk);
+size_t fused_workspace_bytes(int64_t heads, int dv);
+hipError_t launch_fused_chunkwise(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                                  const float* state_in, float* state_out, void* workspace, const Dims& d, int chunk,
+                                  const HeadDecay& decay, const GnArgs& gn, bool accumulate, hipStream_t stream);
+
 // Bytes of the library-owned device scratch (scratch.hip) that the
 // allocation-free chunkwise entry point uses instead of a caller workspace.
 constexpr size_t kScratchBytes = size_t{64} << 20;

@@ -44,4 +44,18 @@ int walk_tiles_per_head(int64_t heads, int dk, int dv) {
   return (dk / (32 * walk_k_tiles(dk))) * (dv / kWalkNarrowVT);
 }
 
+// The single-pass kernel: dk 128 or 256 (its state slab, 32 columns by dk
+// rows per wave, fits the register budget), v tiles of 256 columns (at most
+// four per head: the GroupNorm merge), query blocks of 64 rows.
+bool fused_supports(int dk, int dv, int chunk) {
+  return (dk == 128 || dk == 256) && dv % 256 == 0 && dv / 256 <= 4 && chunk % 64 == 0;
+}
+
+// Its workspace: per (head, v tile) two mailbox slots of 64 rows, each row
+// two tagged 64-bit words (mean, sum of squared deviations): 2 KiB.
+size_t fused_workspace_bytes(int64_t heads, int dv) {
+  const size_t units = static_cast<size_t>(heads) * (dv / 256);
+  return units * 2 * 64 * 2 * sizeof(uint64_t);
+}
+
 }  // namespace ret

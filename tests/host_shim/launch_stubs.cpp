@@ -53,6 +53,11 @@ hipError_t launch_state_prep(const float*, float*, int, int, int, int, bool, int
   return record();
 }
 
+hipError_t launch_fused_chunkwise(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, const float*, float*,
+                                  void*, const Dims&, int, const HeadDecay&, const GnArgs&, bool, hipStream_t) {
+  return record();
+}
+
 // The scratch lookup hands out a fake address (never dereferenced: the
 // launchers above touch nothing).
 hipError_t scratch_pointer(void** out) {

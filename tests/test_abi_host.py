@@ -56,7 +56,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.retention_abi_version() == _lib.ABI_VERSION == 2
+    assert lib.retention_abi_version() == _lib.ABI_VERSION == 3
     assert _lib.status_string(0) == "ok"
     assert _lib.status_string(-1) == "invalid argument"
     assert _lib.status_string(-2) == "unsupported arguments"
@@ -139,22 +139,42 @@ def test_recurrent_step_rejects_invalid_arguments(lib):
 
 def test_workspace_bytes(lib):
     ws = lib.retention_chunkwise_workspace_bytes
-    # bf16 MFMA path, 6.7B-shaped prefill: one bf16 [dv][dk] state per chunk and head, no segments.
-    assert ws(8, 16, 8192, 256, 512, 512, 1) == 8 * 16 * 16 * 256 * 512 * 2
-    # fp32 path: one fp32 state per chunk and head.
-    assert ws(1, 1, 64, 16, 16, 16, 0) == 4 * 16 * 16 * 4
-    # Long sequence with 16 heads: the walk is cut into segments whose fp32 end states follow the chunk states.
+    st = lib.retention_chunk_stages_workspace_bytes
+    # The 6.7B-shaped prefill at chunks of 64 or 128 runs the single-pass
+    # kernel: its workspace is only the GroupNorm exchange, two slots per
+    # (head, 256-column v tile) of 64 rows of two tagged 64-bit words (mean,
+    # sum of squared deviations): 2 KiB.
+    units = 8 * 16 * 2
+    assert ws(8, 16, 8192, 256, 512, 128, 1) == units * 2048
+    # It does not grow with the sequence or with the chunk length.
+    assert ws(8, 16, 65536, 256, 512, 64, 1) == ws(8, 16, 8192, 256, 512, 128, 1)
+    # dk 128, dv 1024 (four v tiles).
+    assert ws(4, 16, 4096, 128, 1024, 64, 1) == 256 * 2048
+    # A chunk past 128 is clamped to the sequence first: N = 100 takes chunk 128.
+    assert ws(8, 16, 100, 256, 512, 512, 1) == units * 2048
+    # Longer chunks plan the two stages, whose entry points keep one bf16 state
+    # per chunk and head (no segments here).
+    assert st(8, 16, 8192, 256, 512, 512, 1) == 8 * 16 * 16 * 256 * 512 * 2
+    assert ws(8, 16, 8192, 256, 512, 512, 1) == st(8, 16, 8192, 256, 512, 512, 1)
+    assert ws(8, 16, 8192, 256, 512, 256, 1) == st(8, 16, 8192, 256, 512, 256, 1)
+    # Few heads (the single-pass kernel would leave most of the GPU idle): the
+    # two-stage path and its chunk states, cut into segments whose fp32 end
+    # states follow the chunk states.
     n = ws(1, 16, 65536, 256, 512, 512, 1)
     chunk_states = 16 * 128 * 256 * 512 * 2
+    assert n == st(1, 16, 65536, 256, 512, 512, 1)
     assert n > chunk_states and (n - chunk_states) % (16 * 256 * 512 * 4) == 0
+    # fp32 path: one fp32 state per chunk and head.
+    assert ws(1, 1, 64, 16, 16, 16, 0) == 4 * 16 * 16 * 4
     # Invalid sizes give 0.
     assert ws(0, 16, 8192, 256, 512, 512, 1) == 0
     assert ws(1, 16, 8192, 256, 512, 0, 1) == 0
+    assert st(0, 16, 8192, 256, 512, 512, 1) == 0
 
 
 def test_chunk_stage_entry_points_validate(lib):
     g = _gamma([0.9, 0.8])
-    need = lib.retention_chunkwise_workspace_bytes(1, 2, 256, 64, 128, 64, 1)
+    need = lib.retention_chunk_stages_workspace_bytes(1, 2, 256, 64, 128, 64, 1)
     # states: null k, bad chunk, short workspace, bad gamma
     assert lib.retention_chunk_states(None, FAKE, g, 1, 2, 256, 64, 128, 64, 1, None, None, FAKE, need, None) == -1
     assert lib.retention_chunk_states(FAKE, FAKE, g, 1, 2, 256, 64, 128, 0, 1, None, None, FAKE, need, None) == -1

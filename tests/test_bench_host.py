@@ -34,7 +34,7 @@ def test_more_than_one_gpu_is_refused():
 
 def test_measured_traffic_is_keyed_by_kernel_source():
     t = bench.measured_traffic()
-    assert set(t) == {"chunk_out", "chunk_out_gated", "state_walk", "decode_step"}
+    assert set(t) == {"fused", "chunk_out", "chunk_out_gated", "state_walk", "decode_step"}
     for v in t.values():
         assert v is None or v > 0
 
@@ -75,3 +75,16 @@ def test_two_stage_design_bytes():
     assert bench.two_stage_design_bytes(B, H, N, 512) == expect
     assert bench.chunk_state_bytes(B, H, N, 512) == B * H * 15 * st
     assert bench.chunk_state_bytes(B, H, N, 512, state_in=True) == B * H * 16 * st
+
+
+def test_single_pass_design_bytes_and_executed_flops():
+    B, H, N = 8, 16, 8192
+    # Each of the two 256-column v tiles of a head reads Q and K whole: (2*2*256 + 2*512) * 2 B per token-head,
+    # plus the fp32 final state.
+    assert bench.single_pass_design_bytes(B, H, N) == 4096 * B * H * N + B * H * 256 * 512 * 4
+    # Scores and values over whole 32-key blocks up to each 64-row block's end: 64 keys per query at chunk 64
+    # (against 32.5 for the causal half), 96 at chunk 128, 288 at chunk 512; scores once per v tile.
+    for C, keys in ((64, 64), (128, 96), (512, 288)):
+        per = keys * (2 * 256 * 2 + 2 * 512) + 4 * 256 * 512
+        assert bench.single_pass_executed_flops(B, H, N, C) == per * B * H * N
+        assert bench.single_pass_executed_flops(B, H, N, C) > bench.algorithmic_flops(B, H, N, C)

@@ -1,0 +1,195 @@
+"""GPU parity of the single-pass chunkwise kernel against the fp64 oracle.
+
+retention_chunkwise takes the single-pass kernel (one workgroup per head and
+256-column v tile walking the chunks with its state in registers, GroupNorm
+statistics exchanged between the v tiles of a head) for bf16, dk 128 or 256,
+dv a multiple of 256, chunk 64 or 128 (after clamping to the sequence), once
+heads times v tiles reach 192. Every case here has that many, so every
+chunkwise call below runs it (the workspace size, checked first, says which
+path was planned); longer chunks plan the two stages. Outputs and
+states are compared element by element with the oracle, per (b, h) slice at
+2e-2 * max|o|. Cases: ragged tails and several chunk lengths, state in and
+out (aliased too), GroupNorm with and without affine, the swish gate, dk 128
+with one v tile, dv 1024 with four, sequences shorter than a block, extreme
+decays, agreement with the two-stage entry points, and a backward pass whose
+retentions all take this kernel.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import retnet_retention_msr_amd as ret
+from oracle import retention_oracle as orc
+from retnet_retention_msr_amd import synthetic
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = 2e-2
+
+
+def _np(t):
+    return t.detach().to("cpu").double().numpy()
+
+
+def _check(got, ref, what=""):
+    got = _np(got) if isinstance(got, torch.Tensor) else np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), what
+    for b in range(ref.shape[0]):
+        for h in range(ref.shape[1]):
+            scale = float(np.max(np.abs(ref[b, h])))
+            err = float(np.max(np.abs(got[b, h] - ref[b, h])))
+            assert err <= TOL * max(scale, 1e-30), f"{what} b={b} h={h}: err {err:.3e} > {TOL} * {scale:.3e}"
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _is_single_pass(B, H, N, dk, dv, C):
+    """The plan: the single-pass kernel's workspace is the GroupNorm exchange only."""
+    units = B * H * (dv // 256)
+    return ret.chunkwise_workspace_bytes(B, H, N, dk, dv, C) == units * 2048
+
+
+CASES = [
+    # B, H, N, dk, dv, chunk, gn, affine, state
+    (6, 16, 600, 256, 512, 128, True, True, True),     # ragged last chunk (64 + 24 rows), state in/out
+    (6, 16, 200, 256, 512, 128, True, False, False),   # one full chunk and a 72-row tail
+    (6, 16, 1000, 256, 512, 128, False, False, True),  # many chunks, ragged last chunk, no GroupNorm
+    (12, 16, 384, 128, 256, 64, True, True, True),     # dk 128, one v tile (no exchange), chunk 64
+    (3, 16, 512, 256, 1024, 128, True, True, False),   # four v tiles
+    (6, 16, 200, 256, 512, 64, True, False, True),     # chunk 64, N not a multiple of 32
+]
+
+
+@pytest.mark.parametrize("B, H, N, dk, dv, C, gn_on, affine, with_state", CASES)
+def test_single_pass_matches_oracle(B, H, N, dk, dv, C, gn_on, affine, with_state):
+    _announce(f"single pass B={B} H={H} N={N} dk={dk} dv={dv} chunk={C} gn={gn_on} affine={affine} "
+              f"state={with_state}")
+    assert _is_single_pass(B, H, N, dk, dv, C)
+    q, k, v = synthetic.make_qkv(B, H, N, dk, dv, dtype=torch.bfloat16, seed=3000 + N + C)
+    g = synthetic.head_gammas(H)
+    S0 = synthetic.make_state(B, H, dk, dv, seed=3001 + N, std=0.5) if with_state else None
+    w = b = None
+    if affine:
+        w, b = synthetic.make_gn_affine(H, dv, seed=3002)
+    gn = ret.GroupNorm(1e-5, w.to(DEV) if w is not None else None, b.to(DEV) if b is not None else None) \
+        if gn_on else None
+    raw, S_ref = orc.chunkwise(q, k, v, g, C, state_in=S0)
+    ref = orc.group_norm(raw, eps=1e-5, weight=w, bias=b) if gn_on else raw
+    o, S = ret.chunkwise(q.to(DEV), k.to(DEV), v.to(DEV), g, C, state_in=None if S0 is None else S0.to(DEV),
+                         state_out=True, gn=gn)
+    torch.cuda.synchronize()
+    _check(o, ref, "o")
+    _check(S, S_ref, "state")
+
+
+def test_single_pass_gated():
+    B, H, N, dk, dv, C = 6, 16, 640, 256, 512, 128
+    _announce(f"single pass gated B={B} H={H} N={N} chunk={C}")
+    assert _is_single_pass(B, H, N, dk, dv, C)
+    q, k, v = synthetic.make_qkv(B, H, N, dk, dv, dtype=torch.bfloat16, seed=3100)
+    g = synthetic.head_gammas(H)
+    gate = synthetic.make_gate((B, H, N, dv), dtype=torch.bfloat16, seed=3101)
+    w, b = synthetic.make_gn_affine(H, dv, seed=3102)
+    raw, _ = orc.chunkwise(q, k, v, g, C)
+    ref = orc.gated_group_norm(raw, _np(gate), eps=1e-5, weight=w, bias=b)
+    o, _ = ret.chunkwise(q.to(DEV), k.to(DEV), v.to(DEV), g, C, gn=ret.GroupNorm(1e-5, w.to(DEV), b.to(DEV)),
+                         gate=gate.to(DEV))
+    torch.cuda.synchronize()
+    _check(o, ref, "gated o")
+
+
+@pytest.mark.parametrize("N", [1, 31, 64, 65])
+def test_single_pass_short_sequences_with_state(N):
+    """A chunk of 512 is clamped to the sequence (at most 128 rows here), so
+    these take the single pass."""
+    B, H, dk, dv, C = 6, 16, 256, 512, 512
+    _announce(f"single pass short N={N}")
+    assert _is_single_pass(B, H, N, dk, dv, C)
+    q, k, v = synthetic.make_qkv(B, H, N, dk, dv, dtype=torch.bfloat16, seed=3200 + N)
+    g = synthetic.head_gammas(H)
+    S0 = synthetic.make_state(B, H, dk, dv, seed=3201, std=0.5)
+    raw, S_ref = orc.chunkwise(q, k, v, g, C, state_in=S0)
+    Sd = S0.to(DEV)
+    # state_out aliases state_in.
+    o, S = ret.chunkwise(q.to(DEV), k.to(DEV), v.to(DEV), g, C, state_in=Sd, state_out=Sd, gn=ret.GroupNorm(1e-5))
+    torch.cuda.synchronize()
+    _check(o, orc.group_norm(raw, eps=1e-5), "o")
+    _check(S, S_ref, "state")
+
+
+def test_single_pass_extreme_decays():
+    B, H, N, dk, dv, C = 6, 16, 384, 256, 512, 128
+    _announce("single pass extreme decays")
+    assert _is_single_pass(B, H, N, dk, dv, C)
+    q, k, v = synthetic.make_qkv(B, H, N, dk, dv, dtype=torch.bfloat16, seed=3300)
+    g = torch.tensor([1e-6, 1 - 2.0 ** -20, 0.05, 0.5, 0.3, 0.999] + [0.9] * 10, dtype=torch.float32)
+    S0 = synthetic.make_state(B, H, dk, dv, seed=3301, std=0.5)
+    raw, S_ref = orc.chunkwise(q, k, v, g, C, state_in=S0)
+    o, S = ret.chunkwise(q.to(DEV), k.to(DEV), v.to(DEV), g, C, state_in=S0.to(DEV), state_out=True,
+                         gn=ret.GroupNorm(1e-5))
+    torch.cuda.synchronize()
+    _check(o, orc.group_norm(raw, eps=1e-5), "o")
+    _check(S, S_ref, "state")
+
+
+def test_single_pass_agrees_with_the_two_stage_path():
+    B, H, N, dk, dv, C = 6, 16, 1024, 256, 512, 128
+    _announce("single pass vs two stages")
+    assert _is_single_pass(B, H, N, dk, dv, C)
+    q, k, v = (t.to(DEV) for t in synthetic.make_qkv(B, H, N, dk, dv, dtype=torch.bfloat16, seed=3400))
+    g = synthetic.head_gammas(H)
+    gn = ret.GroupNorm(1e-5)
+    o1, S1 = ret.chunkwise(q, k, v, g, C, state_out=True, gn=gn)
+    ws = torch.empty(ret.chunk_stages_workspace_bytes(B, H, N, dk, dv, C), dtype=torch.uint8, device=DEV)
+    S2 = torch.empty_like(S1)
+    ret.chunk_states(k, v, g, C, ws, state_out=S2)
+    o2 = ret.chunk_output(q, k, v, g, C, ws, gn=gn)
+    torch.cuda.synchronize()
+    _check(o1, _np(o2), "o vs two stages")
+    _check(S1, _np(S2), "state vs two stages")
+
+
+def test_single_pass_repeatable():
+    """No atomics on the output path: repeated calls give identical bits."""
+    B, H, N, dk, dv, C = 6, 16, 512, 256, 512, 64
+    _announce("single pass repeatable")
+    q, k, v = (t.to(DEV) for t in synthetic.make_qkv(B, H, N, dk, dv, dtype=torch.bfloat16, seed=3500))
+    g = synthetic.head_gammas(H)
+    outs = [ret.chunkwise(q, k, v, g, C, state_out=True, gn=ret.GroupNorm(1e-5)) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, S in outs[1:]:
+        assert torch.equal(o, outs[0][0])
+        assert torch.equal(S, outs[0][1])
+
+
+def test_backward_through_the_single_pass_kernel():
+    """B*H = 192: every retention of the backward (dV over dv = 512; dQ and dK
+    over 256-wide parts) takes the single-pass kernel, with state in and out."""
+    B, H, N, dk, dv, C = 12, 16, 320, 256, 512, 128
+    _announce(f"backward B={B} H={H} N={N} chunk={C} via the single pass")
+    assert _is_single_pass(B, H, N, dk, dv, C) and _is_single_pass(B, H, N, 256, dk, C)
+    q, k, v = synthetic.make_qkv(B, H, N, dk, dv, dtype=torch.bfloat16, seed=3600)
+    g = synthetic.head_gammas(H)
+    dO = synthetic.make_qkv(B, H, N, dk, dv, dtype=torch.bfloat16, seed=3601)[2]
+    S0 = synthetic.make_state(B, H, dk, dv, seed=3602, std=0.5)
+    dSN = synthetic.make_state(B, H, dk, dv, seed=3603, std=0.05)
+    gq, gk, gv, gs = ret.chunkwise_backward(q.to(DEV), k.to(DEV), v.to(DEV), dO.to(DEV), g, C,
+                                            state_in=S0.to(DEV), grad_state_out=dSN.to(DEV), grad_state_in=True)
+    torch.cuda.synchronize()
+    refs = orc.backward(q, k, v, g, dO, state_in=S0, d_state_out=dSN)
+    for name, got, r in zip(("dq", "dk", "dv", "dS0"), (gq, gk, gv, gs), refs):
+        _check(got, r, name)
+
+
+@pytest.mark.parametrize("C", [256, 512])
+def test_long_chunks_plan_the_two_stages(C):
+    """Chunks above 128 plan the two stages: the workspace holds the chunk states."""
+    B, H, N, dk, dv = 6, 16, 1024, 256, 512
+    assert not _is_single_pass(B, H, N, dk, dv, C)
+    assert ret.chunkwise_workspace_bytes(B, H, N, dk, dv, C) == ret.chunk_stages_workspace_bytes(B, H, N, dk, dv, C)
