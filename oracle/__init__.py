@@ -18,4 +18,5 @@ from .retention_oracle import (  # noqa: F401
     recurrent_step,
     state_after,
     swish,
+    xpos_rotate,
 )

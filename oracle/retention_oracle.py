@@ -16,7 +16,9 @@ Sources (the pages this follows; cited by tag below):
         achieved?" (the matrix D and the GroupNorm that follows it).
   [SP]  "RetNet入門" (Spiral.AI blog digest, news.ainew.jp): Multi-Scale
         Retention (MSR) (the normalised head outputs multiplied elementwise by
-        a gated branch).
+        a gated branch); the parallel representation (a conjugate in the
+        retention product) and the remark on LEX Transformer (the
+        intermediate expression of the derivation is xPos itself).
 
 Conventions (readings where the pages are silent):
   * positions n, m and the head index h are 0-based;
@@ -351,3 +353,37 @@ def gated_group_norm(o, gate, eps=1e-5, weight=None, bias=None):
     [B, H, N, dv] (head h's dv channels of it).
     """
     return swish(gate) * group_norm(o, eps, weight, bias)
+
+
+def xpos_rotate(x, theta, pos0=0):
+    """The rotation of the xPos relative position encoding, applied to Q or K.
+
+    [KR] Methods (block structure: xPos applied to Q and K), Key components,
+    3. xPos (a complex rotation that injects relative position into Q and K),
+    and the glossary at its end (xPos couples the rotation with a decay);
+    [SP] the parallel representation (a conjugate in the retention product)
+    and the remark on LEX Transformer. The pages give no formula; the reading
+    here: the d features of a token form d/2 complex numbers
+    z_i = x[2i] + 1j * x[2i+1], and the token at position n = pos0 + (its
+    index along the sequence) has z_i multiplied by exp(1j * n * theta_i).
+    Rotating Q and K alike and taking the real dot product gives
+    Re(sum_i zq_i * conj(zk_i) * exp(1j * (n - m) * theta_i)): the conjugate
+    form, a function of n - m only. The decay half of xPos is the retention's
+    own gamma^(n - m) (the matrix D), so no decay is applied here.
+
+    x is [..., N, d] with d even, theta is [d/2]; returns float64 of x's shape.
+    """
+    x = _f64(x)
+    theta = _f64(theta)
+    d = x.shape[-1]
+    if d % 2 or theta.shape != (d // 2,):
+        raise ValueError("x must have an even last axis d and theta d/2 entries")
+    N = x.shape[-2]
+    n = float(pos0) + np.arange(N, dtype=np.float64)
+    angle = n[:, None] * theta[None, :]  # [N, d/2]
+    c, s = np.cos(angle), np.sin(angle)
+    re, im = x[..., 0::2], x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = re * c - im * s
+    y[..., 1::2] = re * s + im * c
+    return y
