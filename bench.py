@@ -164,6 +164,7 @@ def measured_traffic():
     """
     current = {
         "fused": _source_hash(["fused.hip", "mfma_tiles.h", "common.h", "../build.py"]),
+        "xpos": _source_hash(["xpos.hip", "common.h", "../build.py"]),
         "chunk_out": _source_hash(["mfma_out.hip", "mfma_tiles.h", "common.h", "../build.py"]),
         "chunk_out_gated": _source_hash(["mfma_out.hip", "mfma_tiles.h", "common.h", "../build.py"]),
         "state_walk": _source_hash(["mfma.hip", "mfma_tiles.h", "common.h", "../build.py"]),
@@ -469,6 +470,40 @@ def backward_pass(ret, torch, dev, stream, qd, kd, vd, gamma, steps, warmup=3):
     }
 
 
+def xpos_prologue(ret, torch, dev, stream, qd, kd, steps, warmup=5):
+    """The xPos rotation of Q and K (retention_xpos_rotate, one launch over
+    both) at the headline shape, out of place: Q and K read and written once,
+    4 * B * H * N * dk * 2 bytes per call, bound by HBM."""
+    B, H, N, d = qd.shape
+    theta = ret.xpos_theta(d)
+    oq, ok = torch.empty_like(qd), torch.empty_like(kd)
+    for _ in range(warmup):
+        ret.xpos_rotate(qd, kd, theta, pos0=0, out_q=oq, out_k=ok)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        ret.xpos_rotate(qd, kd, theta, pos0=0, out_q=oq, out_k=ok)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = 4.0 * B * H * N * d * 2
+    del oq, ok
+    return {
+        "kernel": "xpos_kernel (retention_xpos_rotate on Q and K of B8 H16 N8192 dk256, bf16)",
+        "launch_ms": ms,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": nbytes / (ms * 1e-3) / 1e9,
+            "peak": PEAK_HBM / 1e9,
+            "unit": "GB/s",
+            "frac": nbytes / (ms * 1e-3) / PEAK_HBM,
+            "algorithmic_bytes_per_launch": nbytes,
+            "traffic": measured_traffic()["xpos"],
+        },
+    }
+
+
 SINGLE_PASS_CHUNKS = (64, 128)
 
 
@@ -581,6 +616,7 @@ def main():
     ap.add_argument("--skip-decode-b32", action="store_true", help="skip the cache-defeating B=32 decode timing")
     ap.add_argument("--skip-gated", action="store_true", help="skip the swish-gated prefill timing")
     ap.add_argument("--skip-backward", action="store_true", help="skip the backward-pass timing")
+    ap.add_argument("--skip-xpos", action="store_true", help="skip the xPos rotation timing")
     ap.add_argument("--skip-single-pass", action="store_true",
                     help="skip the single-pass kernel timings at chunks 64 and 128")
     args = ap.parse_args()
@@ -643,6 +679,11 @@ def main():
     if not args.skip_gated:
         print(f"[bench] timing {args.steps} swish-gated prefill steps", file=sys.stderr, flush=True)
         gated = gated_prefill(ret, torch, dev, stream, qd, kd, vd, gamma, ws, state, out, gn, args.steps)
+
+    xpos = None
+    if not args.skip_xpos:
+        print(f"[bench] timing {args.steps} xPos rotations of Q and K", file=sys.stderr, flush=True)
+        xpos = xpos_prologue(ret, torch, dev, stream, qd, kd, args.steps)
 
     single_pass = None
     if not args.skip_single_pass:
@@ -796,6 +837,7 @@ def main():
         },
         "gated": gated,
         "single_pass": single_pass,
+        "xpos": xpos,
         "backward": backward,
         "decode": {
             "steps": T,

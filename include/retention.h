@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define RETENTION_ABI_VERSION 3
+#define RETENTION_ABI_VERSION 4
 #define RETENTION_MAX_HEADS 256
 #define RETENTION_MAX_DK 256
 #define RETENTION_MAX_DV 1024
@@ -212,6 +212,36 @@ int retention_recurrent_step(const void* q, const void* k, const void* v,
                              const float* gamma_host, float* state, void* o,
                              int B, int H, int dk, int dv, int dtype,
                              const retention_gn_t* gn, void* stream);
+
+/*
+ * xPos rotation of Q and K, the prologue of retention ("RetNet - Retentive
+ * Network ...", Methods: block structure (xPos applied to Q and K) and Key
+ * components, 3. xPos; "RetNet入門", the conjugate in the parallel
+ * representation). The pages name a complex rotation by position and give no
+ * formula; this takes the features of a token in pairs (x[2i], x[2i+1]) as
+ * complex numbers and multiplies pair i of position n by
+ * exp(1j * (pos0 + n) * theta_i):
+ *   y[2i]   = x[2i] cos(a) - x[2i+1] sin(a),   a = (pos0 + n) * theta_i
+ *   y[2i+1] = x[2i] sin(a) + x[2i+1] cos(a)
+ * so that rotated queries and keys have real dot products that depend on
+ * the positions only through n - m. The decay half of xPos is the
+ * retention's own gamma^(n-m). theta_host holds d/2 finite angles (radians
+ * per position; any schedule, chosen by the caller) and is read before the
+ * call returns. q and k are [B, H, N, d] of type dtype; q_out and k_out have
+ * the same shape and type and may be q and k themselves (in place) but must
+ * not otherwise overlap any of the four buffers. k may be NULL (then k_out
+ * must be NULL too): q alone is rotated. pos0 >= 0 is the position of row 0
+ * (a decode step passes its token's position with N = 1); pos0 + N must not
+ * exceed 2^53. d must be even, 2 <= d <= RETENTION_MAX_DK. Every pointer must
+ * be aligned to a pair of elements (4 bytes for bf16, 8 for fp32). Angles are
+ * formed and reduced modulo 2 pi in double precision, then the sine and
+ * cosine are taken in float. Status: RET_ERR_INVALID_ARG for null or
+ * misaligned pointers, partial overlaps, odd d, non-finite angles or pos0
+ * out of range; RET_ERR_UNSUPPORTED for d above RETENTION_MAX_DK.
+ */
+int retention_xpos_rotate(const void* q, const void* k, void* q_out, void* k_out,
+                          const float* theta_host, int B, int H, int N, int d,
+                          long long pos0, int dtype, void* stream);
 
 /*
  * Backward pass of retention: gradients with respect to q, k, v and the

@@ -27,6 +27,8 @@ __all__ = [
     "chunk_states",
     "chunk_output",
     "recurrent_step",
+    "xpos_rotate",
+    "xpos_theta",
     "chunkwise_workspace_bytes",
     "chunk_stages_workspace_bytes",
     "chunkwise_backward",
@@ -355,6 +357,65 @@ def recurrent_step(q, k, v, gamma: GammaLike, state, gn: Optional[GroupNorm] = N
     if rc != 0:
         raise RetentionError("retention_recurrent_step", rc)
     return out
+
+
+def xpos_theta(d: int, base: float = 10000.0) -> torch.Tensor:
+    """Angles per position for the d/2 feature pairs: theta_i = base^(-2i/d),
+    i = 0 .. d/2 - 1 (float32, CPU). The pages give no schedule for the xPos
+    rotation; this geometric one (fast turns on the first pairs, slow on the
+    last) is a default reading, and any other may be passed to xpos_rotate."""
+    if d <= 0 or d % 2:
+        raise ValueError("d must be a positive even number")
+    i = torch.arange(d // 2, dtype=torch.float64)
+    return (float(base) ** (-2.0 * i / d)).to(torch.float32)
+
+
+def xpos_rotate(q, k=None, theta=None, pos0: int = 0, out_q=None, out_k=None):
+    """xPos rotation of q (and k): pair i of the features at position
+    pos0 + n is multiplied, as a complex number, by exp(1j (pos0 + n) theta_i).
+
+    q, k are [B, H, N, d] device tensors of one dtype (bf16 or fp32); theta is
+    d/2 angles (default ``xpos_theta(d)``). out_q / out_k may be q / k (in
+    place); by default new tensors are returned. Returns (q_rot, k_rot), k_rot
+    None when k is None. A decode step passes its token's position as pos0.
+    """
+    if not isinstance(q, torch.Tensor) or not q.is_cuda or q.dim() != 4 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B,H,N,d] device tensor")
+    B, H, N, d = q.shape
+    dt = _dtype_code(q)
+    if k is not None:
+        _require(k, "k", (B, H, N, d), q.dtype, q.device)
+    if theta is None:
+        theta = xpos_theta(d)
+    th = torch.as_tensor(theta, dtype=torch.float32).detach().to("cpu").contiguous()
+    if th.numel() != d // 2:
+        raise ValueError(f"theta has {th.numel()} entries, expected d/2 = {d // 2}")
+    arr = (ctypes.c_float * (d // 2))(*th.tolist())
+    if out_q is None:
+        out_q = torch.empty_like(q)
+    else:
+        _require(out_q, "out_q", (B, H, N, d), q.dtype, q.device)
+    if k is None:
+        if out_k is not None:
+            raise ValueError("out_k needs k")
+    elif out_k is None:
+        out_k = torch.empty_like(k)
+    else:
+        _require(out_k, "out_k", (B, H, N, d), q.dtype, q.device)
+    # Outputs are their own inputs or apart from every other buffer.
+    if out_q.data_ptr() != q.data_ptr():
+        _no_overlap(out_q, "out_q", q, k)
+    if k is not None:
+        if out_k.data_ptr() != k.data_ptr():
+            _no_overlap(out_k, "out_k", q, k)
+        _no_overlap(out_k, "out_k", out_q)
+    lib = _lib.load()
+    rc = lib.retention_xpos_rotate(q.data_ptr(), None if k is None else k.data_ptr(), out_q.data_ptr(),
+                                   None if k is None else out_k.data_ptr(), arr, B, H, N, d, int(pos0), dt,
+                                   _stream(q))
+    if rc != 0:
+        raise RetentionError("retention_xpos_rotate", rc)
+    return out_q, out_k
 
 
 def chunkwise_backward_workspace_bytes(B, H, N, dk, dv, chunk, dtype=torch.bfloat16) -> int:

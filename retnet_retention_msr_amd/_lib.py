@@ -29,13 +29,14 @@ EXPORTED = (
     "retention_chunk_states",
     "retention_chunk_output",
     "retention_recurrent_step",
+    "retention_xpos_rotate",
     "retention_chunkwise_backward_workspace_bytes",
     "retention_chunkwise_backward",
 )
 
 
 # RETENTION_ABI_VERSION of include/retention.h that the structures here mirror.
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class GnStruct(ctypes.Structure):
@@ -89,6 +90,8 @@ def open_library(path):
     lib.retention_chunk_output.restype = i
     lib.retention_recurrent_step.argtypes = [vp, vp, vp, f_p, vp, vp, i, i, i, i, i, gn_p, vp]
     lib.retention_recurrent_step.restype = i
+    lib.retention_xpos_rotate.argtypes = [vp, vp, vp, vp, f_p, i, i, i, i, ctypes.c_longlong, i, vp]
+    lib.retention_xpos_rotate.restype = i
     lib.retention_chunkwise_backward_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.retention_chunkwise_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.retention_chunkwise_backward.argtypes = [vp, vp, vp, vp, f_p, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, vp,

@@ -78,6 +78,12 @@ int check_gn(const retention_gn_t* gn, GnArgs* out) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? RET_OK : RET_ERR_HIP; }
 
+// Whether [a, a + an) and [b, b + bn) share a byte.
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + bn && y < x + an;
+}
+
 // A chunk at least as long as the sequence is one chunk: every such length
 // gives the same result. It is brought down to the sequence length rounded up
 // to a multiple of the MFMA block height (so the MFMA kernels stay eligible),
@@ -386,6 +392,34 @@ int retention_recurrent_step(const void* q, const void* k, const void* v, const 
   check_gamma(gamma_host, H, &decay);
   return status_of(ret::launch_decode_step(dtype, q, k, v, state, o, B, H, dk, dv, decay, g,
                                            static_cast<hipStream_t>(stream)));
+}
+
+int retention_xpos_rotate(const void* q, const void* k, void* q_out, void* k_out, const float* theta_host, int B,
+                          int H, int N, int d, long long pos0, int dtype, void* stream) {
+  if (!q || !q_out || !theta_host || (k == nullptr) != (k_out == nullptr)) return RET_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || d % 2 != 0 || !valid_dtype(dtype)) return RET_ERR_INVALID_ARG;
+  if (d > RETENTION_MAX_DK) return RET_ERR_UNSUPPORTED;
+  static_assert(RETENTION_MAX_DK <= 2 * ret::kMaxXposPairs, "xPos angle table");
+  if (static_cast<int64_t>(B) * H > INT_MAX) return RET_ERR_INVALID_ARG;
+  if (pos0 < 0 || pos0 > (int64_t{1} << 53) - N) return RET_ERR_INVALID_ARG;
+  for (int i = 0; i < d / 2; ++i)
+    if (!std::isfinite(theta_host[i])) return RET_ERR_INVALID_ARG;
+  const size_t esz = dtype == RET_BF16 ? 2 : 4;
+  const uintptr_t align = 2 * esz;
+  const void* ptrs[4] = {q, k, q_out, k_out};
+  for (const void* p : ptrs)
+    if (p && reinterpret_cast<uintptr_t>(p) % align != 0) return RET_ERR_INVALID_ARG;
+  const size_t n = static_cast<size_t>(B) * H * N * d * esz;
+  // Each output is its own input (in place) or shares no byte with any other
+  // buffer; the outputs never overlap; an in-place call needs q and k apart.
+  if (q_out != q && (overlaps(q_out, n, q, n) || (k && overlaps(q_out, n, k, n)))) return RET_ERR_INVALID_ARG;
+  if (k) {
+    if (k_out != k && (overlaps(k_out, n, k, n) || overlaps(k_out, n, q, n))) return RET_ERR_INVALID_ARG;
+    if (overlaps(k_out, n, q_out, n)) return RET_ERR_INVALID_ARG;
+    if ((q_out == q || k_out == k) && overlaps(q, n, k, n)) return RET_ERR_INVALID_ARG;
+  }
+  return status_of(ret::launch_xpos_rotate(dtype, q, k, q_out, k_out, theta_host, B * H, N, d,
+                                           static_cast<int64_t>(pos0), static_cast<hipStream_t>(stream)));
 }
 
 size_t retention_chunkwise_backward_workspace_bytes(int B, int H, int N, int dk, int dv, int chunk, int dtype) {

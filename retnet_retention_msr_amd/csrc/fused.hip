@@ -295,7 +295,6 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
     const uint16_t* vh = a.v + bh * static_cast<int64_t>(a.N) * dv + vt * kVT;
     uint16_t* oh = a.o + bh * static_cast<int64_t>(a.N) * dv + vt * kVT;
     const int64_t dkdv = static_cast<int64_t>(dk) * dv;
-    const int ucol = vt * kVT + vcol0 + l32;  // this lane's state column
     uint64_t* mymail = a.mail + static_cast<int64_t>(unit) * 2 * kMailWords;
     const int group0 = unit - vt;  // first unit of this head's v tiles
     // Powers of gamma: for gamma > 1/2 a power is split into a per-block
@@ -304,7 +303,8 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
     // since those factors would leave the float range.
     const bool split_decay = lg > -1.0f;
 
-    // R in accumulators: tile mt holds state rows 32mt.., columns ucol.
+    // R in accumulators: tile mt holds state rows 32mt.., column
+    // vt * 256 + vcol0 + l32 (this lane's).
     floatx16 R[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) R[mt] = floatx16{};

@@ -100,6 +100,15 @@ hipError_t launch_fused_chunkwise(const uint16_t* q, const uint16_t* k, const ui
                                   const float* state_in, float* state_out, void* workspace, const Dims& d, int chunk,
                                   const HeadDecay& decay, const GnArgs& gn, bool accumulate, hipStream_t stream);
 
+// xPos rotation (xpos.hip): the pairs (x[2i], x[2i+1]) of every position n
+// of q (and of k, unless null) multiplied, as complex numbers, by
+// exp(i (pos0 + n) theta_i); theta is a host array of d/2 angles, d <= 2 *
+// kMaxXposPairs. Outputs may be the inputs (in place). BH = B * H heads of N
+// positions, [BH][N][d] contiguous.
+constexpr int kMaxXposPairs = 128;
+hipError_t launch_xpos_rotate(int dtype, const void* q, const void* k, void* q_out, void* k_out, const float* theta,
+                              int BH, int N, int d, int64_t pos0, hipStream_t stream);
+
 // Bytes of the library-owned device scratch (scratch.hip) that the
 // allocation-free chunkwise entry point uses instead of a caller workspace.
 constexpr size_t kScratchBytes = size_t{64} << 20;

@@ -58,6 +58,11 @@ hipError_t launch_fused_chunkwise(const uint16_t*, const uint16_t*, const uint16
   return record();
 }
 
+hipError_t launch_xpos_rotate(int, const void*, const void*, void*, void*, const float*, int, int, int, int64_t,
+                              hipStream_t) {
+  return record();
+}
+
 // The scratch lookup hands out a fake address (never dereferenced: the
 // launchers above touch nothing).
 hipError_t scratch_pointer(void** out) {

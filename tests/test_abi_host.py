@@ -56,7 +56,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.retention_abi_version() == _lib.ABI_VERSION == 3
+    assert lib.retention_abi_version() == _lib.ABI_VERSION == 4
     assert _lib.status_string(0) == "ok"
     assert _lib.status_string(-1) == "invalid argument"
     assert _lib.status_string(-2) == "unsupported arguments"
@@ -306,3 +306,52 @@ def test_valid_backward_and_decode_calls_reach_the_launchers(lib, shape):
                                             dtype, FAKE, FAKE, FAKE, FAKE, need, None) == 0
     assert lib.retention_recurrent_step(FAKE, FAKE, FAKE, g, FAKE, FAKE, B, H, dk, dv, dtype, None, None) == 0
     assert _launches(lib) > before
+
+
+def _theta(n, value=0.5):
+    return (ctypes.c_float * n)(*([value] * n))
+
+
+def test_xpos_rotate_rejects_invalid_arguments(lib):
+    th = _theta(128)
+    A, B_ = 0x100000, 0x900000  # two fake buffers far apart (the 2x2x8x256 bf16 tensors span 16 KiB)
+    call = lambda q=A, k=B_, qo=A, ko=B_, th=th, B=2, H=2, N=8, d=256, pos0=0, dtype=1: \
+        lib.retention_xpos_rotate(q, k, qo, ko, th, B, H, N, d, pos0, dtype, None)
+    assert call(q=None) == -1
+    assert call(qo=None) == -1
+    assert call(th=None) == -1
+    assert call(k=None) == -1                      # k_out without k
+    assert call(ko=None) == -1                     # k without k_out
+    assert call(d=255) == -1                       # odd width
+    assert call(d=0) == -1 and call(N=0) == -1 and call(B=0) == -1
+    assert call(dtype=2) == -1
+    assert call(d=258, th=_theta(129)) == -2       # wider than RETENTION_MAX_DK
+    assert call(pos0=-1) == -1
+    assert call(pos0=2**53 - 7) == -1              # pos0 + N past 2^53
+    assert call(q=A + 2, qo=A + 2) == -1           # bf16 pairs need 4-byte alignment
+    assert call(q=A + 4, qo=A + 4, dtype=0) == -1  # fp32 pairs need 8
+    bad = _theta(128)
+    bad[7] = float("nan")
+    assert call(th=bad) == -1
+    bad[7] = float("inf")
+    assert call(th=bad) == -1
+    # Overlaps: an output inside another buffer, the outputs on each other, or
+    # in place with q and k overlapping.
+    assert call(qo=A + 64) == -1                   # q_out partly over q
+    assert call(qo=B_ + 64, ko=0x2000000) == -1    # q_out over k
+    assert call(qo=0x2000000, ko=0x2000000 + 64) == -1
+    assert call(k=A + 1024, ko=0x3000000) == -1    # in-place q with k overlapping q
+
+
+@shim_only
+def test_valid_xpos_calls_reach_the_launcher(lib):
+    th = _theta(128)
+    before = _launches(lib)
+    A, B_ = 0x100000, 0x900000
+    # In place, out of place, q alone, the largest position, a narrow odd-pair width.
+    assert lib.retention_xpos_rotate(A, B_, A, B_, th, 2, 2, 8, 256, 0, 1, None) == 0
+    assert lib.retention_xpos_rotate(A, B_, 0x2000000, 0x3000000, th, 2, 2, 8, 256, 0, 0, None) == 0
+    assert lib.retention_xpos_rotate(A, None, A, None, th, 8, 16, 8192, 256, 123456789, 1, None) == 0
+    assert lib.retention_xpos_rotate(A, None, A, None, th, 1, 1, 1, 256, 2**53 - 1, 1, None) == 0
+    assert lib.retention_xpos_rotate(A, B_, A, B_, _theta(3), 1, 3, 5, 6, 7, 1, None) == 0
+    assert _launches(lib) == before + 5

@@ -34,7 +34,7 @@ def test_more_than_one_gpu_is_refused():
 
 def test_measured_traffic_is_keyed_by_kernel_source():
     t = bench.measured_traffic()
-    assert set(t) == {"fused", "chunk_out", "chunk_out_gated", "state_walk", "decode_step"}
+    assert set(t) == {"fused", "xpos", "chunk_out", "chunk_out_gated", "state_walk", "decode_step"}
     for v in t.values():
         assert v is None or v > 0
 
