@@ -151,6 +151,7 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
   // Per-wave row partials [8][64], then mean [64] and sum of squared deviations [64]
   // of this workgroup's columns, then the merged shift [64] and 1/std [64].
   __shared__ __attribute__((aligned(16))) float sG[kWavesF * kRowsF + 4 * kRowsF];
+  __shared__ __attribute__((aligned(16))) float sGw[kWavesF * kRowsF];
   // GroupNorm weight and bias of the unit's 256 columns.
   __shared__ float sAff[2 * kVT];
 
@@ -394,41 +395,58 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
     // columns): two passes through LDS (mean, then the sum of squared
     // deviations about it), then publication to the other v tiles.
     auto local_stats = [&](const floatx16 (&acc)[2]) __attribute__((always_inline)) {
-      float* s_part = sG;
+      float* s_wmean = sG;                  // [8 waves][64 rows]: row means over the wave's 32 columns
+      float* s_wm2 = sGw;                   // [8 waves][64 rows]: sums of squared deviations about them
       float* s_mean = sG + kWavesF * kRowsF;
       float* s_m2 = s_mean + kRowsF;
       const int my_slot = lane & 31;
       const int my_row = (my_slot >> 4) * 32 + acc_row(my_slot & 15, lane);
+      {
+        float x[32];
 #pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) x[qt * 16 + e] = acc[qt][e];
+        // The wave's own slots: written and read back by this wave only (its
+        // LDS operations complete in order), so no barrier.
+        s_wmean[wave * kRowsF + my_row] = reduce_scatter32(x, lane) * (1.0f / 32);
+      }
+      {
         float x[32];
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            if (pass == 0) {
+            const floatx4 m = *reinterpret_cast<const floatx4*>(s_wmean + wave * kRowsF + qt * 32 + 8 * g +
+                                                                4 * (lane >> 5));
 #pragma unroll
-              for (int e = 0; e < 4; ++e) x[qt * 16 + 4 * g + e] = acc[qt][4 * g + e];
-            } else {
-              // Means of rows qt*32 + 8g + 4*(l/32) + 0..3 in one 16-byte read.
-              const floatx4 m = *reinterpret_cast<const floatx4*>(s_mean + qt * 32 + 8 * g + 4 * (lane >> 5));
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float d = acc[qt][4 * g + e] - m[e];
-                x[qt * 16 + 4 * g + e] = d * d;
-              }
+            for (int e = 0; e < 4; ++e) {
+              const float d = acc[qt][4 * g + e] - m[e];
+              x[qt * 16 + 4 * g + e] = d * d;
             }
           }
-        s_part[wave * kRowsF + my_row] = reduce_scatter32(x, lane);
-        lds_barrier();
-        if (wave == kGnWave) {
-          float t = 0.f;
+        s_wm2[wave * kRowsF + my_row] = reduce_scatter32(x, lane);
+      }
+      lds_barrier();
+      if (wave == kGnWave) {
+        // Row `lane`: the eight waves' (mean, M2) over 32 columns each merged
+        // in a fixed order: mean of the means, M2 = sum M2_w + 32 sum (m_w - mean)^2.
+        float mw[kWavesF], msum = 0.f;
 #pragma unroll
-          for (int w2 = 0; w2 < kWavesF; ++w2) t += s_part[w2 * kRowsF + lane];
-          if (pass == 0) s_mean[lane] = t * (1.0f / kVT);
-          else s_m2[lane] = t;
+        for (int w2 = 0; w2 < kWavesF; ++w2) {
+          mw[w2] = s_wmean[w2 * kRowsF + lane];
+          msum += mw[w2];
         }
-        lds_barrier();
+        const float mean = msum * (1.0f / kWavesF);
+        float m2 = 0.f, dev = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < kWavesF; ++w2) {
+          m2 += s_wm2[w2 * kRowsF + lane];
+          const float d = mw[w2] - mean;
+          dev += d * d;
+        }
+        s_mean[lane] = mean;
+        s_m2[lane] = m2 + 32.0f * dev;
       }
       if (a.nvt > 1 && wave == kGnWave) {
         // Publish (mean, M2) of row `lane` into slot ex % 2 as two tagged
@@ -792,9 +810,6 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
         // first blocks) go out before this block's stores, so the waits for
         // those copies do not wait for the stores as well.
         if (gn.enabled) local_stats(acc);
-        uint32_t gv[2][4][2];
-        load_epi(gv, q0, qvalid);
-        gn_merge(ex - 1);
         const bool do_update = last_qb && !(last_chunk && a.state_out == nullptr);
         if (!last_qb) {
           copy_k(cs, sXK2);
@@ -808,6 +823,9 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
             copy_v(cs + kTileF, sXK1);
           }
         }
+        uint32_t gv[2][4][2];
+        load_epi(gv, q0, qvalid);
+        gn_merge(ex - 1);
         store_block(acc, gv, q0, qvalid);
         pend_st = kOStores;
       }
