@@ -507,7 +507,8 @@ def xpos_prologue(ret, torch, dev, stream, qd, kd, steps, warmup=5):
 SINGLE_PASS_CHUNKS = (64, 128)
 
 
-def single_pass_prefill(ret, torch, dev, stream, qd, kd, vd, gamma, state, out, gn, steps, warmup=10):
+def single_pass_prefill(ret, torch, dev, stream, qd, kd, vd, gamma, state, out, gn, steps, warmup=10,
+                        chunks=SINGLE_PASS_CHUNKS):
     """The headline shape at the chunk lengths that plan the single-pass
     kernel (retention_chunkwise, one launch after a small zeroing kernel).
     The chunk length changes only the blocking of the same retention (every
@@ -515,7 +516,7 @@ def single_pass_prefill(ret, torch, dev, stream, qd, kd, vd, gamma, state, out, 
     count; these are not the headline configuration, whose chunk is 512."""
     B, H, N = qd.shape[0], qd.shape[1], qd.shape[2]
     res = {}
-    for C in SINGLE_PASS_CHUNKS:
+    for C in chunks:
         ws = torch.empty(max(ret.chunkwise_workspace_bytes(B, H, N, DK, DV, C), 1), dtype=torch.uint8, device=dev)
         assert ret.chunkwise_workspace_bytes(B, H, N, DK, DV, C) == B * H * (DV // 256) * 2048, "not the single pass"
 
@@ -617,6 +618,8 @@ def main():
     ap.add_argument("--skip-gated", action="store_true", help="skip the swish-gated prefill timing")
     ap.add_argument("--skip-backward", action="store_true", help="skip the backward-pass timing")
     ap.add_argument("--skip-xpos", action="store_true", help="skip the xPos rotation timing")
+    ap.add_argument("--single-pass-chunks", default="64,128",
+                    help="chunk lengths of the single-pass timings (each must plan the single pass)")
     ap.add_argument("--skip-single-pass", action="store_true",
                     help="skip the single-pass kernel timings at chunks 64 and 128")
     args = ap.parse_args()
@@ -687,8 +690,11 @@ def main():
 
     single_pass = None
     if not args.skip_single_pass:
-        print(f"[bench] timing the single-pass kernel at chunks {SINGLE_PASS_CHUNKS}", file=sys.stderr, flush=True)
-        single_pass = single_pass_prefill(ret, torch, dev, stream, qd, kd, vd, gamma, state, out, gn, args.steps)
+        print(f"[bench] timing the single-pass kernel at chunks {args.single_pass_chunks}", file=sys.stderr,
+              flush=True)
+        chunks = tuple(int(c) for c in args.single_pass_chunks.split(","))
+        single_pass = single_pass_prefill(ret, torch, dev, stream, qd, kd, vd, gamma, state, out, gn, args.steps,
+                                          chunks=chunks)
 
     backward = None
     if not args.skip_backward:
