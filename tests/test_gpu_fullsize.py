@@ -2,8 +2,8 @@
 
 Shapes are those the operator is benchmarked on: a 1.3B-shaped forward (B=2,
 H=8, N=2048, dk=256, dv=512, chunk 256), the 6.7B-shaped chunkwise prefill with
-GroupNorm (B=8, H=16, N=8192, chunk 512; the launch bench.py times), its gated
-form, the decode step on an fp32 [8,16,256,512] state, and a 64k-token
+GroupNorm (B=8, H=16, N=8192, chunk 512; the launch bench.py times), the same
+prefill at chunks 64 and 128 (the single-pass kernel), its gated form, the decode step on an fp32 [8,16,256,512] state, and a 64k-token
 sequence (B=1, H=16, N=65536) at chunk sizes 64..512. The forward outputs and
 final states are compared element by element, every (b, h) slice, with the
 fp64 oracle run in full on the host (one batch row at a time); only the
@@ -106,6 +106,32 @@ def test_6p7b_prefill_with_groupnorm_full(prefill_6p7b, prefill_6p7b_oracle):
     out = torch.empty(B, H, N, dv, dtype=torch.bfloat16, device=DEV)
     state = torch.empty(B, H, dk, dv, dtype=torch.float32, device=DEV)
     ws = torch.empty(ret.chunkwise_workspace_bytes(B, H, N, dk, dv, C), dtype=torch.uint8, device=DEV)
+    ret.chunkwise(qd, kd, vd, g, C, state_out=state, gn=ret.GroupNorm(1e-5), out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for b in range(B):
+        _check(_f64(out[b : b + 1]), orc.group_norm(raws[b], eps=1e-5), f"o b={b}")
+        _check(_f64(state[b : b + 1]), states[b], f"state b={b}")
+
+
+@pytest.mark.parametrize("C", [64, 128])
+def test_6p7b_prefill_single_pass_full(prefill_6p7b, prefill_6p7b_oracle, C):
+    """Every output and state element of the prefill at chunks 64 and 128, which
+    plan the single-pass kernel. The reference is the oracle's chunk-512 result:
+    the chunkwise form gives the same retention at every chunk length (pinned
+    on the CPU against the parallel and recurrent forms), so the fp64 outputs
+    of different chunk lengths differ only by rounding far below the bound."""
+    _announce(f"B=8 H=16 N=8192 chunk {C} (single pass) + GroupNorm: all outputs and states")
+    q, k, v = prefill_6p7b
+    raws, states = prefill_6p7b_oracle
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    g = synthetic.head_gammas(H)
+    nbytes = ret.chunkwise_workspace_bytes(B, H, N, dk, dv, C)
+    assert nbytes == B * H * (dv // 256) * 2048, "not the single-pass plan"
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out = torch.empty(B, H, N, dv, dtype=torch.bfloat16, device=DEV)
+    state = torch.empty(B, H, dk, dv, dtype=torch.float32, device=DEV)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
     ret.chunkwise(qd, kd, vd, g, C, state_out=state, gn=ret.GroupNorm(1e-5), out=out, workspace=ws)
     torch.cuda.synchronize()
     for b in range(B):

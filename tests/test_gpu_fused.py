@@ -62,6 +62,7 @@ CASES = [
     (6, 16, 1000, 256, 512, 128, False, False, True),  # many chunks, ragged last chunk, no GroupNorm
     (12, 16, 384, 128, 256, 64, True, True, True),     # dk 128, one v tile (no exchange), chunk 64
     (3, 16, 512, 256, 1024, 128, True, True, False),   # four v tiles
+    (4, 16, 300, 256, 768, 64, True, True, True),      # three v tiles (exchange among three), ragged
     (6, 16, 200, 256, 512, 64, True, False, True),     # chunk 64, N not a multiple of 32
 ]
 

@@ -521,3 +521,23 @@ def test_extreme_decays(dtype):
     o, S = ret.chunkwise(qd, kd, vd, g, C, state_in=S0d, state_out=True)
     _check(o, ref, TOL[dtype], "o")
     _check(S, Sref, TOL[dtype], "state")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_backward_extreme_decays_with_final_state_gradient(dtype):
+    """gamma = 1e-6 and 1 - 2^-20 with a starting state and a final-state
+    gradient (which enters the reverse-time retentions divided by gamma: 1e6
+    for the first head), all four gradients against the oracle."""
+    _announce(f"backward extreme decays with dS_N {dtype}")
+    B, H, N, dk, dv, C = 1, 2, 300, 64, 128, 64
+    q, k, v, _, S0 = _inputs(B, H, N, dk, dv, dtype, seed=510, with_state=True)
+    g = torch.tensor([1e-6, 1.0 - 2.0 ** -20])
+    dO = synthetic.make_qkv(B, H, N, dk, dv, dtype=dtype, seed=511)[2]
+    dSN = synthetic.make_state(B, H, dk, dv, seed=512, std=0.1)
+    qd, kd, vd, dOd, S0d, dSNd = _dev(q, k, v, dO, S0, dSN)
+    gq, gk, gv, gs = ret.chunkwise_backward(qd, kd, vd, dOd, g, C, state_in=S0d, grad_state_out=dSNd,
+                                            grad_state_in=True)
+    torch.cuda.synchronize()
+    refs = orc.backward(q, k, v, g, dO, state_in=S0, d_state_out=dSN)
+    for name, got, r in zip(("dq", "dk", "dv", "dS0"), (gq, gk, gv, gs), refs):
+        _check(got, r, TOL[dtype], name)
