@@ -114,10 +114,15 @@ int retention_parallel(const void* q, const void* k, const void* v,
  * Bytes of device workspace retention_chunkwise needs for these sizes
  * (a pure function of its arguments; 0 for invalid sizes). Where the
  * single-pass kernel applies (bf16, dk 128 or 256, dv a multiple of 256 up to
- * 1024, chunk 64 or 128 after clamping to N, and at least 192 (head,
- * 256-column v tile) pairs) this is only the GroupNorm exchange: 2 KiB per
- * (head, 256-column v tile). Otherwise it holds a state per chunk (the
- * two-stage path, retention_chunk_stages_workspace_bytes).
+ * 1024, chunk 64 or 128 after clamping to N) it is the GroupNorm exchange,
+ * 2 KiB per (head, 256-column v tile), when there are at least 192 such
+ * pairs. With fewer, each sequence is cut into nseg segments of whole chunks
+ * (nseg = ceil(256 / pairs), at most chunks / 4; used when pairs * nseg >=
+ * 192), walked in parallel from states a first pass computes: 2 KiB per
+ * (head, segment, v tile), plus the segments' fp32 end states
+ * (B*H*nseg*dk*dv*4 bytes) and room for a copy of state_in (B*H*dk*dv*4),
+ * each part rounded up to 256 bytes. Otherwise it holds a state per chunk
+ * (the two-stage path, retention_chunk_stages_workspace_bytes).
  */
 size_t retention_chunkwise_workspace_bytes(int B, int H, int N, int dk, int dv,
                                            int chunk, int dtype);

@@ -33,6 +33,12 @@ constexpr int64_t kFusedMinUnits = 192;
 // values once per 64-row query block (its state takes the registers a
 // longer block would need) and measures slower than the two stages.
 constexpr int kFusedMaxChunk = 128;
+// With fewer (head, v tile) pairs than kFusedMinUnits the sequences are cut
+// into segments (walked in parallel from states a first pass computes) until
+// there are about kFusedTargetUnits units, one per CU, keeping at least
+// kFusedMinChunksPerSeg chunks per segment.
+constexpr int64_t kFusedTargetUnits = 256;
+constexpr int kFusedMinChunksPerSeg = 4;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -103,24 +109,41 @@ struct ChunkPlan {
   int nchunks;
   int chunks_per_seg;
   int nseg;
-  size_t states_bytes;  // per-chunk states
-  size_t seg_bytes;     // segment end states (MFMA path, nseg > 1)
+  size_t states_bytes;  // per-chunk states (two stages); the mailbox (single pass)
+  size_t seg_bytes;     // segment end states (nseg > 1)
+  size_t in_bytes;      // single pass with segments: a copy of state_in when state_out aliases it
   size_t total;
 };
 
-bool use_fused(int B, int H, int dk, int dv, int chunk, int dtype) {
-  return dtype == RET_BF16 && chunk <= kFusedMaxChunk && ret::fused_supports(dk, dv, chunk) &&
-         static_cast<int64_t>(B) * H * (dv / 256) >= kFusedMinUnits;
+// Segments of the single pass for these sizes: 1 when the heads alone give
+// enough units, 0 when neither they nor segments of at least
+// kFusedMinChunksPerSeg chunks do (then the two stages run).
+int fused_segments(int B, int H, int dk, int dv, int chunk, int dtype, int nchunks) {
+  if (dtype != RET_BF16 || chunk > kFusedMaxChunk || !ret::fused_supports(dk, dv, chunk)) return 0;
+  const int64_t base = static_cast<int64_t>(B) * H * (dv / 256);
+  if (base >= kFusedMinUnits) return 1;
+  int64_t nseg = (kFusedTargetUnits + base - 1) / base;
+  nseg = std::min<int64_t>(nseg, nchunks / kFusedMinChunksPerSeg);
+  if (nseg < 2 || base * nseg < kFusedMinUnits) return 0;
+  return static_cast<int>(nseg);
 }
 
 // `stages`: plan the two stages even where the single-pass kernel applies
 // (the explicit stage entry points).
 ChunkPlan plan_chunkwise(int B, int H, int N, int dk, int dv, int chunk, int dtype, bool stages = false) {
   ChunkPlan p{};
-  if (!stages && use_fused(B, H, dk, dv, chunk, dtype)) {
+  p.nchunks = static_cast<int>((static_cast<int64_t>(N) + chunk - 1) / chunk);
+  const int fseg = stages ? 0 : fused_segments(B, H, dk, dv, chunk, dtype, p.nchunks);
+  if (fseg > 0) {
     p.fused = true;
-    p.nchunks = static_cast<int>((static_cast<int64_t>(N) + chunk - 1) / chunk);
-    p.total = ret::fused_workspace_bytes(static_cast<int64_t>(B) * H, dv);
+    p.chunks_per_seg = (p.nchunks + fseg - 1) / fseg;
+    p.nseg = (p.nchunks + p.chunks_per_seg - 1) / p.chunks_per_seg;
+    const size_t heads = static_cast<size_t>(B) * H;
+    const size_t dkdv = static_cast<size_t>(dk) * dv;
+    p.states_bytes = align_up(ret::fused_workspace_bytes(static_cast<int64_t>(heads) * p.nseg, dv));
+    p.seg_bytes = p.nseg > 1 ? align_up(heads * p.nseg * dkdv * sizeof(float)) : 0;
+    p.in_bytes = p.nseg > 1 ? align_up(heads * dkdv * sizeof(float)) : 0;
+    p.total = p.states_bytes + p.seg_bytes + p.in_bytes;
     return p;
   }
   p.mfma = dtype == RET_BF16 && ret::mfma_supports(dk, dv) && chunk % kMfmaRows == 0;
@@ -245,9 +268,25 @@ int run_chunkwise(const ChunkPlan& p, const void* q, const void* k, const void* 
                   float* state_out, const Dims& d, int chunk, int dtype, const HeadDecay& decay, const GnArgs& g,
                   char* ws, hipStream_t s, bool accumulate = false) {
   if (p.fused) {
+    float* segs = nullptr;
+    if (p.nseg > 1) {
+      segs = reinterpret_cast<float*>(ws + p.states_bytes);
+      // The first segment's workgroups read state_in while the last one's may
+      // already write state_out: an aliased state_in is read from a copy.
+      const size_t sbytes = static_cast<size_t>(d.B) * d.H * d.dk * d.dv * sizeof(float);
+      if (state_in && state_out && overlaps(state_in, sbytes, state_out, sbytes)) {
+        float* copy = reinterpret_cast<float*>(ws + p.states_bytes + p.seg_bytes);
+        if (ret::copy_device(copy, state_in, sbytes, s) != hipSuccess) return RET_ERR_HIP;
+        state_in = copy;
+      }
+      if (ret::launch_segment_ends(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), state_in, segs,
+                                   p.chunks_per_seg, d, chunk, decay, s) != hipSuccess)
+        return RET_ERR_HIP;
+    }
     return status_of(ret::launch_fused_chunkwise(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                                  static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), state_in,
-                                                 state_out, ws, d, chunk, decay, g, accumulate, s));
+                                                 state_out, ws, d, chunk, decay, g, accumulate, s, p.chunks_per_seg,
+                                                 segs));
   }
   if (launch_states(p, k, v, state_in, state_out, ws, d, chunk, dtype, decay, s) != hipSuccess) return RET_ERR_HIP;
   return status_of(launch_output(p, q, k, v, o, ws, state_in != nullptr, d, chunk, dtype, decay, g, s, accumulate));

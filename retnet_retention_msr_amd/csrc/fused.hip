@@ -91,6 +91,11 @@ struct FusedArgs {
   const float* state_in;  // [B*H][dk][dv] or null
   float* state_out;       // [B*H][dk][dv] or null
   uint64_t* mail;         // [units][2 slots][kMailWords], zeroed before the launch
+  // Sequences cut into nseg segments of chunks_per_seg chunks (nseg = 1: whole
+  // sequences): seg_states[bh][s] holds the state reached at the end of
+  // segment s < nseg - 1 when it starts from zero (segment 0 from state_in).
+  const float* seg_states;
+  int nseg, chunks_per_seg;
   int H, N, dk, dv, chunk, nchunks, nvt, units;
   int spin_limit;         // polls of a partner's flag before giving up on it
 };
@@ -287,14 +292,24 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
   const int lwg = xcd_logical_block(blockIdx.x, G);
 
   for (int unit = lwg; unit < a.units; unit += G) {
+    // Unit = (head, segment, v tile), v tile fastest: the v tiles of a
+    // segment (which exchange GroupNorm statistics) are neighbours.
     const int vt = unit % a.nvt;
-    const int64_t bh = unit / a.nvt;
+    const int seg = (unit / a.nvt) % a.nseg;
+    const int64_t bh = unit / a.nvt / a.nseg;
     const int h = static_cast<int>(bh % a.H);
     const float lg = decay.log2g[h];
-    const uint16_t* qh = a.q + bh * static_cast<int64_t>(a.N) * dk;
-    const uint16_t* kh = a.k + bh * static_cast<int64_t>(a.N) * dk;
-    const uint16_t* vh = a.v + bh * static_cast<int64_t>(a.N) * dv + vt * kVT;
-    uint16_t* oh = a.o + bh * static_cast<int64_t>(a.N) * dv + vt * kVT;
+    // This unit's rows: [row0, row0 + Nu) of the head's sequence, chunks
+    // counted from row0 (segments start on chunk boundaries).
+    const int row0 = seg * a.chunks_per_seg * a.chunk;
+    const int Nu = min(a.chunks_per_seg * a.chunk, a.N - row0);
+    const int ncu = (Nu + a.chunk - 1) / a.chunk;
+    const int64_t rbase = bh * static_cast<int64_t>(a.N) + row0;  // first row in [B*H*N]
+    const uint16_t* qh = a.q + rbase * dk;
+    const uint16_t* kh = a.k + rbase * dk;
+    const uint16_t* vh = a.v + rbase * dv + vt * kVT;
+    uint16_t* oh = a.o + rbase * dv + vt * kVT;
+    float* const state_out = seg == a.nseg - 1 ? a.state_out : nullptr;
     const int64_t dkdv = static_cast<int64_t>(dk) * dv;
     uint64_t* mymail = a.mail + static_cast<int64_t>(unit) * 2 * kMailWords;
     const int group0 = unit - vt;  // first unit of this head's v tiles
@@ -309,15 +324,20 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
     floatx16 R[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) R[mt] = floatx16{};
-    const bool has_in = a.state_in != nullptr;
+    // The state this unit starts from: state_in for the first segment; for a
+    // later one starting at row0, sum over earlier segments s' of
+    // gamma^(row0 - end_s') U_s' (U_0 already carries state_in).
+    const bool has_in = seg > 0 || a.state_in != nullptr;
+    const int nsrc = seg > 0 ? seg : (a.state_in ? 1 : 0);
     // The state moves between HBM and the accumulators through LDS, four
     // 32-row tiles (32 KiB of fp32 each) at a time in sQ and the three buffer
     // sets: the copies are whole 1-KiB rows, and a lane's 16 accumulator
     // values lie at constant offsets from one per-lane LDS address.
     uint16_t* const stage[4] = {sQ, sXK0, sXK1, sXK2};
     const int acc_lds = (4 * (lane >> 5)) * kVT + vcol0 + l32;  // float index of accumulator 0
-    if (has_in) {
-      const float* sbase = a.state_in + bh * dkdv + vt * kVT;
+    for (int src = 0; src < nsrc; ++src) {
+      const float* sbase = (seg > 0 ? a.seg_states + (bh * a.nseg + src) * dkdv : a.state_in + bh * dkdv) + vt * kVT;
+      const float fsrc = seg > 0 ? gpow(lg, static_cast<float>(row0 - (src + 1) * a.chunks_per_seg * a.chunk)) : 1.f;
 #pragma unroll
       for (int g4 = 0; g4 < MT; g4 += 4) {
 #pragma unroll
@@ -335,7 +355,7 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
         for (int t = 0; t < 4 && g4 + t < MT; ++t) {
           const float* f = reinterpret_cast<const float*>(stage[t]) + acc_lds;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) R[g4 + t][r] = f[(8 * (r >> 2) + (r & 3)) * kVT];
+          for (int r = 0; r < 16; ++r) R[g4 + t][r] = fmaf(fsrc, f[(8 * (r >> 2) + (r & 3)) * kVT], R[g4 + t][r]);
         }
         __syncthreads();
       }
@@ -347,14 +367,14 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
       if (wave < 4) {
         int qoff[2];
         q_offsets(qoff);
-        const int rows = min(kRowsF, a.N - q0);
+        const int rows = min(kRowsF, Nu - q0);
         const __amdgpu_buffer_rsrc_t r = make_rsrc(qh + static_cast<int64_t>(q0) * dk, rows * dk * 2);
 #pragma unroll
         for (int m = 0; m < 8; ++m) dma16s(r, sQ + (wave + 4 * m) * 512, qoff[m & 1], 8 * (m & ~1) * dk * 2);
       }
     };
     auto copy_k = [&](int t0, uint16_t* set) __attribute__((always_inline)) {
-      const int rows = min(kTileF, a.N - t0);
+      const int rows = min(kTileF, Nu - t0);
       const __amdgpu_buffer_rsrc_t r = make_rsrc(kh + static_cast<int64_t>(t0) * dk, rows * dk * 2);
 #pragma unroll
       for (int m = 0; m < 2; ++m) dma16s(r, set + kTileF * kVT + (wave + kWavesF * m) * 512, kqoff, m * 16 * dk * 2);
@@ -362,13 +382,13 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
     // K block at t0 for the update pass: into the V-tile slot layout of `set`'s K part.
     auto copy_kx = [&](int t0, uint16_t* set) __attribute__((always_inline)) {
       const int kxoff = kx_offset();
-      const int rows = min(kTileF, a.N - t0);
+      const int rows = min(kTileF, Nu - t0);
       const __amdgpu_buffer_rsrc_t r = make_rsrc(kh + static_cast<int64_t>(t0) * dk, rows * dk * 2);
 #pragma unroll
       for (int m = 0; m < 2; ++m) dma16s(r, set + kTileF * kVT + (wave + kWavesF * m) * 512, kxoff, m * 16 * dk * 2);
     };
     auto copy_v = [&](int t0, uint16_t* set) __attribute__((always_inline)) {
-      const int rows = min(kTileF, a.N - t0);
+      const int rows = min(kTileF, Nu - t0);
       const __amdgpu_buffer_rsrc_t r =
           make_rsrc(vh + static_cast<int64_t>(t0) * dv, ((rows - 1) * dv + kVT) * 2);
 #pragma unroll
@@ -536,7 +556,7 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
       if constexpr (EPI != 0) {
         const int so = store_offset();
         const uint16_t* gbase = EPI == 1 ? static_cast<const uint16_t*>(gn.gate) : a.o;
-        const uint16_t* gblk = gbase + (bh * a.N + pq0) * static_cast<int64_t>(dv) + vt * kVT;
+        const uint16_t* gblk = gbase + (rbase + pq0) * static_cast<int64_t>(dv) + vt * kVT;
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
@@ -612,21 +632,21 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
 
     // ---- chunks
     int cs = 0;
-    if (a.nchunks > 0) {
+    if (ncu > 0) {
       // First query block's Q and the first key-step copies of chunk 0.
       copy_q(0);
       copy_k(0, sXK2);
       copy_v(0, sXK0);
-      if (min(a.chunk, a.N) > kTileF) copy_k(kTileF, sXK0);
+      if (min(a.chunk, Nu) > kTileF) copy_k(kTileF, sXK0);
     }
-    for (int c = 0; c < a.nchunks; ++c, cs += a.chunk) {
-      const int L = min(a.chunk, a.N - cs);
+    for (int c = 0; c < ncu; ++c, cs += a.chunk) {
+      const int L = min(a.chunk, Nu - cs);
       const int nqb = (L + kRowsF - 1) / kRowsF;
-      const bool last_chunk = c + 1 == a.nchunks;
+      const bool last_chunk = c + 1 == ncu;
       for (int qb = 0; qb < nqb; ++qb) {
         const int q0 = cs + qb * kRowsF;
-        const int qvalid = min(kRowsF, a.N - q0);
-        const int kend = min(q0 + kRowsF, a.N);
+        const int qvalid = min(kRowsF, Nu - q0);
+        const int kend = min(q0 + kRowsF, Nu);
         const int nkb = (kend - cs + kTileF - 1) / kTileF;  // key blocks up to the diagonal
 
         floatx16 acc[2];
@@ -810,11 +830,11 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
         // first blocks) go out before this block's stores, so the waits for
         // those copies do not wait for the stores as well.
         if (gn.enabled) local_stats(acc);
-        const bool do_update = last_qb && !(last_chunk && a.state_out == nullptr);
+        const bool do_update = last_qb && !(last_chunk && state_out == nullptr);
         if (!last_qb) {
           copy_k(cs, sXK2);
           copy_v(cs, sXK0);
-          if (min(q0 + 2 * kRowsF, a.N) - cs > kTileF) copy_k(cs + kTileF, sXK0);
+          if (min(q0 + 2 * kRowsF, Nu) - cs > kTileF) copy_k(cs + kTileF, sXK0);
         } else if (do_update) {
           copy_kx(cs, sXK0);
           copy_v(cs, sXK0);
@@ -832,7 +852,7 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
 
       // ---- update pass: R = gamma^L R + sum over the chunk's key blocks of
       // K^T (zeta V), zeta_t = gamma^(L-1-t) (t local). Set j % 3 holds V_j and K_j.
-      const bool do_update = !(last_chunk && a.state_out == nullptr);
+      const bool do_update = !(last_chunk && state_out == nullptr);
       if (do_update) {
         const int nkc = (L + kTileF - 1) / kTileF;
         const float carry = gpow(lg, static_cast<float>(L));
@@ -919,11 +939,11 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
         const int ncs = cs + a.chunk;
         copy_k(ncs, sXK2);
         copy_v(ncs, sXK0);
-        if (min(a.chunk, a.N - ncs) > kTileF) copy_k(ncs + kTileF, sXK0);
+        if (min(a.chunk, Nu - ncs) > kTileF) copy_k(ncs + kTileF, sXK0);
       }
     }
-    if (a.state_out) {
-      float* obase = a.state_out + bh * dkdv + vt * kVT;
+    if (state_out) {
+      float* obase = state_out + bh * dkdv + vt * kVT;
       wait_vmem();
       __syncthreads();
 #pragma unroll
@@ -963,9 +983,14 @@ __global__ void __launch_bounds__(256) zero_ints_kernel(int* p, int n) {
 
 }  // namespace
 
+hipError_t copy_device(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, stream);
+}
+
 hipError_t launch_fused_chunkwise(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                                   const float* state_in, float* state_out, void* workspace, const Dims& d, int chunk,
-                                  const HeadDecay& decay, const GnArgs& gn, bool accumulate, hipStream_t stream) {
+                                  const HeadDecay& decay, const GnArgs& gn, bool accumulate, hipStream_t stream,
+                                  int chunks_per_seg, const float* seg_states) {
   FusedArgs a;
   a.q = q;
   a.k = k;
@@ -974,8 +999,13 @@ hipError_t launch_fused_chunkwise(const uint16_t* q, const uint16_t* k, const ui
   a.state_in = state_in;
   a.state_out = state_out;
   const int64_t heads = static_cast<int64_t>(d.B) * d.H;
+  const int nchunks = (d.N + chunk - 1) / chunk;
+  a.chunks_per_seg = chunks_per_seg > 0 && chunks_per_seg < nchunks ? chunks_per_seg : nchunks;
+  a.nseg = (nchunks + a.chunks_per_seg - 1) / a.chunks_per_seg;
+  a.seg_states = seg_states;
+  if (a.nseg > 1 && !seg_states) return hipErrorInvalidValue;
   a.nvt = d.dv / kVT;
-  a.units = static_cast<int>(heads * a.nvt);
+  a.units = static_cast<int>(heads * a.nseg * a.nvt);
   a.mail = static_cast<uint64_t*>(workspace);
   a.H = d.H;
   a.N = d.N;

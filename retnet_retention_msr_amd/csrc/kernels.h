@@ -93,12 +93,23 @@ bool mfma_supports(int dk, int dv);
 // v tile) walks the chunks with its state slab in registers; GroupNorm
 // statistics are exchanged between the v tiles of a head through a small
 // workspace (fused_workspace_bytes). Covers dk 128 and 256, dv a multiple of
-// 256 up to 1024, chunk a multiple of 64.
+// 256 up to 1024, chunk a multiple of 64. With chunks_per_seg below the chunk
+// count the sequences are cut into segments of that many chunks, each walked
+// by its own workgroups from the state seg_states gives it: fp32
+// [B*H][nseg][dk][dv], slot s < nseg-1 the end state of segment s started
+// from zero (segment 0 from state_in), as launch_segment_ends leaves it.
 bool fused_supports(int dk, int dv, int chunk);
 size_t fused_workspace_bytes(int64_t heads, int dv);
 hipError_t launch_fused_chunkwise(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                                   const float* state_in, float* state_out, void* workspace, const Dims& d, int chunk,
-                                  const HeadDecay& decay, const GnArgs& gn, bool accumulate, hipStream_t stream);
+                                  const HeadDecay& decay, const GnArgs& gn, bool accumulate, hipStream_t stream,
+                                  int chunks_per_seg = 0, const float* seg_states = nullptr);
+// End states of segments 0..nseg-2 (segments of chunks_per_seg chunks), each
+// walked from zero (segment 0 from state_in), into seg_states [B*H][nseg][dk][dv]
+// (the MFMA state walk's first mode; dk 128 or 256, dv a multiple of 128).
+hipError_t launch_segment_ends(const uint16_t* k, const uint16_t* v, const float* state_in, float* seg_states,
+                               int chunks_per_seg, const Dims& d, int chunk, const HeadDecay& decay,
+                               hipStream_t stream);
 
 // xPos rotation (xpos.hip): the pairs (x[2i], x[2i+1]) of every position n
 // of q (and of k, unless null) multiplied, as complex numbers, by
@@ -108,6 +119,9 @@ hipError_t launch_fused_chunkwise(const uint16_t* q, const uint16_t* k, const ui
 constexpr int kMaxXposPairs = 128;
 hipError_t launch_xpos_rotate(int dtype, const void* q, const void* k, void* q_out, void* k_out, const float* theta,
                               int BH, int N, int d, int64_t pos0, hipStream_t stream);
+
+// Device-to-device copy of `bytes` bytes on `stream`.
+hipError_t copy_device(void* dst, const void* src, size_t bytes, hipStream_t stream);
 
 // Bytes of the library-owned device scratch (scratch.hip) that the
 // allocation-free chunkwise entry point uses instead of a caller workspace.

@@ -635,6 +635,62 @@ __global__ void __launch_bounds__(kFixThreads) walk_fixup_kernel(FixArgs a, Head
 
 }  // namespace
 
+namespace {
+
+// One walk launch in `mode` (grid: every head, k tile, v tile and launched segment).
+hipError_t launch_walk_mode(WalkArgs& a, int mode, const Dims& d, const HeadDecay& decay, hipStream_t stream) {
+  const bool full = walk_full_dk(d.dk);
+  const bool wide = walk_wide(static_cast<int64_t>(d.B) * d.H, d.dk, d.dv);
+  const int MT = walk_k_tiles(d.dk);
+  const int64_t per_seg = static_cast<int64_t>(d.B) * d.H * a.nkt * a.nvt;
+  a.mode = mode;
+  const int64_t nblocks = per_seg * (mode == 0 ? a.nseg - 1 : a.nseg);
+  const dim3 grid(static_cast<unsigned>(nblocks));
+  if (full && d.dk == 256 && wide) mfma_state_walk2_kernel<2, 4><<<grid, kWalk2Threads, 0, stream>>>(a, decay);
+  else if (full && d.dk == 256) mfma_state_walk2_kernel<2, 2><<<grid, kWalk2Threads, 0, stream>>>(a, decay);
+  else if (full && wide) mfma_state_walk2_kernel<1, 4><<<grid, kWalk2Threads, 0, stream>>>(a, decay);
+  else if (full) mfma_state_walk2_kernel<1, 2><<<grid, kWalk2Threads, 0, stream>>>(a, decay);
+  else if (MT == 2) mfma_state_walk_kernel<2><<<grid, kThreads, 0, stream>>>(a, decay);
+  else mfma_state_walk_kernel<1><<<grid, kThreads, 0, stream>>>(a, decay);
+  return hipGetLastError();
+}
+
+WalkArgs walk_args(const uint16_t* k, const uint16_t* v, const float* state_in, float* state_out,
+                   uint16_t* chunk_states, float* seg_states, int chunks_per_seg, const Dims& d, int chunk) {
+  WalkArgs a;
+  a.k = k;
+  a.v = v;
+  a.state_in = state_in;
+  a.state_out = state_out;
+  a.chunk_states = chunk_states;
+  a.seg_states = seg_states;
+  a.H = d.H;
+  a.N = d.N;
+  a.dk = d.dk;
+  a.dv = d.dv;
+  a.chunk = chunk;
+  a.nchunks = (d.N + chunk - 1) / chunk;
+  a.chunks_per_seg = chunks_per_seg;
+  a.nseg = (a.nchunks + chunks_per_seg - 1) / chunks_per_seg;
+  const bool full = walk_full_dk(d.dk);
+  const int MT = walk_k_tiles(d.dk);
+  a.nkt = full ? 1 : d.dk / (32 * MT);
+  const bool wide = walk_wide(static_cast<int64_t>(d.B) * d.H, d.dk, d.dv);
+  a.nvt = d.dv / (full ? (wide ? 256 : kWalk2VT) : kWalkVT);
+  a.mode = 0;
+  return a;
+}
+
+}  // namespace
+
+hipError_t launch_segment_ends(const uint16_t* k, const uint16_t* v, const float* state_in, float* seg_states,
+                               int chunks_per_seg, const Dims& d, int chunk, const HeadDecay& decay,
+                               hipStream_t stream) {
+  WalkArgs a = walk_args(k, v, state_in, nullptr, nullptr, seg_states, chunks_per_seg, d, chunk);
+  if (a.nseg < 2) return hipSuccess;
+  return launch_walk_mode(a, 0, d, decay, stream);
+}
+
 hipError_t launch_mfma_state_walk(const uint16_t* k, const uint16_t* v, const float* state_in, float* state_out,
                                   uint16_t* chunk_states, float* seg_states, int chunks_per_seg, const Dims& d,
                                   int chunk, const HeadDecay& decay, hipStream_t stream) {

@@ -156,6 +156,13 @@ def test_workspace_bytes(lib):
     # per chunk and head (no segments here).
     assert st(8, 16, 8192, 256, 512, 512, 1) == 8 * 16 * 16 * 256 * 512 * 2
     assert ws(8, 16, 8192, 256, 512, 512, 1) == st(8, 16, 8192, 256, 512, 512, 1)
+    # Few heads at chunk 64: the single pass over segments of the sequence (32
+    # (head, v tile) pairs, so 8 segments of 128 chunks): the mailbox of 256
+    # units, the segments' fp32 end states and room for a copy of state_in,
+    # 72.5 MiB instead of the 4 GiB of bf16 chunk states the two stages need.
+    seg = 16 * 8 * 2 * 2048 + 16 * 8 * 256 * 512 * 4 + 16 * 256 * 512 * 4
+    assert ws(1, 16, 65536, 256, 512, 64, 1) == seg
+    assert st(1, 16, 65536, 256, 512, 64, 1) > 4 * 2**30
     assert ws(8, 16, 8192, 256, 512, 256, 1) == st(8, 16, 8192, 256, 512, 256, 1)
     # Few heads (the single-pass kernel would leave most of the GPU idle): the
     # two-stage path and its chunk states, cut into segments whose fp32 end
@@ -270,7 +277,8 @@ def _launches(lib):
 @shim_only
 @pytest.mark.parametrize("shape", [
     (8, 16, 8192, 256, 512, 512, 1),   # the 6.7B-shaped prefill
-    (1, 16, 65536, 256, 512, 64, 1),   # one long sequence, small chunks (segmented walk, two passes)
+    (1, 16, 65536, 256, 512, 64, 1),   # one long sequence, small chunks (segmented single pass)
+    (1, 16, 65536, 256, 128, 64, 1),   # one long sequence, dv 128: segmented walk (two passes)
     (1, 16, 65536, 256, 512, 512, 1),  # segmented walk with the fix-up pass
     (2, 8, 2048, 256, 512, 256, 1),
     (1, 1, 64, 16, 16, 16, 0),         # fp32 generic path

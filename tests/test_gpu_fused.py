@@ -55,6 +55,32 @@ def _is_single_pass(B, H, N, dk, dv, C):
     return ret.chunkwise_workspace_bytes(B, H, N, dk, dv, C) == units * 2048
 
 
+def _align(x):
+    return (x + 255) // 256 * 256
+
+
+def _segments(B, H, N, dk, dv, C):
+    """Segments the planner cuts each sequence into for the single pass (the
+    rule the header states): enough for about 256 (head, segment, v tile)
+    units, at least 4 chunks each, at least 192 units in all."""
+    base = B * H * (dv // 256)
+    nchunks = -(-N // C)
+    nseg = min(-(-256 // base), nchunks // 4)
+    assert nseg >= 2 and base * nseg >= 192, "not a segmented plan"
+    cps = -(-nchunks // nseg)
+    return -(-nchunks // cps)
+
+
+def _is_segmented_single_pass(B, H, N, dk, dv, C):
+    """Workspace of the segmented single pass: the exchange mailbox of every
+    (head, segment, v tile), the segments' fp32 end states, and room for a copy
+    of state_in."""
+    nseg = _segments(B, H, N, dk, dv, C)
+    want = (_align(B * H * nseg * (dv // 256) * 2048) + _align(B * H * nseg * dk * dv * 4)
+            + _align(B * H * dk * dv * 4))
+    return ret.chunkwise_workspace_bytes(B, H, N, dk, dv, C) == want
+
+
 CASES = [
     # B, H, N, dk, dv, chunk, gn, affine, state
     (6, 16, 600, 256, 512, 128, True, True, True),     # ragged last chunk (64 + 24 rows), state in/out
@@ -194,3 +220,53 @@ def test_long_chunks_plan_the_two_stages(C):
     B, H, N, dk, dv = 6, 16, 1024, 256, 512
     assert not _is_single_pass(B, H, N, dk, dv, C)
     assert ret.chunkwise_workspace_bytes(B, H, N, dk, dv, C) == ret.chunk_stages_workspace_bytes(B, H, N, dk, dv, C)
+
+
+SEG_CASES = [
+    # B, H, N, dk, dv, chunk, gn, affine, state: few heads, the sequence cut into segments
+    (1, 16, 4096, 256, 512, 64, True, True, True),     # 8 segments of 8 chunks, state in and out
+    (1, 8, 4100, 256, 512, 64, True, False, True),     # 13 segments, ragged last chunk (4 rows)
+    (1, 16, 4096, 256, 512, 128, False, False, False), # chunk 128, no GroupNorm
+    (2, 16, 2048, 128, 256, 64, True, True, True),     # dk 128, one v tile
+]
+
+
+@pytest.mark.parametrize("B, H, N, dk, dv, C, gn_on, affine, with_state", SEG_CASES)
+def test_segmented_single_pass_matches_oracle(B, H, N, dk, dv, C, gn_on, affine, with_state):
+    _announce(f"segmented single pass B={B} H={H} N={N} dk={dk} dv={dv} chunk={C} gn={gn_on} state={with_state}")
+    assert _is_segmented_single_pass(B, H, N, dk, dv, C)
+    q, k, v = synthetic.make_qkv(B, H, N, dk, dv, dtype=torch.bfloat16, seed=3700 + N + C)
+    g = synthetic.head_gammas(H)
+    S0 = synthetic.make_state(B, H, dk, dv, seed=3701 + N, std=0.5) if with_state else None
+    w = b = None
+    if affine:
+        w, b = synthetic.make_gn_affine(H, dv, seed=3702)
+    gn = ret.GroupNorm(1e-5, w.to(DEV) if w is not None else None, b.to(DEV) if b is not None else None) \
+        if gn_on else None
+    raw, S_ref = orc.chunkwise(q, k, v, g, C, state_in=S0)
+    ref = orc.group_norm(raw, eps=1e-5, weight=w, bias=b) if gn_on else raw
+    o, S = ret.chunkwise(q.to(DEV), k.to(DEV), v.to(DEV), g, C, state_in=None if S0 is None else S0.to(DEV),
+                         state_out=True, gn=gn)
+    torch.cuda.synchronize()
+    _check(o, ref, "o")
+    _check(S, S_ref, "state")
+
+
+def test_segmented_single_pass_aliased_state_and_gate():
+    """state_out aliasing state_in (read from a copy, since the first segment's
+    workgroups may still read it while the last one's write), with the gate."""
+    B, H, N, dk, dv, C = 1, 16, 2048, 256, 512, 64
+    _announce("segmented single pass, aliased state, gated")
+    assert _is_segmented_single_pass(B, H, N, dk, dv, C)
+    q, k, v = synthetic.make_qkv(B, H, N, dk, dv, dtype=torch.bfloat16, seed=3800)
+    g = synthetic.head_gammas(H)
+    S0 = synthetic.make_state(B, H, dk, dv, seed=3801, std=0.5)
+    gate = synthetic.make_gate((B, H, N, dv), dtype=torch.bfloat16, seed=3802)
+    raw, S_ref = orc.chunkwise(q, k, v, g, C, state_in=S0)
+    Sd = S0.to(DEV)
+    o, S = ret.chunkwise(q.to(DEV), k.to(DEV), v.to(DEV), g, C, state_in=Sd, state_out=Sd, gn=ret.GroupNorm(1e-5),
+                         gate=gate.to(DEV))
+    torch.cuda.synchronize()
+    assert S.data_ptr() == Sd.data_ptr()
+    _check(o, orc.gated_group_norm(raw, _np(gate), eps=1e-5), "gated o")
+    _check(S, S_ref, "state")
