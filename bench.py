@@ -438,36 +438,47 @@ def backward_min_bytes(B, H, N, dk=DK, dv=DV):
     return float(B * H * N * ((2 * dk + 2 * dv) + (2 * dk + dv)) * 2)
 
 
-def backward_pass(ret, torch, dev, stream, qd, kd, vd, gamma, steps, warmup=3):
-    """The backward pass of the same prefill (no states): dQ, dK, dV for a seeded dO."""
+def backward_pass(ret, torch, dev, stream, qd, kd, vd, gamma, steps, warmup=3, chunks=(CHUNK, 64)):
+    """The backward pass of the same prefill (no states): dQ, dK, dV for a
+    seeded dO, at the forward's chunk and at chunk 64, where its retentions
+    plan the single-pass kernel (the gradients do not depend on the chunk)."""
     gen = torch.Generator(device=dev).manual_seed(BACKWARD_SEED)
     dO = torch.randn(B, H, N, DV, generator=gen, device=dev).to(torch.bfloat16)
     grads = (torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd))
-    ws = torch.empty(ret.chunkwise_backward_workspace_bytes(B, H, N, DK, DV, CHUNK), dtype=torch.uint8, device=dev)
-    for _ in range(warmup):
-        ret.chunkwise_backward(qd, kd, vd, dO, gamma, CHUNK, workspace=ws, grads=grads)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        ret.chunkwise_backward(qd, kd, vd, dO, gamma, CHUNK, workspace=ws, grads=grads)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    flop = backward_flops(B, H, N, CHUNK)
-    nbytes = backward_min_bytes(B, H, N)
-    del dO, grads, ws
-    return {
-        "workload": "backward of the prefill above without GroupNorm or states: dQ, dK, dV for bf16 dO ~ N(0,1)",
-        "steps": steps,
-        "ms": ms,
-        "tokens_per_s": B * N / (ms * 1e-3),
-        "executed_flop": flop,
-        "mfma_tflops": flop / (ms * 1e-3) / 1e12,
-        "mfma_frac": flop / (ms * 1e-3) / PEAK_BF16,
-        "min_bytes": nbytes,
-        "hbm_frac_of_min_bytes": nbytes / (ms * 1e-3) / PEAK_HBM,
-    }
+    out = {}
+    for C in chunks:
+        ws = torch.empty(ret.chunkwise_backward_workspace_bytes(B, H, N, DK, DV, C), dtype=torch.uint8, device=dev)
+        for _ in range(warmup):
+            ret.chunkwise_backward(qd, kd, vd, dO, gamma, C, workspace=ws, grads=grads)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            ret.chunkwise_backward(qd, kd, vd, dO, gamma, C, workspace=ws, grads=grads)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        flop = backward_flops(B, H, N, C)
+        nbytes = backward_min_bytes(B, H, N)
+        del ws
+        out[C] = {
+            "workload": f"backward of the prefill above without GroupNorm or states at chunk {C}: dQ, dK, dV "
+                        "for bf16 dO ~ N(0,1)",
+            "chunk": C,
+            "steps": steps,
+            "ms": ms,
+            "tokens_per_s": B * N / (ms * 1e-3),
+            "executed_flop": flop,
+            "mfma_tflops": flop / (ms * 1e-3) / 1e12,
+            "mfma_frac": flop / (ms * 1e-3) / PEAK_BF16,
+            "min_bytes": nbytes,
+            "hbm_frac_of_min_bytes": nbytes / (ms * 1e-3) / PEAK_HBM,
+        }
+    del dO, grads
+    res = dict(out[chunks[0]])
+    for C in chunks[1:]:
+        res[f"chunk_{C}"] = out[C]
+    return res
 
 
 def xpos_prologue(ret, torch, dev, stream, qd, kd, steps, warmup=5):
