@@ -268,7 +268,13 @@ int retention_xpos_rotate(const void* q, const void* k, void* q_out, void* k_out
  * of the forward call. Each gradient is evaluated as a retention of its own
  * (grad_q forward in time; grad_k and grad_v over the token-reversed sequence)
  * with the chunkwise kernels at the given chunk; a width above 256 is split
- * into parts whose results are summed. With grad_state_out given, every
+ * into parts whose results are summed. For bf16 at chunk <= 128 (after
+ * clamping), dk 256 and dv a multiple of 256 (at most 1024), with at least
+ * 192 (head, 256-column) units in each retention, the three retentions run on
+ * the single-pass kernel reading the inputs in place (reverse order, row
+ * pitch) and the workspace holds the parts of grad_q / grad_k, four fp32
+ * state buffers and the exchange words; otherwise the operands are first
+ * copied (reversed, split) into the workspace. With grad_state_out given, every
  * gamma must be a normal float (>= FLT_MIN, about 1.2e-38): the final-state
  * gradient is divided by gamma on its way in, and RET_ERR_UNSUPPORTED is
  * returned otherwise. workspace must hold

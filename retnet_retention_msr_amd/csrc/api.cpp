@@ -216,6 +216,11 @@ hipError_t launch_output(const ChunkPlan& p, const void* q, const void* k, const
 constexpr int kPartWidth = 256;  // widest query/key dimension the MFMA kernels take
 
 struct BackwardPlan {
+  // Single-pass plan: every retention on the single-pass kernel, reading the
+  // operands in place (row pitches, reverse order) with the parts of the dQ
+  // and dK retentions in one launch each, summed afterwards; no copies.
+  bool direct;
+  size_t tparts, mail;  // direct: part outputs [nparts][B*H*N*dk], exchange mailbox
   int nparts;  // parts of the dv-wide query/key dimension of the dQ and dK retentions
   int part_w;
   size_t qf, kf, dof, oa, dos, vs, dofs, vfs, kpart;  // byte offsets (token-row buffers)
@@ -224,6 +229,20 @@ struct BackwardPlan {
   size_t cw_bytes;
   size_t total;
 };
+
+// Whether the backward runs directly on the single-pass kernel: bf16, the
+// retentions' widths and chunk within its range, enough (head, part, v tile)
+// units for each launch without segments, and reverse-order offsets within
+// 2^30 bytes.
+bool backward_direct(int B, int H, int N, int dk, int dv, int chunk, int dtype, int nparts, int part_w) {
+  if (dtype != RET_BF16 || chunk > kFusedMaxChunk) return false;
+  if (!ret::fused_supports(dk, dv, chunk) || !ret::fused_supports(part_w, dk, chunk)) return false;
+  if (dv % part_w != 0) return false;
+  const int64_t heads = static_cast<int64_t>(B) * H;
+  if (heads * (dv / 256) < kFusedMinUnits || heads * nparts * (dk / 256) < kFusedMinUnits) return false;
+  const int64_t widest = std::max(dk, dv);
+  return (static_cast<int64_t>(N) - 1) * widest * 2 + widest * 2 < (int64_t{1} << 30);
+}
 
 BackwardPlan plan_backward(int B, int H, int N, int dk, int dv, int chunk, int dtype) {
   BackwardPlan p{};
@@ -238,6 +257,18 @@ BackwardPlan plan_backward(int B, int H, int N, int dk, int dv, int chunk, int d
     off += align_up(bytes);
     return at;
   };
+  p.direct = backward_direct(B, H, N, dk, dv, chunk, dtype, p.nparts, p.part_w);
+  if (p.direct) {
+    const int64_t heads = static_cast<int64_t>(B) * H;
+    p.tparts = take(static_cast<size_t>(p.nparts) * tok * dk * es);
+    p.s_a = take(st);
+    p.s_t = take(st);
+    p.s_0t = take(st);
+    p.s_nt = take(st);
+    p.mail = take(std::max(ret::fused_workspace_bytes(heads, dv), ret::fused_workspace_bytes(heads * p.nparts, dk)));
+    p.total = off;
+    return p;
+  }
   p.qf = take(tok * dk * es);
   p.kf = take(tok * dk * es);
   p.dof = take(tok * dv * es);
@@ -502,6 +533,67 @@ int retention_chunkwise_backward(const void* q, const void* k, const void* v, co
   auto st_at = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   auto ok = [](hipError_t e) { return e == hipSuccess; };
   char* cw = ws + p.cw;
+
+  if (p.direct) {
+    // The same three retentions as below, each one launch of the single-pass
+    // kernel reading Q, K, V and dO where they are: reverse order in place of
+    // reversed copies, row pitch dv and column offsets in place of the
+    // 256-column parts, the parts of one gradient side by side in a launch.
+    const int P = p.nparts, pw = p.part_w;
+    const int64_t st_part = static_cast<int64_t>(B) * H * pw * dk;  // fp32 elements between state parts
+    const GnArgs nogn{};
+    auto u16 = [](const void* x) { return static_cast<const uint16_t*>(x); };
+    float* s_a = nullptr;
+    if (grad_state_out) {
+      s_a = st_at(p.s_a);
+      if (!ok(ret::launch_state_prep(grad_state_out, s_a, B, H, dk, dv, false, dv, 0, inv_gamma, s)))
+        return RET_ERR_HIP;
+    }
+    float* s_t = grad_state_in ? st_at(p.s_t) : nullptr;
+    // dV (and the state gradient): reverse-time retention, query K, key Q, value dO.
+    ret::FusedLayout rv;
+    rv.reverse = true;
+    if (!ok(ret::launch_fused_chunkwise(u16(k), u16(q), u16(grad_o), static_cast<uint16_t*>(grad_v), s_a, s_t,
+                                        at(p.mail), Dims{B, H, N, dk, dv}, chunk, decay, nogn, false, s, 0, nullptr,
+                                        &rv)))
+      return RET_ERR_HIP;
+    if (grad_state_in) {
+      if (!ok(ret::launch_state_prep(s_t, grad_state_in, B, H, dk, dv, false, dv, 0, fwd_gamma, s)))
+        return RET_ERR_HIP;
+    }
+    float* s_0t = nullptr;
+    if (state_in) {
+      s_0t = st_at(p.s_0t);
+      if (!ok(ret::launch_state_prep(state_in, s_0t, B, H, dk, dv, true, pw, st_part, nullptr, s))) return RET_ERR_HIP;
+    }
+    float* s_nt = nullptr;
+    if (grad_state_out) {
+      s_nt = st_at(p.s_nt);
+      if (!ok(ret::launch_state_prep(grad_state_out, s_nt, B, H, dk, dv, true, pw, st_part, inv_gamma, s)))
+        return RET_ERR_HIP;
+    }
+    uint16_t* tp = static_cast<uint16_t*>(at(p.tparts));
+    ret::FusedLayout lq;
+    lq.ldq = dv;
+    lq.ldk = dv;
+    lq.nparts = P;
+    lq.q_part = pw;
+    lq.k_part = pw;
+    lq.o_part = tok * dk;
+    lq.s_part = st_part;
+    const Dims dd{B, H, N, pw, dk};
+    // dQ parts: query dO, key V, value K, starting state S0^T (rows of the part).
+    if (!ok(ret::launch_fused_chunkwise(u16(grad_o), u16(v), u16(k), tp, s_0t, nullptr, at(p.mail), dd, chunk, decay,
+                                        nogn, false, s, 0, nullptr, &lq)))
+      return RET_ERR_HIP;
+    if (!ok(ret::launch_sum_parts(dtype, tp, grad_q, rows, dk, P, tok * dk, false, s))) return RET_ERR_HIP;
+    // dK parts (reversed time): query V, key dO, value Q, starting state dS_N^T / gamma.
+    lq.reverse = true;
+    if (!ok(ret::launch_fused_chunkwise(u16(v), u16(grad_o), u16(q), tp, s_nt, nullptr, at(p.mail), dd, chunk, decay,
+                                        nogn, false, s, 0, nullptr, &lq)))
+      return RET_ERR_HIP;
+    return status_of(ret::launch_sum_parts(dtype, tp, grad_k, rows, dk, P, tok * dk, false, s));
+  }
 
   // Operand copies, each source read once: Q and K token-reversed; dO
   // token-reversed whole (the dV retention's value) and, when the dv-wide

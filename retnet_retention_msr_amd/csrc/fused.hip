@@ -96,6 +96,14 @@ struct FusedArgs {
   // segment s < nseg - 1 when it starts from zero (segment 0 from state_in).
   const float* seg_states;
   int nseg, chunks_per_seg;
+  // Row pitches (elements) of q and k (dk when they are whole tensors). With
+  // `reverse` every sequence is taken in reverse token order: logical row t
+  // of q, k, v and o is memory row N-1-t (a reverse-time retention without
+  // reversed copies). `nparts` independent retentions share one launch: part
+  // p reads q and k q_part and k_part elements further, writes o o_part
+  // further and starts from state_in s_part further (no segments then).
+  int ldq, ldk, reverse, nparts;
+  int64_t q_part, k_part, o_part, s_part;
   int H, N, dk, dv, chunk, nchunks, nvt, units;
   int spin_limit;         // polls of a partner's flag before giving up on it
 };
@@ -141,7 +149,10 @@ __device__ __forceinline__ bf16x8 state_operand(const floatx16& t, int s) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
-template <int MT, int EPI>
+// GEN: the general layout (row pitches, reverse order, parts); the plain
+// instances fold those to dk, forward order and one part, keeping the
+// registers they would hold.
+template <int MT, int EPI, bool GEN>
 __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, HeadDecay decay, GnArgs gn) {
   constexpr int XK = kTileF * kVT + kTileF * kPitch;  // V tile at 0, K block after it
   constexpr int PT = kRowsF * kTileF;                 // score tile (64 queries x 32 keys)
@@ -166,6 +177,8 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
   const int l16 = lane & 15;
   const int vcol0 = wave * 32;  // this wave's columns within the v tile
   const int dk = a.dk, dv = a.dv;
+  const int ldq = GEN ? a.ldq : dk, ldk = GEN ? a.ldk : dk;
+  const int nparts = GEN ? a.nparts : 1;
 
   // ---- per-lane LDS offsets (elements), fixed for the kernel; the empty asm
   // keeps each read one opaque offset away from its array, so the compiler
@@ -251,7 +264,7 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
   {
     const int row = 2 * wave + (lane >> 5);
     const int g = (lane & 31) ^ (row & 15);
-    kqoff = g * 8 < dk ? (row * dk + g * 8) * 2 : kOutOfRange;
+    kqoff = g * 8 < dk ? (row * ldk + g * 8) * 2 : kOutOfRange;
   }
   // The Q block is copied by waves 0-3 only (pieces c = wave + 4m, m = 0..7,
   // rows 2c, 2c+1): wave 7, which publishes the GroupNorm statistics and so
@@ -264,7 +277,7 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
     for (int par = 0; par < 2; ++par) {
       const int row = 2 * (wave & 3) + 8 * par + (l >> 5);
       const int g = (l & 31) ^ (row & 15);
-      qoff[par] = g * 8 < dk ? (row * dk + g * 8) * 2 : kOutOfRange;
+      qoff[par] = g * 8 < dk ? (row * ldq + g * 8) * 2 : kOutOfRange;
     }
   };
   // The same pieces of a K block in the V tiles' layout (the update pass):
@@ -275,7 +288,7 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
     asm volatile("" : "+v"(l));
     const int row = 2 * wave + (l >> 5);
     const int pos = x_pos(row, l & 31);
-    return pos * 8 < dk ? (row * dk + pos * 8) * 2 : kOutOfRange;
+    return pos * 8 < dk ? (row * ldk + pos * 8) * 2 : kOutOfRange;
   };
   // A piece c of a V tile: lane l fills granule 64c + l of the swizzled tile,
   // row 2c + l/32, slot l%32, taking source granule x_pos(row, slot) of the
@@ -295,8 +308,9 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
     // Unit = (head, segment, v tile), v tile fastest: the v tiles of a
     // segment (which exchange GroupNorm statistics) are neighbours.
     const int vt = unit % a.nvt;
-    const int seg = (unit / a.nvt) % a.nseg;
-    const int64_t bh = unit / a.nvt / a.nseg;
+    const int part = (unit / a.nvt) % nparts;
+    const int seg = (unit / a.nvt / nparts) % a.nseg;
+    const int64_t bh = unit / a.nvt / nparts / a.nseg;
     const int h = static_cast<int>(bh % a.H);
     const float lg = decay.log2g[h];
     // This unit's rows: [row0, row0 + Nu) of the head's sequence, chunks
@@ -305,11 +319,16 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
     const int Nu = min(a.chunks_per_seg * a.chunk, a.N - row0);
     const int ncu = (Nu + a.chunk - 1) / a.chunk;
     const int64_t rbase = bh * static_cast<int64_t>(a.N) + row0;  // first row in [B*H*N]
-    const uint16_t* qh = a.q + rbase * dk;
-    const uint16_t* kh = a.k + rbase * dk;
-    const uint16_t* vh = a.v + rbase * dv + vt * kVT;
-    uint16_t* oh = a.o + rbase * dv + vt * kVT;
-    float* const state_out = seg == a.nseg - 1 ? a.state_out : nullptr;
+    const bool rev = GEN && a.reverse != 0;
+    // Forward: the unit's first row. Reverse: the head's memory row 0 (the
+    // unit's logical row t sits at memory row N-1-t).
+    const int64_t mrow = rev ? bh * static_cast<int64_t>(a.N) : rbase;
+    const uint16_t* qh = a.q + part * a.q_part + mrow * ldq;
+    const uint16_t* kh = a.k + part * a.k_part + mrow * ldk;
+    const uint16_t* vh = a.v + mrow * dv + vt * kVT;
+    uint16_t* oh = a.o + part * a.o_part + mrow * dv + vt * kVT;
+    const int nm1 = a.N - 1 - row0;  // reverse: memory row of logical row t is nm1 - t
+    float* const state_out = seg == a.nseg - 1 ? (a.state_out ? a.state_out + part * a.s_part : nullptr) : nullptr;
     const int64_t dkdv = static_cast<int64_t>(dk) * dv;
     uint64_t* mymail = a.mail + static_cast<int64_t>(unit) * 2 * kMailWords;
     const int group0 = unit - vt;  // first unit of this head's v tiles
@@ -327,8 +346,9 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
     // The state this unit starts from: state_in for the first segment; for a
     // later one starting at row0, sum over earlier segments s' of
     // gamma^(row0 - end_s') U_s' (U_0 already carries state_in).
-    const bool has_in = seg > 0 || a.state_in != nullptr;
-    const int nsrc = seg > 0 ? seg : (a.state_in ? 1 : 0);
+    const float* const state_in = a.state_in ? a.state_in + part * a.s_part : nullptr;
+    const bool has_in = seg > 0 || state_in != nullptr;
+    const int nsrc = seg > 0 ? seg : (state_in ? 1 : 0);
     // The state moves between HBM and the accumulators through LDS, four
     // 32-row tiles (32 KiB of fp32 each) at a time in sQ and the three buffer
     // sets: the copies are whole 1-KiB rows, and a lane's 16 accumulator
@@ -336,7 +356,7 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
     uint16_t* const stage[4] = {sQ, sXK0, sXK1, sXK2};
     const int acc_lds = (4 * (lane >> 5)) * kVT + vcol0 + l32;  // float index of accumulator 0
     for (int src = 0; src < nsrc; ++src) {
-      const float* sbase = (seg > 0 ? a.seg_states + (bh * a.nseg + src) * dkdv : a.state_in + bh * dkdv) + vt * kVT;
+      const float* sbase = (seg > 0 ? a.seg_states + (bh * a.nseg + src) * dkdv : state_in + bh * dkdv) + vt * kVT;
       const float fsrc = seg > 0 ? gpow(lg, static_cast<float>(row0 - (src + 1) * a.chunks_per_seg * a.chunk)) : 1.f;
 #pragma unroll
       for (int g4 = 0; g4 < MT; g4 += 4) {
@@ -363,36 +383,98 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
 
     // Copies.
     // (Waves 0-3 only; kQCopies copies each.)
+    // In reverse order a copy's descriptor spans the head's rows and each
+    // lane's offset carries its memory row nm1 - (t0 + r): rows before the
+    // head's first (logical rows past the end) come out negative, past the
+    // descriptor's range as unsigned numbers, and so read as zero.
+    const int rev_q_range = ((a.N - 1) * ldq + dk) * 2;
+    const int rev_k_range = ((a.N - 1) * ldk + dk) * 2;
+    const int rev_v_range = ((a.N - 1) * dv + kVT) * 2;
+    // Row r of a tile's piece layout and the byte offset of its column part
+    // (the same permutations as the forward offsets above).
+    auto rev_row = [&](int pieces_per_row_step) __attribute__((always_inline)) {
+      int l = lane;
+      asm volatile("" : "+v"(l));
+      return 2 * (wave & (pieces_per_row_step - 1)) + (l >> 5);
+    };
     auto copy_q = [&](int q0) __attribute__((always_inline)) {
       if (wave < 4) {
-        int qoff[2];
-        q_offsets(qoff);
-        const int rows = min(kRowsF, Nu - q0);
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(qh + static_cast<int64_t>(q0) * dk, rows * dk * 2);
+        if (!rev) {
+          int qoff[2];
+          q_offsets(qoff);
+          const int rows = min(kRowsF, Nu - q0);
+          const __amdgpu_buffer_rsrc_t r =
+              make_rsrc(qh + static_cast<int64_t>(q0) * ldq, ((rows - 1) * ldq + dk) * 2);
 #pragma unroll
-        for (int m = 0; m < 8; ++m) dma16s(r, sQ + (wave + 4 * m) * 512, qoff[m & 1], 8 * (m & ~1) * dk * 2);
+          for (int m = 0; m < 8; ++m) dma16s(r, sQ + (wave + 4 * m) * 512, qoff[m & 1], 8 * (m & ~1) * ldq * 2);
+        } else {
+          const __amdgpu_buffer_rsrc_t r = make_rsrc(qh, rev_q_range);
+          const int row = rev_row(4);
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const int rr = row + 8 * m;
+            const int g = (lane & 31) ^ (rr & 15);
+            const int off = g * 8 < dk ? ((nm1 - q0 - rr) * ldq + g * 8) * 2 : kOutOfRange;
+            dma16s(r, sQ + (wave + 4 * m) * 512, off, 0);
+          }
+        }
       }
     };
     auto copy_k = [&](int t0, uint16_t* set) __attribute__((always_inline)) {
-      const int rows = min(kTileF, Nu - t0);
-      const __amdgpu_buffer_rsrc_t r = make_rsrc(kh + static_cast<int64_t>(t0) * dk, rows * dk * 2);
+      if (!rev) {
+        const int rows = min(kTileF, Nu - t0);
+        const __amdgpu_buffer_rsrc_t r =
+            make_rsrc(kh + static_cast<int64_t>(t0) * ldk, ((rows - 1) * ldk + dk) * 2);
 #pragma unroll
-      for (int m = 0; m < 2; ++m) dma16s(r, set + kTileF * kVT + (wave + kWavesF * m) * 512, kqoff, m * 16 * dk * 2);
+        for (int m = 0; m < 2; ++m)
+          dma16s(r, set + kTileF * kVT + (wave + kWavesF * m) * 512, kqoff, m * 16 * ldk * 2);
+      } else {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(kh, rev_k_range);
+        const int row = rev_row(8);
+        const int g = (lane & 31) ^ (row & 15);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int off = g * 8 < dk ? ((nm1 - t0 - row - 16 * m) * ldk + g * 8) * 2 : kOutOfRange;
+          dma16s(r, set + kTileF * kVT + (wave + kWavesF * m) * 512, off, 0);
+        }
+      }
     };
     // K block at t0 for the update pass: into the V-tile slot layout of `set`'s K part.
     auto copy_kx = [&](int t0, uint16_t* set) __attribute__((always_inline)) {
-      const int kxoff = kx_offset();
-      const int rows = min(kTileF, Nu - t0);
-      const __amdgpu_buffer_rsrc_t r = make_rsrc(kh + static_cast<int64_t>(t0) * dk, rows * dk * 2);
+      if (!rev) {
+        const int kxoff = kx_offset();
+        const int rows = min(kTileF, Nu - t0);
+        const __amdgpu_buffer_rsrc_t r =
+            make_rsrc(kh + static_cast<int64_t>(t0) * ldk, ((rows - 1) * ldk + dk) * 2);
 #pragma unroll
-      for (int m = 0; m < 2; ++m) dma16s(r, set + kTileF * kVT + (wave + kWavesF * m) * 512, kxoff, m * 16 * dk * 2);
+        for (int m = 0; m < 2; ++m)
+          dma16s(r, set + kTileF * kVT + (wave + kWavesF * m) * 512, kxoff, m * 16 * ldk * 2);
+      } else {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(kh, rev_k_range);
+        const int row = rev_row(8);
+        const int pos = x_pos(row, lane & 31);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int off = pos * 8 < dk ? ((nm1 - t0 - row - 16 * m) * ldk + pos * 8) * 2 : kOutOfRange;
+          dma16s(r, set + kTileF * kVT + (wave + kWavesF * m) * 512, off, 0);
+        }
+      }
     };
     auto copy_v = [&](int t0, uint16_t* set) __attribute__((always_inline)) {
-      const int rows = min(kTileF, Nu - t0);
-      const __amdgpu_buffer_rsrc_t r =
-          make_rsrc(vh + static_cast<int64_t>(t0) * dv, ((rows - 1) * dv + kVT) * 2);
+      if (!rev) {
+        const int rows = min(kTileF, Nu - t0);
+        const __amdgpu_buffer_rsrc_t r =
+            make_rsrc(vh + static_cast<int64_t>(t0) * dv, ((rows - 1) * dv + kVT) * 2);
 #pragma unroll
-      for (int m = 0; m < 2; ++m) dma16s(r, set + (wave + kWavesF * m) * 512, voff, m * 16 * dv * 2);
+        for (int m = 0; m < 2; ++m) dma16s(r, set + (wave + kWavesF * m) * 512, voff, m * 16 * dv * 2);
+      } else {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(vh, rev_v_range);
+        const int row = rev_row(8);
+        const int pos = x_pos(row, lane & 31);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          dma16s(r, set + (wave + kWavesF * m) * 512, ((nm1 - t0 - row - 16 * m) * dv + pos * 8) * 2, 0);
+      }
     };
 
     int ex = 0;  // exchanges published by this unit
@@ -552,30 +634,61 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
       asm volatile("" : "+v"(l));
       return ((4 * (l >> 5) + (l & 1)) * dv + vcol0 + ((l & 31) & ~1)) * 2;
     };
+    // Reverse order: the lane's row in a group of 8 and its column byte
+    // offset (memory row nm1 - (pq0 + row0 + that row)).
+    auto rev_store = [&](int& rr, int& cb) __attribute__((always_inline)) {
+      int l = lane;
+      asm volatile("" : "+v"(l));
+      rr = 4 * (l >> 5) + (l & 1);
+      cb = (vcol0 + ((l & 31) & ~1)) * 2;
+    };
     auto load_epi = [&](uint32_t (&gv)[2][4][2], int pq0, int pqvalid) __attribute__((always_inline)) {
       if constexpr (EPI != 0) {
-        const int so = store_offset();
-        const uint16_t* gbase = EPI == 1 ? static_cast<const uint16_t*>(gn.gate) : a.o;
-        const uint16_t* gblk = gbase + (rbase + pq0) * static_cast<int64_t>(dv) + vt * kVT;
+        const uint16_t* gbase = EPI == 1 ? static_cast<const uint16_t*>(gn.gate) : a.o + part * a.o_part;
+        if (!rev) {
+          const int so = store_offset();
+          const uint16_t* gblk = gbase + (rbase + pq0) * static_cast<int64_t>(dv) + vt * kVT;
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
+          for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int row0 = qt * 32 + 8 * g;
-            const int nrows = min(max(pqvalid - row0, 0), 8);
-            const __amdgpu_buffer_rsrc_t r = make_rsrc(gblk + row0 * dv, nrows > 0 ? ((nrows - 1) * dv + kVT) * 2 : 0);
+            for (int g = 0; g < 4; ++g) {
+              const int row0 = qt * 32 + 8 * g;
+              const int nrows = min(max(pqvalid - row0, 0), 8);
+              const __amdgpu_buffer_rsrc_t r =
+                  make_rsrc(gblk + row0 * dv, nrows > 0 ? ((nrows - 1) * dv + kVT) * 2 : 0);
 #pragma unroll
-            for (int hp = 0; hp < 2; ++hp)
-              gv[qt][g][hp] = __builtin_amdgcn_raw_buffer_load_b32(r, so + 2 * hp * dv * 2, 0, 0);
-          }
+              for (int hp = 0; hp < 2; ++hp)
+                gv[qt][g][hp] = __builtin_amdgcn_raw_buffer_load_b32(r, so + 2 * hp * dv * 2, 0, 0);
+            }
+        } else {
+          int rr, cb;
+          rev_store(rr, cb);
+          const __amdgpu_buffer_rsrc_t r = make_rsrc(gbase + mrow * dv + vt * kVT, rev_v_range);
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+              for (int hp = 0; hp < 2; ++hp) {
+                // Rows past the block's end lie before the head's first row:
+                // negative offsets, out of the descriptor's range, read as zero.
+                const int row = pq0 + qt * 32 + 8 * g + rr + 2 * hp;
+                gv[qt][g][hp] = __builtin_amdgcn_raw_buffer_load_b32(r, (nm1 - row) * dv * 2 + cb, 0, 0);
+              }
+        }
       }
     };
     // Normalise a block's accumulators (rows pq0.., pqvalid valid) and store
     // them: kOStores stores per lane.
     auto store_block = [&](floatx16 (&opend)[2], const uint32_t (&gv)[2][4][2], int pq0, int pqvalid)
         __attribute__((always_inline)) {
-      uint16_t* oblk = oh + static_cast<int64_t>(pq0) * dv;
-      const int so = store_offset();
+      uint16_t* oblk = rev ? oh : oh + static_cast<int64_t>(pq0) * dv;
+      int so, rr = 0, cb = 0;
+      if (!rev) so = store_offset();
+      else {
+        rev_store(rr, cb);
+        so = 0;
+      }
       // Normalise and store four rows of a lane at a time (rows row0 +
       // 4*(l/32) + 0..3 are accumulators 4g..4g+3): their 1/std and shift are
       // one 16-byte LDS read each. As bf16 pairs: one DPP exchange with the
@@ -605,9 +718,14 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
             }
           }
           const int nrows = min(max(pqvalid - row0, 0), 8);
-          const __amdgpu_buffer_rsrc_t r = make_rsrc(oblk + row0 * dv, nrows > 0 ? ((nrows - 1) * dv + kVT) * 2 : 0);
+          // Reverse: one descriptor over the head's rows; rows past the
+          // block's end get negative offsets and their stores are dropped.
+          const __amdgpu_buffer_rsrc_t r =
+              rev ? make_rsrc(oblk, rev_v_range)
+                  : make_rsrc(oblk + row0 * dv, nrows > 0 ? ((nrows - 1) * dv + kVT) * 2 : 0);
 #pragma unroll
           for (int hp = 0; hp < 2; ++hp) {
+            const int off = rev ? (nm1 - (pq0 + row0 + rr + 2 * hp)) * dv * 2 + cb : so + 2 * hp * dv * 2;
             unsigned packed;
             if constexpr (EPI != 0) {
               const float a0 = y[2 * hp], a1 = y[2 * hp + 1];
@@ -624,7 +742,7 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
               const unsigned nbr = __builtin_amdgcn_update_dpp(0u, own, 0xB1, 0xf, 0xf, true);
               packed = __builtin_amdgcn_perm(nbr, own, sel);
             }
-            __builtin_amdgcn_raw_buffer_store_b32(packed, r, so + 2 * hp * dv * 2, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(packed, r, off, 0, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -990,7 +1108,7 @@ hipError_t copy_device(void* dst, const void* src, size_t bytes, hipStream_t str
 hipError_t launch_fused_chunkwise(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                                   const float* state_in, float* state_out, void* workspace, const Dims& d, int chunk,
                                   const HeadDecay& decay, const GnArgs& gn, bool accumulate, hipStream_t stream,
-                                  int chunks_per_seg, const float* seg_states) {
+                                  int chunks_per_seg, const float* seg_states, const FusedLayout* layout) {
   FusedArgs a;
   a.q = q;
   a.k = k;
@@ -1004,8 +1122,19 @@ hipError_t launch_fused_chunkwise(const uint16_t* q, const uint16_t* k, const ui
   a.nseg = (nchunks + a.chunks_per_seg - 1) / a.chunks_per_seg;
   a.seg_states = seg_states;
   if (a.nseg > 1 && !seg_states) return hipErrorInvalidValue;
+  const FusedLayout plain;
+  const FusedLayout& lay = layout ? *layout : plain;
+  if (lay.nparts < 1 || (a.nseg > 1 && (lay.nparts > 1 || lay.reverse))) return hipErrorInvalidValue;
+  a.ldq = lay.ldq > 0 ? lay.ldq : d.dk;
+  a.ldk = lay.ldk > 0 ? lay.ldk : d.dk;
+  a.reverse = lay.reverse ? 1 : 0;
+  a.nparts = lay.nparts;
+  a.q_part = lay.q_part;
+  a.k_part = lay.k_part;
+  a.o_part = lay.o_part;
+  a.s_part = lay.s_part;
   a.nvt = d.dv / kVT;
-  a.units = static_cast<int>(heads * a.nseg * a.nvt);
+  a.units = static_cast<int>(heads * a.nseg * a.nparts * a.nvt);
   a.mail = static_cast<uint64_t*>(workspace);
   a.H = d.H;
   a.N = d.N;
@@ -1021,17 +1150,21 @@ hipError_t launch_fused_chunkwise(const uint16_t* q, const uint16_t* k, const ui
 
   const int epi = (gn.enabled && gn.gate) ? 1 : (accumulate ? 2 : 0);
   const void* fn = nullptr;
-#define RET_FUSED_PICK(MTV)                                                               \
-  fn = epi == 1   ? reinterpret_cast<const void*>(fused_chunk_kernel<MTV, 1>)             \
-       : epi == 2 ? reinterpret_cast<const void*>(fused_chunk_kernel<MTV, 2>)             \
-                  : reinterpret_cast<const void*>(fused_chunk_kernel<MTV, 0>)
+  const bool gen = layout != nullptr;
+  if (gen && epi == 1) return hipErrorInvalidValue;  // the general layout has no gated instance
+#define RET_FUSED_PICK(MTV)                                                                            \
+  fn = gen          ? (epi == 2 ? reinterpret_cast<const void*>(fused_chunk_kernel<MTV, 2, true>)      \
+                                : reinterpret_cast<const void*>(fused_chunk_kernel<MTV, 0, true>))     \
+       : epi == 1   ? reinterpret_cast<const void*>(fused_chunk_kernel<MTV, 1, false>)                 \
+       : epi == 2   ? reinterpret_cast<const void*>(fused_chunk_kernel<MTV, 2, false>)                 \
+                    : reinterpret_cast<const void*>(fused_chunk_kernel<MTV, 0, false>)
   if (d.dk == 256) {
     RET_FUSED_PICK(8);
   } else {
     RET_FUSED_PICK(4);
   }
 #undef RET_FUSED_PICK
-  int slot = (d.dk == 256 ? 9 : 10);
+  int slot = (d.dk == 256 ? 9 : 10) + (gen ? 3 : 0);  // 12, 13: the general-layout instances
   int resident = 0;
   e = resident_workgroups(fn, kThreadsF, slot, &resident);
   if (e != hipSuccess) return e;

@@ -98,12 +98,25 @@ bool mfma_supports(int dk, int dv);
 // by its own workgroups from the state seg_states gives it: fp32
 // [B*H][nseg][dk][dv], slot s < nseg-1 the end state of segment s started
 // from zero (segment 0 from state_in), as launch_segment_ends leaves it.
+// `layout` (optional) reads q and k with row pitches ldq, ldk (elements),
+// takes every sequence in reverse token order (logical row t at memory row
+// N-1-t, for q, k, v and o alike), and runs nparts independent retentions in
+// one launch: part p reads q and k q_part and k_part elements further, writes
+// o o_part further and starts from state_in s_part further. It excludes
+// segments; reverse order needs (N-1)*max(ldq, ldk, dv)*2 below 2^30.
+struct FusedLayout {
+  int ldq = 0, ldk = 0;  // 0: dk
+  bool reverse = false;
+  int nparts = 1;
+  int64_t q_part = 0, k_part = 0, o_part = 0, s_part = 0;
+};
 bool fused_supports(int dk, int dv, int chunk);
 size_t fused_workspace_bytes(int64_t heads, int dv);
 hipError_t launch_fused_chunkwise(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                                   const float* state_in, float* state_out, void* workspace, const Dims& d, int chunk,
                                   const HeadDecay& decay, const GnArgs& gn, bool accumulate, hipStream_t stream,
-                                  int chunks_per_seg = 0, const float* seg_states = nullptr);
+                                  int chunks_per_seg = 0, const float* seg_states = nullptr,
+                                  const FusedLayout* layout = nullptr);
 // End states of segments 0..nseg-2 (segments of chunks_per_seg chunks), each
 // walked from zero (segment 0 from state_in), into seg_states [B*H][nseg][dk][dv]
 // (the MFMA state walk's first mode; dk 128 or 256, dv a multiple of 128).

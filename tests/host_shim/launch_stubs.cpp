@@ -55,7 +55,7 @@ hipError_t launch_state_prep(const float*, float*, int, int, int, int, bool, int
 
 hipError_t launch_fused_chunkwise(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, const float*, float*,
                                   void*, const Dims&, int, const HeadDecay&, const GnArgs&, bool, hipStream_t, int,
-                                  const float*) {
+                                  const float*, const FusedLayout*) {
   return record();
 }
 hipError_t copy_device(void*, const void*, size_t, hipStream_t) { return record(); }

@@ -158,13 +158,16 @@ def test_6p7b_prefill_gated_full(prefill_6p7b, prefill_6p7b_oracle):
         _check(_f64(out[b : b + 1]), ref, f"gated o b={b}")
 
 
-def test_6p7b_backward_sampled(prefill_6p7b):
+@pytest.mark.parametrize("C", [512, 64])
+def test_6p7b_backward_sampled(prefill_6p7b, C):
     """The backward pass at the 6.7B prefill shape, as the bench times it (no
-    states, chunk 512): sampled rows of dQ, dK and dV of two batch rows."""
-    _announce("B=8 H=16 N=8192 chunk 512 backward: sampled rows of dQ, dK, dV")
+    states; chunk 512 on the two stages over copied operands, chunk 64 on the
+    single pass reading them in place): sampled rows of dQ, dK and dV of two
+    batch rows."""
+    _announce(f"B=8 H=16 N=8192 chunk {C} backward: sampled rows of dQ, dK, dV")
     q, k, v = prefill_6p7b
     B, H, N, dk = q.shape
-    dv, C = v.shape[-1], 512
+    dv = v.shape[-1]
     g = synthetic.head_gammas(H)
     dO = synthetic.make_qkv(B, H, N, dk, dv, dtype=torch.bfloat16, seed=1007)[2]
     qd, kd, vd, dOd = q.to(DEV), k.to(DEV), v.to(DEV), dO.to(DEV)

@@ -11,8 +11,9 @@ states are compared element by element with the oracle, per (b, h) slice at
 2e-2 * max|o|. Cases: ragged tails and several chunk lengths, state in and
 out (aliased too), GroupNorm with and without affine, the swish gate, dk 128
 with one v tile, dv 1024 with four, sequences shorter than a block, extreme
-decays, agreement with the two-stage entry points, and a backward pass whose
-retentions all take this kernel.
+decays, agreement with the two-stage entry points, and backward passes whose
+retentions all take this kernel with the inputs read in place (reverse order,
+row pitch, 256-wide parts in one launch).
 """
 
 import numpy as np
@@ -195,21 +196,49 @@ def test_single_pass_repeatable():
         assert torch.equal(S, outs[0][1])
 
 
-def test_backward_through_the_single_pass_kernel():
-    """B*H = 192: every retention of the backward (dV over dv = 512; dQ and dK
-    over 256-wide parts) takes the single-pass kernel, with state in and out."""
-    B, H, N, dk, dv, C = 12, 16, 320, 256, 512, 128
-    _announce(f"backward B={B} H={H} N={N} chunk={C} via the single pass")
-    assert _is_single_pass(B, H, N, dk, dv, C) and _is_single_pass(B, H, N, 256, dk, C)
-    q, k, v = synthetic.make_qkv(B, H, N, dk, dv, dtype=torch.bfloat16, seed=3600)
+def _is_direct_backward(B, H, N, dk, dv, C):
+    """Workspace of the backward on the single pass with in-place operands:
+    the 256-wide parts of grad_q / grad_k (bf16), four fp32 state buffers and
+    the exchange words of the wider of its launches."""
+    P = -(-dv // 256)
+    tok, st = B * H * N, B * H * dk * dv * 4
+    want = (_align(P * tok * dk * 2) + 4 * _align(st)
+            + _align(max(B * H * (dv // 256), B * H * P * (dk // 256)) * 2048))
+    return ret.chunkwise_backward_workspace_bytes(B, H, N, dk, dv, C) == want
+
+
+BACKWARD_CASES = [
+    # B, H, N, dv, chunk, state in / final-state gradient, decays
+    (12, 16, 320, 512, 128, True, "schedule"),   # 192 units per retention, state in and out
+    (12, 16, 200, 512, 64, False, "schedule"),   # ragged last chunk (8 rows), no states
+    (4, 16, 150, 768, 64, True, "schedule"),     # three parts of dO / V, three v tiles of dV
+    (12, 16, 130, 512, 64, True, "extreme"),     # gamma 1e-6 and 1 - 2^-20 with dS_N (divided by gamma)
+]
+
+
+@pytest.mark.parametrize("B, H, N, dv, C, with_state, decays", BACKWARD_CASES)
+def test_backward_through_the_single_pass_kernel(B, H, N, dv, C, with_state, decays):
+    """Every retention of the backward (dV over the v tiles of dO; dQ and dK
+    over the 256-wide parts of V and dO, one launch each, the reverse-time
+    ones reading their operands back to front) takes the single-pass kernel
+    with the inputs where they are; all four gradients against the oracle."""
+    dk = 256
+    _announce(f"backward B={B} H={H} N={N} dv={dv} chunk={C} state={with_state} {decays} via the single pass")
+    assert _is_direct_backward(B, H, N, dk, dv, C)
+    q, k, v = synthetic.make_qkv(B, H, N, dk, dv, dtype=torch.bfloat16, seed=3600 + N)
     g = synthetic.head_gammas(H)
-    dO = synthetic.make_qkv(B, H, N, dk, dv, dtype=torch.bfloat16, seed=3601)[2]
-    S0 = synthetic.make_state(B, H, dk, dv, seed=3602, std=0.5)
-    dSN = synthetic.make_state(B, H, dk, dv, seed=3603, std=0.05)
-    gq, gk, gv, gs = ret.chunkwise_backward(q.to(DEV), k.to(DEV), v.to(DEV), dO.to(DEV), g, C,
-                                            state_in=S0.to(DEV), grad_state_out=dSN.to(DEV), grad_state_in=True)
+    if decays == "extreme":
+        g = g.clone()
+        g[0], g[H - 1] = 1e-6, 1.0 - 2.0 ** -20
+    dO = synthetic.make_qkv(B, H, N, dk, dv, dtype=torch.bfloat16, seed=3601 + N)[2]
+    S0 = synthetic.make_state(B, H, dk, dv, seed=3602, std=0.5) if with_state else None
+    dSN = synthetic.make_state(B, H, dk, dv, seed=3603, std=0.05) if with_state else None
+    dev = lambda t: None if t is None else t.to(DEV)
+    gq, gk, gv, gs = ret.chunkwise_backward(dev(q), dev(k), dev(v), dev(dO), g, C, state_in=dev(S0),
+                                            grad_state_out=dev(dSN), grad_state_in=True)
     torch.cuda.synchronize()
-    refs = orc.backward(q, k, v, g, dO, state_in=S0, d_state_out=dSN)
+    S0_ref = S0 if S0 is not None else torch.zeros(B, H, dk, dv)
+    refs = orc.backward(q, k, v, g, dO, state_in=S0_ref, d_state_out=dSN)
     for name, got, r in zip(("dq", "dk", "dv", "dS0"), (gq, gk, gv, gs), refs):
         _check(got, r, name)
 
