@@ -268,8 +268,8 @@ int retention_xpos_rotate(const void* q, const void* k, void* q_out, void* k_out
  * of the forward call. Each gradient is evaluated as a retention of its own
  * (grad_q forward in time; grad_k and grad_v over the token-reversed sequence)
  * with the chunkwise kernels at the given chunk; a width above 256 is split
- * into parts whose results are summed. For bf16 at chunk <= 128 (after
- * clamping), dk 256 and dv a multiple of 256 (at most 1024), with at least
+ * into parts whose results are summed. For bf16 with the chunk a multiple of
+ * 64 (after clamping), dk 256 and dv a multiple of 256 (at most 1024), with at least
  * 192 (head, 256-column) units in each retention, the three retentions run on
  * the single-pass kernel reading the inputs in place (reverse order, row
  * pitch) and the workspace holds the parts of grad_q / grad_k, four fp32

@@ -240,13 +240,27 @@ def test_backward_rejects_invalid_arguments(lib):
     assert _backward(lib, H=257, gamma=[0.9] * 257) == -2
 
 
+def _align(x):
+    return (x + 255) // 256 * 256
+
+
 def test_backward_workspace_bytes(lib):
     ws = lib.retention_chunkwise_backward_workspace_bytes
-    # It holds at least the reversed Q, K, dO and V copies and the forward-size chunk workspace.
     B, H, N, dk, dv = 8, 16, 8192, 256, 512
     tok = B * H * N
-    assert ws(B, H, N, dk, dv, 512, 1) >= (2 * tok * dk + 2 * tok * dv) * 2 + \
-        lib.retention_chunkwise_workspace_bytes(B, H, N, dk, dv, 512, 1)
+    st = B * H * dk * dv * 4
+    # bf16 on the single pass (any chunk that is a multiple of 64): the two
+    # 256-wide parts of grad_q / grad_k, four fp32 state buffers and the
+    # exchange words of 256 (head, 256-column) units.
+    direct = _align(2 * tok * dk * 2) + 4 * _align(st) + _align(256 * 2048)
+    for C in (64, 128, 256, 512):
+        assert ws(B, H, N, dk, dv, C, 1) == direct, C
+    # fp32 (two stages): at least the reversed Q, K, dO and V copies and the
+    # forward-size chunk workspace.
+    assert ws(B, H, N, dk, dv, 512, 0) >= (2 * tok * dk + 2 * tok * dv) * 4 + \
+        lib.retention_chunkwise_workspace_bytes(B, H, N, dk, dv, 512, 0)
+    # Too few heads for the single pass (16 (head, v tile) units): copies again.
+    assert ws(1, 8, N, dk, dv, 512, 1) >= (2 * N * 8 * dk + 2 * N * 8 * dv) * 2
     assert ws(0, H, N, dk, dv, 512, 1) == 0
     assert ws(B, H, N, dk, dv, 0, 1) == 0
 

@@ -213,6 +213,8 @@ BACKWARD_CASES = [
     (12, 16, 200, 512, 64, False, "schedule"),   # ragged last chunk (8 rows), no states
     (4, 16, 150, 768, 64, True, "schedule"),     # three parts of dO / V, three v tiles of dV
     (12, 16, 130, 512, 64, True, "extreme"),     # gamma 1e-6 and 1 - 2^-20 with dS_N (divided by gamma)
+    (12, 16, 600, 512, 256, True, "schedule"),   # chunk 256: four query blocks a chunk, ragged last chunk
+    (12, 16, 1100, 512, 512, False, "schedule"), # chunk 512: eight query blocks, 76-row last chunk
 ]
 
 
