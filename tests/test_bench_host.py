@@ -88,3 +88,15 @@ def test_single_pass_design_bytes_and_executed_flops():
         per = keys * (2 * 256 * 2 + 2 * 512) + 4 * 256 * 512
         assert bench.single_pass_executed_flops(B, H, N, C) == per * B * H * N
         assert bench.single_pass_executed_flops(B, H, N, C) > bench.algorithmic_flops(B, H, N, C)
+
+
+def test_backward_method_and_executed_flops():
+    # Three retentions of the forward's kind (the count is symmetric in the
+    # two widths): 3 * 918,272 flop per token-head at chunk 512.
+    tok = 8 * 16 * 8192
+    assert bench.backward_method_flops(8, 16, 8192, 512) == 3 * 918_272 * tok
+    # Executed: dQ and dK each as two 256-wide parts, whose value products
+    # (width dk) are formed once per part.
+    per_part = 513 * (256 + 256) + 4 * 256 * 256
+    assert bench.backward_flops(8, 16, 8192, 512) == (918_272 + 4 * per_part) * tok
+    assert bench.backward_flops(8, 16, 8192, 64) > bench.backward_method_flops(8, 16, 8192, 64)
