@@ -270,11 +270,13 @@ int retention_xpos_rotate(const void* q, const void* k, void* q_out, void* k_out
  * with the chunkwise kernels at the given chunk; a width above 256 is split
  * into parts whose results are summed. For bf16 with the chunk a multiple of
  * 64 (after clamping), dk 256 and dv a multiple of 256 (at most 1024), with at least
- * 192 (head, 256-column) units in each retention, the three retentions run on
+ * 192 (head, 256-column) units in each launch, the three retentions run on
  * the single-pass kernel reading the inputs in place (reverse order, row
- * pitch) and the workspace holds the parts of grad_q / grad_k, four fp32
- * state buffers and the exchange words; otherwise the operands are first
- * copied (reversed, split) into the workspace. With grad_state_out given, every
+ * pitch; one launch for grad_v, one per 256-wide part for grad_q and grad_k
+ * together, the later parts adding to the first in fp32 before rounding) and
+ * the workspace holds four fp32 state buffers and the exchange words;
+ * otherwise the operands are first copied (reversed, split) into the
+ * workspace. With grad_state_out given, every
  * gamma must be a normal float (>= FLT_MIN, about 1.2e-38): the final-state
  * gradient is divided by gamma on its way in, and RET_ERR_UNSUPPORTED is
  * returned otherwise. workspace must hold

@@ -217,10 +217,10 @@ constexpr int kPartWidth = 256;  // widest query/key dimension the MFMA kernels 
 
 struct BackwardPlan {
   // Single-pass plan: every retention on the single-pass kernel, reading the
-  // operands in place (row pitches, reverse order) with the parts of the dQ
-  // and dK retentions in one launch each, summed afterwards; no copies.
+  // operands in place (row pitches, reverse order), one launch per 256-wide
+  // part for the dQ and dK retentions together; no copies.
   bool direct;
-  size_t tparts, mail;  // direct: part outputs [nparts][B*H*N*dk], exchange mailbox
+  size_t mail;  // direct: exchange words of the widest launch
   int nparts;  // parts of the dv-wide query/key dimension of the dQ and dK retentions
   int part_w;
   size_t qf, kf, dof, oa, dos, vs, dofs, vfs, kpart;  // byte offsets (token-row buffers)
@@ -231,17 +231,17 @@ struct BackwardPlan {
 };
 
 // Whether the backward runs directly on the single-pass kernel: bf16, the
-// retentions' widths and chunk within its range, enough (head, part, v tile)
-// units for each launch without segments, and reverse-order offsets within
-// 2^30 bytes. Unlike the forward, long chunks take it too: the two stages
+// retentions' widths and chunk within its range, enough units for each launch
+// without segments ((head, v tile) for dV; (retention, head, v tile) for a
+// part of dQ and dK together), and reverse-order offsets within 2^30 bytes. Unlike the forward, long chunks take it too: the two stages
 // would first copy every operand (reversed, split), which costs more than the
 // single pass loses to them at chunks of 256 and 512.
-bool backward_direct(int B, int H, int N, int dk, int dv, int chunk, int dtype, int nparts, int part_w) {
+bool backward_direct(int B, int H, int N, int dk, int dv, int chunk, int dtype, int part_w) {
   if (dtype != RET_BF16) return false;
   if (!ret::fused_supports(dk, dv, chunk) || !ret::fused_supports(part_w, dk, chunk)) return false;
   if (dv % part_w != 0) return false;
   const int64_t heads = static_cast<int64_t>(B) * H;
-  if (heads * (dv / 256) < kFusedMinUnits || heads * nparts * (dk / 256) < kFusedMinUnits) return false;
+  if (heads * (dv / 256) < kFusedMinUnits || 2 * heads * (dk / 256) < kFusedMinUnits) return false;
   const int64_t widest = std::max(dk, dv);
   return (static_cast<int64_t>(N) - 1) * widest * 2 + widest * 2 < (int64_t{1} << 30);
 }
@@ -259,15 +259,14 @@ BackwardPlan plan_backward(int B, int H, int N, int dk, int dv, int chunk, int d
     off += align_up(bytes);
     return at;
   };
-  p.direct = backward_direct(B, H, N, dk, dv, chunk, dtype, p.nparts, p.part_w);
+  p.direct = backward_direct(B, H, N, dk, dv, chunk, dtype, p.part_w);
   if (p.direct) {
     const int64_t heads = static_cast<int64_t>(B) * H;
-    p.tparts = take(static_cast<size_t>(p.nparts) * tok * dk * es);
     p.s_a = take(st);
     p.s_t = take(st);
     p.s_0t = take(st);
     p.s_nt = take(st);
-    p.mail = take(std::max(ret::fused_workspace_bytes(heads, dv), ret::fused_workspace_bytes(heads * p.nparts, dk)));
+    p.mail = take(std::max(ret::fused_workspace_bytes(heads, dv), ret::fused_workspace_bytes(2 * heads, dk)));
     p.total = off;
     return p;
   }
@@ -537,10 +536,12 @@ int retention_chunkwise_backward(const void* q, const void* k, const void* v, co
   char* cw = ws + p.cw;
 
   if (p.direct) {
-    // The same three retentions as below, each one launch of the single-pass
-    // kernel reading Q, K, V and dO where they are: reverse order in place of
-    // reversed copies, row pitch dv and column offsets in place of the
-    // 256-column parts, the parts of one gradient side by side in a launch.
+    // The same three retentions as below, on the single-pass kernel reading
+    // Q, K, V and dO where they are: reverse order in place of reversed
+    // copies, row pitch dv and column offsets in place of the 256-column
+    // parts. dV is one launch; each part of dQ and dK is one launch holding
+    // both retentions, the first part writing grad_q and grad_k, the later
+    // ones adding to them (in fp32, before rounding).
     const int P = p.nparts, pw = p.part_w;
     const int64_t st_part = static_cast<int64_t>(B) * H * pw * dk;  // fp32 elements between state parts
     const GnArgs nogn{};
@@ -574,27 +575,28 @@ int retention_chunkwise_backward(const void* q, const void* k, const void* v, co
       if (!ok(ret::launch_state_prep(grad_state_out, s_nt, B, H, dk, dv, true, pw, st_part, inv_gamma, s)))
         return RET_ERR_HIP;
     }
-    uint16_t* tp = static_cast<uint16_t*>(at(p.tparts));
-    ret::FusedLayout lq;
-    lq.ldq = dv;
-    lq.ldk = dv;
-    lq.nparts = P;
-    lq.q_part = pw;
-    lq.k_part = pw;
-    lq.o_part = tok * dk;
-    lq.s_part = st_part;
     const Dims dd{B, H, N, pw, dk};
-    // dQ parts: query dO, key V, value K, starting state S0^T (rows of the part).
-    if (!ok(ret::launch_fused_chunkwise(u16(grad_o), u16(v), u16(k), tp, s_0t, nullptr, at(p.mail), dd, chunk, decay,
-                                        nogn, false, s, 0, nullptr, &lq)))
-      return RET_ERR_HIP;
-    if (!ok(ret::launch_sum_parts(dtype, tp, grad_q, rows, dk, P, tok * dk, false, s))) return RET_ERR_HIP;
-    // dK parts (reversed time): query V, key dO, value Q, starting state dS_N^T / gamma.
-    lq.reverse = true;
-    if (!ok(ret::launch_fused_chunkwise(u16(v), u16(grad_o), u16(q), tp, s_nt, nullptr, at(p.mail), dd, chunk, decay,
-                                        nogn, false, s, 0, nullptr, &lq)))
-      return RET_ERR_HIP;
-    return status_of(ret::launch_sum_parts(dtype, tp, grad_k, rows, dk, P, tok * dk, false, s));
+    for (int i = 0; i < P; ++i) {
+      // dQ part: query dO, key V, value K, starting state S0^T (rows of the part).
+      // dK part (reversed time): query V, key dO, value Q, starting state dS_N^T / gamma.
+      ret::FusedJob dkj;
+      dkj.q = u16(v) + static_cast<int64_t>(i) * pw;
+      dkj.k = u16(grad_o) + static_cast<int64_t>(i) * pw;
+      dkj.v = u16(q);
+      dkj.o = static_cast<uint16_t*>(grad_k);
+      dkj.state_in = s_nt ? s_nt + i * st_part : nullptr;
+      dkj.reverse = true;
+      ret::FusedLayout lq;
+      lq.ldq = dv;
+      lq.ldk = dv;
+      lq.second = &dkj;
+      if (!ok(ret::launch_fused_chunkwise(u16(grad_o) + static_cast<int64_t>(i) * pw,
+                                          u16(v) + static_cast<int64_t>(i) * pw, u16(k),
+                                          static_cast<uint16_t*>(grad_q), s_0t ? s_0t + i * st_part : nullptr,
+                                          nullptr, at(p.mail), dd, chunk, decay, nogn, i > 0, s, 0, nullptr, &lq)))
+        return RET_ERR_HIP;
+    }
+    return RET_OK;
   }
 
   // Operand copies, each source read once: Q and K token-reversed; dO

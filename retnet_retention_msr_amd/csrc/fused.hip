@@ -99,11 +99,17 @@ struct FusedArgs {
   // Row pitches (elements) of q and k (dk when they are whole tensors). With
   // `reverse` every sequence is taken in reverse token order: logical row t
   // of q, k, v and o is memory row N-1-t (a reverse-time retention without
-  // reversed copies). `nparts` independent retentions share one launch: part
-  // p reads q and k q_part and k_part elements further, writes o o_part
-  // further and starts from state_in s_part further (no segments then).
-  int ldq, ldk, reverse, nparts;
-  int64_t q_part, k_part, o_part, s_part;
+  // reversed copies).
+  int ldq, ldk, reverse;
+  // A second retention of the same sizes in the same launch: units from
+  // job_units on take q2, k2, v2, o2, state_in2 and reverse2 (no final
+  // state, no segments). job_units = units when there is none.
+  const uint16_t* q2;
+  const uint16_t* k2;
+  const uint16_t* v2;
+  uint16_t* o2;
+  const float* state_in2;
+  int reverse2, job_units;
   int H, N, dk, dv, chunk, nchunks, nvt, units;
   int spin_limit;         // polls of a partner's flag before giving up on it
 };
@@ -149,9 +155,9 @@ __device__ __forceinline__ bf16x8 state_operand(const floatx16& t, int s) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
-// GEN: the general layout (row pitches, reverse order, parts); the plain
-// instances fold those to dk, forward order and one part, keeping the
-// registers they would hold.
+// GEN: the general layout (row pitches, reverse order, a second retention);
+// the plain instances fold those to dk, forward order and one retention,
+// keeping the registers they would hold.
 template <int MT, int EPI, bool GEN>
 __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, HeadDecay decay, GnArgs gn) {
   constexpr int XK = kTileF * kVT + kTileF * kPitch;  // V tile at 0, K block after it
@@ -178,7 +184,6 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
   const int vcol0 = wave * 32;  // this wave's columns within the v tile
   const int dk = a.dk, dv = a.dv;
   const int ldq = GEN ? a.ldq : dk, ldk = GEN ? a.ldk : dk;
-  const int nparts = GEN ? a.nparts : 1;
 
   // ---- per-lane LDS offsets (elements), fixed for the kernel; the empty asm
   // keeps each read one opaque offset away from its array, so the compiler
@@ -305,12 +310,17 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
   const int lwg = xcd_logical_block(blockIdx.x, G);
 
   for (int unit = lwg; unit < a.units; unit += G) {
-    // Unit = (head, segment, v tile), v tile fastest: the v tiles of a
-    // segment (which exchange GroupNorm statistics) are neighbours.
-    const int vt = unit % a.nvt;
-    const int part = (unit / a.nvt) % nparts;
-    const int seg = (unit / a.nvt / nparts) % a.nseg;
-    const int64_t bh = unit / a.nvt / nparts / a.nseg;
+    // Unit = (retention, head, segment, v tile), v tile fastest: the v tiles
+    // of a segment (which exchange GroupNorm statistics) are neighbours.
+    const bool second = GEN && unit >= a.job_units;
+    const int ju = second ? unit - a.job_units : unit;
+    const uint16_t* const jq = second ? a.q2 : a.q;
+    const uint16_t* const jk = second ? a.k2 : a.k;
+    const uint16_t* const jv = second ? a.v2 : a.v;
+    uint16_t* const jo = second ? a.o2 : a.o;
+    const int vt = ju % a.nvt;
+    const int seg = (ju / a.nvt) % a.nseg;
+    const int64_t bh = ju / a.nvt / a.nseg;
     const int h = static_cast<int>(bh % a.H);
     const float lg = decay.log2g[h];
     // This unit's rows: [row0, row0 + Nu) of the head's sequence, chunks
@@ -319,16 +329,16 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
     const int Nu = min(a.chunks_per_seg * a.chunk, a.N - row0);
     const int ncu = (Nu + a.chunk - 1) / a.chunk;
     const int64_t rbase = bh * static_cast<int64_t>(a.N) + row0;  // first row in [B*H*N]
-    const bool rev = GEN && a.reverse != 0;
+    const bool rev = GEN && (second ? a.reverse2 : a.reverse) != 0;
     // Forward: the unit's first row. Reverse: the head's memory row 0 (the
     // unit's logical row t sits at memory row N-1-t).
     const int64_t mrow = rev ? bh * static_cast<int64_t>(a.N) : rbase;
-    const uint16_t* qh = a.q + part * a.q_part + mrow * ldq;
-    const uint16_t* kh = a.k + part * a.k_part + mrow * ldk;
-    const uint16_t* vh = a.v + mrow * dv + vt * kVT;
-    uint16_t* oh = a.o + part * a.o_part + mrow * dv + vt * kVT;
+    const uint16_t* qh = jq + mrow * ldq;
+    const uint16_t* kh = jk + mrow * ldk;
+    const uint16_t* vh = jv + mrow * dv + vt * kVT;
+    uint16_t* oh = jo + mrow * dv + vt * kVT;
     const int nm1 = a.N - 1 - row0;  // reverse: memory row of logical row t is nm1 - t
-    float* const state_out = seg == a.nseg - 1 ? (a.state_out ? a.state_out + part * a.s_part : nullptr) : nullptr;
+    float* const state_out = seg == a.nseg - 1 && !second ? a.state_out : nullptr;
     const int64_t dkdv = static_cast<int64_t>(dk) * dv;
     uint64_t* mymail = a.mail + static_cast<int64_t>(unit) * 2 * kMailWords;
     const int group0 = unit - vt;  // first unit of this head's v tiles
@@ -346,7 +356,7 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
     // The state this unit starts from: state_in for the first segment; for a
     // later one starting at row0, sum over earlier segments s' of
     // gamma^(row0 - end_s') U_s' (U_0 already carries state_in).
-    const float* const state_in = a.state_in ? a.state_in + part * a.s_part : nullptr;
+    const float* const state_in = second ? a.state_in2 : a.state_in;
     const bool has_in = seg > 0 || state_in != nullptr;
     const int nsrc = seg > 0 ? seg : (state_in ? 1 : 0);
     // The state moves between HBM and the accumulators through LDS, four
@@ -644,7 +654,7 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
     };
     auto load_epi = [&](uint32_t (&gv)[2][4][2], int pq0, int pqvalid) __attribute__((always_inline)) {
       if constexpr (EPI != 0) {
-        const uint16_t* gbase = EPI == 1 ? static_cast<const uint16_t*>(gn.gate) : a.o + part * a.o_part;
+        const uint16_t* gbase = EPI == 1 ? static_cast<const uint16_t*>(gn.gate) : jo;
         if (!rev) {
           const int so = store_offset();
           const uint16_t* gblk = gbase + (rbase + pq0) * static_cast<int64_t>(dv) + vt * kVT;
@@ -1124,17 +1134,21 @@ hipError_t launch_fused_chunkwise(const uint16_t* q, const uint16_t* k, const ui
   if (a.nseg > 1 && !seg_states) return hipErrorInvalidValue;
   const FusedLayout plain;
   const FusedLayout& lay = layout ? *layout : plain;
-  if (lay.nparts < 1 || (a.nseg > 1 && (lay.nparts > 1 || lay.reverse))) return hipErrorInvalidValue;
+  const FusedJob* two = lay.second;
+  if (a.nseg > 1 && (lay.reverse || two)) return hipErrorInvalidValue;
+  if (two && state_out) return hipErrorInvalidValue;  // the second retention leaves no final state
   a.ldq = lay.ldq > 0 ? lay.ldq : d.dk;
   a.ldk = lay.ldk > 0 ? lay.ldk : d.dk;
   a.reverse = lay.reverse ? 1 : 0;
-  a.nparts = lay.nparts;
-  a.q_part = lay.q_part;
-  a.k_part = lay.k_part;
-  a.o_part = lay.o_part;
-  a.s_part = lay.s_part;
+  a.q2 = two ? two->q : nullptr;
+  a.k2 = two ? two->k : nullptr;
+  a.v2 = two ? two->v : nullptr;
+  a.o2 = two ? two->o : nullptr;
+  a.state_in2 = two ? two->state_in : nullptr;
+  a.reverse2 = two && two->reverse ? 1 : 0;
   a.nvt = d.dv / kVT;
-  a.units = static_cast<int>(heads * a.nseg * a.nparts * a.nvt);
+  a.job_units = static_cast<int>(heads * a.nseg * a.nvt);
+  a.units = a.job_units * (two ? 2 : 1);
   a.mail = static_cast<uint64_t*>(workspace);
   a.H = d.H;
   a.N = d.N;

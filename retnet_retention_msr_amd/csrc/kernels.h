@@ -100,15 +100,24 @@ bool mfma_supports(int dk, int dv);
 // from zero (segment 0 from state_in), as launch_segment_ends leaves it.
 // `layout` (optional) reads q and k with row pitches ldq, ldk (elements),
 // takes every sequence in reverse token order (logical row t at memory row
-// N-1-t, for q, k, v and o alike), and runs nparts independent retentions in
-// one launch: part p reads q and k q_part and k_part elements further, writes
-// o o_part further and starts from state_in s_part further. It excludes
-// segments; reverse order needs (N-1)*max(ldq, ldk, dv)*2 below 2^30.
+// N-1-t, for q, k, v and o alike), and may add a second retention of the same
+// sizes and pitches to the launch (its own operands, output, starting state
+// and order; no final state): the units of the two run side by side. It
+// excludes segments and the gate; reverse order needs (N-1)*max(ldq, ldk,
+// dv)*2 below 2^30; with a second retention the workspace holds the exchange
+// words of twice the units.
+struct FusedJob {
+  const uint16_t* q = nullptr;
+  const uint16_t* k = nullptr;
+  const uint16_t* v = nullptr;
+  uint16_t* o = nullptr;
+  const float* state_in = nullptr;
+  bool reverse = false;
+};
 struct FusedLayout {
   int ldq = 0, ldk = 0;  // 0: dk
   bool reverse = false;
-  int nparts = 1;
-  int64_t q_part = 0, k_part = 0, o_part = 0, s_part = 0;
+  const FusedJob* second = nullptr;
 };
 bool fused_supports(int dk, int dv, int chunk);
 size_t fused_workspace_bytes(int64_t heads, int dv);

@@ -249,10 +249,9 @@ def test_backward_workspace_bytes(lib):
     B, H, N, dk, dv = 8, 16, 8192, 256, 512
     tok = B * H * N
     st = B * H * dk * dv * 4
-    # bf16 on the single pass (any chunk that is a multiple of 64): the two
-    # 256-wide parts of grad_q / grad_k, four fp32 state buffers and the
-    # exchange words of 256 (head, 256-column) units.
-    direct = _align(2 * tok * dk * 2) + 4 * _align(st) + _align(256 * 2048)
+    # bf16 on the single pass (any chunk that is a multiple of 64): four fp32
+    # state buffers and the exchange words of 256 units.
+    direct = 4 * _align(st) + _align(256 * 2048)
     for C in (64, 128, 256, 512):
         assert ws(B, H, N, dk, dv, C, 1) == direct, C
     # fp32 (two stages): at least the reversed Q, K, dO and V copies and the

@@ -13,7 +13,7 @@ out (aliased too), GroupNorm with and without affine, the swish gate, dk 128
 with one v tile, dv 1024 with four, sequences shorter than a block, extreme
 decays, agreement with the two-stage entry points, and backward passes whose
 retentions all take this kernel with the inputs read in place (reverse order,
-row pitch, 256-wide parts in one launch).
+row pitch, two retentions in one launch, later parts accumulating).
 """
 
 import numpy as np
@@ -198,12 +198,10 @@ def test_single_pass_repeatable():
 
 def _is_direct_backward(B, H, N, dk, dv, C):
     """Workspace of the backward on the single pass with in-place operands:
-    the 256-wide parts of grad_q / grad_k (bf16), four fp32 state buffers and
-    the exchange words of the wider of its launches."""
-    P = -(-dv // 256)
-    tok, st = B * H * N, B * H * dk * dv * 4
-    want = (_align(P * tok * dk * 2) + 4 * _align(st)
-            + _align(max(B * H * (dv // 256), B * H * P * (dk // 256)) * 2048))
+    four fp32 state buffers and the exchange words of the wider of its
+    launches (dV: (head, v tile) units; a part of dQ and dK: two retentions)."""
+    st = B * H * dk * dv * 4
+    want = 4 * _align(st) + _align(max(B * H * (dv // 256), 2 * B * H * (dk // 256)) * 2048)
     return ret.chunkwise_backward_workspace_bytes(B, H, N, dk, dv, C) == want
 
 
@@ -211,7 +209,7 @@ BACKWARD_CASES = [
     # B, H, N, dv, chunk, state in / final-state gradient, decays
     (12, 16, 320, 512, 128, True, "schedule"),   # 192 units per retention, state in and out
     (12, 16, 200, 512, 64, False, "schedule"),   # ragged last chunk (8 rows), no states
-    (4, 16, 150, 768, 64, True, "schedule"),     # three parts of dO / V, three v tiles of dV
+    (6, 16, 150, 768, 64, True, "schedule"),     # three parts of dO / V (two adding), three v tiles of dV
     (12, 16, 130, 512, 64, True, "extreme"),     # gamma 1e-6 and 1 - 2^-20 with dS_N (divided by gamma)
     (12, 16, 600, 512, 256, True, "schedule"),   # chunk 256: four query blocks a chunk, ragged last chunk
     (12, 16, 1100, 512, 512, False, "schedule"), # chunk 512: eight query blocks, 76-row last chunk
@@ -220,10 +218,11 @@ BACKWARD_CASES = [
 
 @pytest.mark.parametrize("B, H, N, dv, C, with_state, decays", BACKWARD_CASES)
 def test_backward_through_the_single_pass_kernel(B, H, N, dv, C, with_state, decays):
-    """Every retention of the backward (dV over the v tiles of dO; dQ and dK
-    over the 256-wide parts of V and dO, one launch each, the reverse-time
-    ones reading their operands back to front) takes the single-pass kernel
-    with the inputs where they are; all four gradients against the oracle."""
+    """Every retention of the backward takes the single-pass kernel with the
+    inputs where they are: dV over the v tiles of dO (reversed), then one
+    launch per 256-wide part of V and dO holding both the dQ and the
+    (reversed) dK retention, later parts adding to the first; all four
+    gradients against the oracle."""
     dk = 256
     _announce(f"backward B={B} H={H} N={N} dv={dv} chunk={C} state={with_state} {decays} via the single pass")
     assert _is_direct_backward(B, H, N, dk, dv, C)
