@@ -877,16 +877,19 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
           // elements apart in the swizzled rows), on two accumulators (even
           // and odd steps) so consecutive MFMAs do not wait for each other.
           floatx4 sodd = floatx4{};
+          constexpr int NS = DKMAX / 32;
+          bf16x8 kc = ld8(kt + kread[0]), qc = ld8(sQ + qread[0]);
 #pragma unroll
-          for (int s2 = 0; s2 < DKMAX / 32; s2 += 2) {
-            bf16x8 kf[2], qf[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              kf[u] = ld8(kt + kread[(s2 + u) & 3] + 128 * (s2 >> 2));
-              qf[u] = ld8(sQ + qread[(s2 + u) & 3] + 128 * (s2 >> 2));
+          for (int s = 0; s < NS; ++s) {
+            bf16x8 kn = kc, qn = qc;
+            if (s + 1 < NS) {
+              kn = ld8(kt + kread[(s + 1) & 3] + 128 * ((s + 1) >> 2));
+              qn = ld8(sQ + qread[(s + 1) & 3] + 128 * ((s + 1) >> 2));
             }
-            sacc = mfma16(kf[0], qf[0], sacc);
-            sodd = mfma16(kf[1], qf[1], sodd);
+            if (s & 1) sodd = mfma16(kc, qc, sodd);
+            else sacc = mfma16(kc, qc, sacc);
+            kc = kn;
+            qc = qn;
             __builtin_amdgcn_sched_barrier(0);
           }
           sacc += sodd;
@@ -1031,17 +1034,21 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
             copy_v(cs + (j + 2) * kTileF, xfar);
           }
           __builtin_amdgcn_sched_barrier(0);
+          bf16x8 c0 = ld_kt(ktx, kblk, 0, 0), c1 = ld_kt(ktx, kblk, 0, 1);
 #pragma unroll
-          for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int m4 = 0; m4 < MT; m4 += 4) {
-              bf16x8 ka[4];
-#pragma unroll
-              for (int u = 0; u < 4; ++u) ka[u] = ld_kt(ktx, kblk, s, m4 + u);
-#pragma unroll
-              for (int u = 0; u < 4; ++u) R[m4 + u] = mfma32(ka[u], bz[s], R[m4 + u]);
-              __builtin_amdgcn_sched_barrier(0);
+          for (int p = 0; p < MT; ++p) {
+            const int s = (2 * p) / MT, mt = (2 * p) % MT;
+            bf16x8 n0 = c0, n1 = c1;
+            if (p + 1 < MT) {
+              n0 = ld_kt(ktx, kblk, (2 * p + 2) / MT, (2 * p + 2) % MT);
+              n1 = ld_kt(ktx, kblk, (2 * p + 3) / MT, (2 * p + 3) % MT);
             }
+            R[mt] = mfma32(c0, bz[s], R[mt]);
+            R[mt + 1] = mfma32(c1, bz[s], R[mt + 1]);
+            c0 = n0;
+            c1 = n1;
+            __builtin_amdgcn_sched_barrier(0);
+          }
           vm_keep_n((cn ? 4 : 0) + (j == 0 ? pend_st : 0));
           lds_barrier();
         };
