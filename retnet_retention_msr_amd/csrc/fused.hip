@@ -231,7 +231,6 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
   // row (row % 16 = l % 16 for both qt): base + ((4i + 2s) ^ (l16 & 14)) | gbit.
   int qro_row = l32 * kPitch;
   asm volatile("" : "+v"(qro_row));
-  const int qro_x = l16 & 14, qro_g = ((lane >> 5) ^ l16) & 1;
   // Update A operand (K^T): two ds_read_b64_tr_b16 from a K block stored in
   // the V tiles' layout (granules x_pos-swizzled), rows 16s + 8*(l/32) +
   // (l%16)/4 (and +4), columns 32mt + 16*((l/16)%2) + 4*(l%4)... The row's
@@ -792,7 +791,10 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
         if (c > 0 || has_in) {
           // (Offsets kept from being hoisted out of the block loop, where the
           // 16 of them would hold registers for the whole kernel.)
-          int qx = qro_x, qg = qro_g;
+          // (The lane number formed again here: two registers held across the
+          // block loop for these cost spill reloads in the read-out.)
+          const int ln = static_cast<int>(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
+          int qx = ln & 14, qg = ((ln >> 5) ^ ln) & 1;
           asm volatile("" : "+v"(qx), "+v"(qg));
           auto ld_qa = [&](int j, bf16x8 (&dst)[2]) __attribute__((always_inline)) {
             const int i = j >> 1, s = j & 1;
@@ -944,6 +946,13 @@ __global__ void __launch_bounds__(kThreadsF, 1) fused_chunk_kernel(FusedArgs a, 
         using H0 = std::integral_constant<int, 0>;
         using H1 = std::integral_constant<int, 1>;
         using H2 = std::integral_constant<int, 2>;
+        // The first scores read K_0, whose pieces every wave copied after this
+        // block's Q: wait for it (V_0 and K_1, and the previous block's
+        // stores, may stay in flight), then a barrier, so that no wave reads
+        // another's piece before it lands. The read-out above hid most of
+        // its latency.
+        vm_keep_n(2 + (nkb > 1 ? 2 : 0) + pend_st);
+        lds_barrier();
         step(-1, H2{});
         pend_st = 0;  // step 0's wait covers them
         for (int i = 0;;) {
