@@ -233,9 +233,10 @@ struct BackwardPlan {
 // Whether the backward runs directly on the single-pass kernel: bf16, the
 // retentions' widths and chunk within its range, enough units for each launch
 // without segments ((head, v tile) for dV; (retention, head, v tile) for a
-// part of dQ and dK together), and reverse-order offsets within 2^30 bytes. Unlike the forward, long chunks take it too: the two stages
-// would first copy every operand (reversed, split), which costs more than the
-// single pass loses to them at chunks of 256 and 512.
+// part of dQ and dK together), and reverse-order offsets within 2^30 bytes.
+// Unlike the forward, long chunks take it too: the two stages would first
+// copy every operand (reversed, split), which costs more than the single pass
+// loses to them at chunks of 256 and 512.
 bool backward_direct(int B, int H, int N, int dk, int dv, int chunk, int dtype, int part_w) {
   if (dtype != RET_BF16) return false;
   if (!ret::fused_supports(dk, dv, chunk) || !ret::fused_supports(part_w, dk, chunk)) return false;
