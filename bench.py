@@ -603,7 +603,21 @@ def gated_prefill(ret, torch, dev, stream, qd, kd, vd, gamma, ws, state, out, gn
     out_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
     # Method bytes of the gated output: Q, K, V, O plus the gate read once.
     bytes_out = method_bytes(B, H, N) + B * H * N * DV * 2
-    del gate
+    # The same gated prefill at chunk 64, where retention_chunkwise plans the
+    # single pass (gate applied in its epilogue); one call per step.
+    c64 = 64
+    ws64 = torch.empty(max(ret.chunkwise_workspace_bytes(B, H, N, DK, DV, c64), 1), dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        ret.chunkwise(qd, kd, vd, gamma, c64, state_out=state, gn=gn, out=out, workspace=ws64, gate=gate)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        ret.chunkwise(qd, kd, vd, gamma, c64, state_out=state, gn=gn, out=out, workspace=ws64, gate=gate)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms64 = e0.elapsed_time(e1) / steps
+    del gate, ws64
     return {
         "workload": "the prefill above with the gated epilogue swish(gate) * GroupNorm(O), gate bf16 [B,H,N,dv]",
         "steps": steps,
@@ -618,6 +632,11 @@ def gated_prefill(ret, torch, dev, stream, qd, kd, vd, gamma, ws, state, out, gn
             "unit": "GB/s",
             "frac": bytes_out / (out_ms * 1e-3) / PEAK_HBM,
             "traffic": measured_traffic()["chunk_out_gated"],
+        },
+        "single_pass_chunk_64": {
+            "ms_per_step": ms64,
+            "tokens_per_s": B * N / (ms64 * 1e-3),
+            "hbm_frac_of_method_bytes": bytes_out / (ms64 * 1e-3) / PEAK_HBM,
         },
     }
 
