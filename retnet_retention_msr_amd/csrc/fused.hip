@@ -1173,10 +1173,15 @@ hipError_t launch_fused_chunkwise(const uint16_t* q, const uint16_t* k, const ui
   a.chunk = chunk;
   a.nchunks = (d.N + chunk - 1) / chunk;
   a.spin_limit = 1 << 22;
-  const int mail_ints = a.units * 2 * kMailWords * 2;
-  zero_ints_kernel<<<dim3((mail_ints + 255) / 256), 256, 0, stream>>>(reinterpret_cast<int*>(a.mail), mail_ints);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // The exchange words are read only by the GroupNorm exchange between the v
+  // tiles of a head; a call without it leaves them untouched.
+  hipError_t e = hipSuccess;
+  if (gn.enabled && a.nvt > 1) {
+    const int mail_ints = a.units * 2 * kMailWords * 2;
+    zero_ints_kernel<<<dim3((mail_ints + 255) / 256), 256, 0, stream>>>(reinterpret_cast<int*>(a.mail), mail_ints);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
 
   const int epi = (gn.enabled && gn.gate) ? 1 : (accumulate ? 2 : 0);
   const void* fn = nullptr;
