@@ -515,6 +515,24 @@ int retention_chunkwise_backward(const void* q, const void* k, const void* v, co
     for (int h = 0; h < H; ++h)
       if (gamma_host[h] < FLT_MIN) return RET_ERR_UNSUPPORTED;
   }
+  {
+    // The gradients are written while the inputs are still read (in place,
+    // by other workgroups): no gradient may share bytes with an input or
+    // another gradient.
+    const size_t es = dtype == RET_F32 ? 4 : 2;
+    const size_t tok = static_cast<size_t>(B) * H * N;
+    const size_t nk = tok * dk * es, nv = tok * dv * es;
+    const void* in[4] = {q, k, v, grad_o};
+    const size_t in_n[4] = {nk, nk, nv, nv};
+    const void* out[3] = {grad_q, grad_k, grad_v};
+    const size_t out_n[3] = {nk, nk, nv};
+    for (int i = 0; i < 3; ++i) {
+      for (int j = 0; j < 4; ++j)
+        if (overlaps(out[i], out_n[i], in[j], in_n[j])) return RET_ERR_INVALID_ARG;
+      for (int j = 0; j < i; ++j)
+        if (overlaps(out[i], out_n[i], out[j], out_n[j])) return RET_ERR_INVALID_ARG;
+    }
+  }
   chunk = effective_chunk(N, chunk);
   const BackwardPlan p = plan_backward(B, H, N, dk, dv, chunk, dtype);
   if (!workspace || workspace_bytes < p.total) return RET_ERR_INVALID_ARG;

@@ -220,10 +220,16 @@ def test_gate_needs_groupnorm():
         ret._gn_struct(None, 2, 128, None, gate=object())
 
 
-def _backward(lib, gq=FAKE, ws=FAKE, ws_bytes=1 << 40, chunk=64, gamma=None, B=1, H=2, N=256, dk=64, dv=128,
-              dtype=1):
+# Distinct fake addresses (1 TiB apart, never dereferenced) for the backward's
+# q, k, v, dO and its three gradients, which may not share bytes.
+BW = [FAKE + (i << 40) for i in range(7)]
+
+
+def _backward(lib, gq=BW[4], ws=FAKE, ws_bytes=1 << 40, chunk=64, gamma=None, B=1, H=2, N=256, dk=64, dv=128,
+              dtype=1, ptrs=None):
     g = _gamma(gamma or [0.9] * H)
-    return lib.retention_chunkwise_backward(FAKE, FAKE, FAKE, FAKE, g, gq, FAKE, FAKE, B, H, N, dk, dv, chunk, dtype,
+    q, k, v, do, _, gk, gv = ptrs or BW
+    return lib.retention_chunkwise_backward(q, k, v, do, g, gq, gk, gv, B, H, N, dk, dv, chunk, dtype,
                                             None, None, None, ws, ws_bytes, None)
 
 
@@ -238,6 +244,19 @@ def test_backward_rejects_invalid_arguments(lib):
     assert _backward(lib, N=0) == -1
     assert _backward(lib, dtype=2) == -1
     assert _backward(lib, H=257, gamma=[0.9] * 257) == -2
+
+
+def test_backward_rejects_gradients_that_share_bytes(lib):
+    """The gradients are written while the inputs are still being read: a
+    gradient sharing bytes with an input or with another gradient is refused
+    (before anything is launched)."""
+    nk = 1 * 2 * 256 * 64 * 2  # bytes of q, k, grad_q, grad_k at the helper's shape (bf16)
+    q, k, v, do, gq, gk, gv = BW
+    assert _backward(lib, gq=q + nk - 2) == -1                                     # grad_q's first element in q
+    assert _backward(lib, ptrs=[q, k, v, do, None, q - 2, gv]) == -1               # grad_k's last element in q
+    assert _backward(lib, ptrs=[q, k, v, do, None, gk, do + 64]) == -1             # grad_v inside dO
+    assert _backward(lib, gq=gk + nk // 2) == -1                                   # grad_q inside grad_k
+    assert _backward(lib, ptrs=[q, k, v, do, None, gk, gq + 2], gq=gq) == -1       # grad_v inside grad_q
 
 
 def _align(x):
@@ -268,7 +287,7 @@ def test_backward_rejects_subnormal_gamma_with_a_final_state_gradient(lib):
     """dL/dS_N enters divided by gamma: a subnormal gamma would overflow that quotient."""
     need = lib.retention_chunkwise_backward_workspace_bytes(1, 2, 256, 64, 128, 64, 1)
     g = _gamma([1e-39, 0.9])
-    assert lib.retention_chunkwise_backward(FAKE, FAKE, FAKE, FAKE, g, FAKE, FAKE, FAKE, 1, 2, 256, 64, 128, 64, 1,
+    assert lib.retention_chunkwise_backward(*BW[:4], g, *BW[4:], 1, 2, 256, 64, 128, 64, 1,
                                             None, FAKE, None, FAKE, need, None) == _lib.RET_ERR_UNSUPPORTED
 
 
@@ -323,7 +342,7 @@ def test_valid_backward_and_decode_calls_reach_the_launchers(lib, shape):
     need = lib.retention_chunkwise_backward_workspace_bytes(B, H, N, dk, dv, chunk, dtype)
     g = _gamma([1 - 2.0 ** (-5 - h) for h in range(H)])
     before = _launches(lib)
-    assert lib.retention_chunkwise_backward(FAKE, FAKE, FAKE, FAKE, g, FAKE, FAKE, FAKE, B, H, N, dk, dv, chunk,
+    assert lib.retention_chunkwise_backward(*BW[:4], g, *BW[4:], B, H, N, dk, dv, chunk,
                                             dtype, FAKE, FAKE, FAKE, FAKE, need, None) == 0
     assert lib.retention_recurrent_step(FAKE, FAKE, FAKE, g, FAKE, FAKE, B, H, dk, dv, dtype, None, None) == 0
     assert _launches(lib) > before
