@@ -49,7 +49,11 @@
  *     once), filled on first use through atomic stores and never changed
  *     afterwards; calls on different streams do not interfere except through
  *     buffers the caller shares.
- *   - O must not alias Q, K or V. No entry point throws; all report status.
+ *   - O must not share bytes with Q, K or V, nor a gate with O, nor the
+ *     recurrent step's state with its token vectors: the kernels write while
+ *     other workgroups still read. Such calls are refused with
+ *     RET_ERR_INVALID_ARG (the ranges are checked, the pointers never
+ *     dereferenced on the host). No entry point throws; all report status.
  *
  * Status codes:
  *   RET_OK (0), RET_ERR_INVALID_ARG (-1): a required pointer is NULL, a size
@@ -264,7 +268,8 @@ int retention_xpos_rotate(const void* q, const void* k, void* q_out, void* k_out
  *   grad_v = A^T grad_o + diag(gamma^(N-1-m)) K dS_N
  *   grad_state_in = Q^T diag(gamma^(n+1)) grad_o + gamma^N dS_N   (fp32; NULL: not written)
  * grad_q, grad_k ([B, H, N, dk]) and grad_v ([B, H, N, dv]) have the input
- * type and must not alias any input. state_in (fp32, NULL = zeros) is the S0
+ * type and must not share bytes with any input or with each other
+ * (RET_ERR_INVALID_ARG). state_in (fp32, NULL = zeros) is the S0
  * of the forward call. Each gradient is evaluated as a retention of its own
  * (grad_q forward in time; grad_k and grad_v over the token-reversed sequence)
  * with the chunkwise kernels at the given chunk; a width above 256 is split

@@ -90,6 +90,18 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   return x < y + bn && y < x + an;
 }
 
+// Whether O ([B, H, N, dv]) shares bytes with Q, K ([B, H, N, dk]) or V, or a
+// gate (laid out like O, may be null) with O: the kernels write O while other
+// workgroups still read the inputs (and the gate at the positions they store).
+bool output_overlaps(const void* q, const void* k, const void* v, const void* o, const void* gate, int B, int H,
+                     int N, int dk, int dv, int dtype) {
+  const size_t es = dtype == RET_F32 ? 4 : 2;
+  const size_t tok = static_cast<size_t>(B) * H * N;
+  const size_t nk = tok * dk * es, nv = tok * dv * es;
+  return overlaps(o, nv, q, nk) || overlaps(o, nv, k, nk) || overlaps(o, nv, v, nv) ||
+         (gate && overlaps(gate, nv, o, nv));
+}
+
 // A chunk at least as long as the sequence is one chunk: every such length
 // gives the same result. It is brought down to the sequence length rounded up
 // to a multiple of the MFMA block height (so the MFMA kernels stay eligible),
@@ -361,6 +373,8 @@ int retention_parallel(const void* q, const void* k, const void* v, const float*
   st = check_gn(gn, &g);
   if (st != RET_OK) return st;
 
+  if (output_overlaps(q, k, v, o, g.gate, B, H, N, dk, dv, dtype)) return RET_ERR_INVALID_ARG;
+
   HeadDecay decay;
   check_gamma(gamma_host, H, &decay);
   const Dims d{B, H, N, dk, dv};
@@ -393,6 +407,7 @@ int retention_chunkwise(const void* q, const void* k, const void* v, const float
   const int st = check_chunkwise(gamma_host, B, H, N, dk, dv, &chunk, dtype, gn, workspace, workspace_bytes, &g, &p,
                                  &decay);
   if (st != RET_OK) return st;
+  if (output_overlaps(q, k, v, o, g.gate, B, H, N, dk, dv, dtype)) return RET_ERR_INVALID_ARG;
   const Dims d{B, H, N, dk, dv};
   return run_chunkwise(p, q, k, v, o, state_in, state_out, d, chunk, dtype, decay, g, static_cast<char*>(workspace),
                        static_cast<hipStream_t>(stream));
@@ -413,6 +428,7 @@ int retention_chunkwise_noalloc(const void* q, const void* k, const void* v, con
   if (st != RET_OK) return st;
   const ChunkPlan p = plan_chunkwise(B, H, N, dk, dv, effective_chunk(N, chunk), dtype);
   if (p.total > ret::kScratchBytes) return RET_ERR_UNSUPPORTED;
+  if (output_overlaps(q, k, v, o, g.gate, B, H, N, dk, dv, dtype)) return RET_ERR_INVALID_ARG;
   void* ws = nullptr;
   if (p.total > 0 && ret::scratch_pointer(&ws) != hipSuccess) return RET_ERR_HIP;
   return retention_chunkwise(q, k, v, gamma_host, o, B, H, N, dk, dv, chunk, dtype, state_in, state_out, gn, ws,
@@ -444,6 +460,7 @@ int retention_chunk_output(const void* q, const void* k, const void* v, const fl
   const int st = check_chunkwise(gamma_host, B, H, N, dk, dv, &chunk, dtype, gn, workspace, workspace_bytes, &g, &p,
                                  &decay, true);
   if (st != RET_OK) return st;
+  if (output_overlaps(q, k, v, o, g.gate, B, H, N, dk, dv, dtype)) return RET_ERR_INVALID_ARG;
   const Dims d{B, H, N, dk, dv};
   return status_of(launch_output(p, q, k, v, o, static_cast<const char*>(workspace), has_state_in != 0, d, chunk,
                                  dtype, decay, g, static_cast<hipStream_t>(stream)));
@@ -460,6 +477,17 @@ int retention_recurrent_step(const void* q, const void* k, const void* v, const 
   GnArgs g;
   st = check_gn(gn, &g);
   if (st != RET_OK) return st;
+  // (One token: O, Q, K, V and the gate as the N = 1 case; the fp32 state is
+  // read and written in place and may share bytes with none of them.)
+  if (output_overlaps(q, k, v, o, g.gate, B, H, 1, dk, dv, dtype)) return RET_ERR_INVALID_ARG;
+  {
+    const size_t es = dtype == RET_F32 ? 4 : 2;
+    const size_t sb = static_cast<size_t>(B) * H * dk * dv * sizeof(float);
+    const size_t nk = static_cast<size_t>(B) * H * dk * es, nv = static_cast<size_t>(B) * H * dv * es;
+    if (overlaps(state, sb, q, nk) || overlaps(state, sb, k, nk) || overlaps(state, sb, v, nv) ||
+        overlaps(state, sb, o, nv) || (g.gate && overlaps(state, sb, g.gate, nv)))
+      return RET_ERR_INVALID_ARG;
+  }
   HeadDecay decay;
   check_gamma(gamma_host, H, &decay);
   return status_of(ret::launch_decode_step(dtype, q, k, v, state, o, B, H, dk, dv, decay, g,

@@ -246,6 +246,28 @@ def test_backward_rejects_invalid_arguments(lib):
     assert _backward(lib, H=257, gamma=[0.9] * 257) == -2
 
 
+def test_outputs_that_share_bytes_with_inputs_are_refused(lib):
+    """O is written while other workgroups still read Q, K and V (and the
+    gate where they store): an O sharing bytes with any of them, or a gate
+    sharing bytes with O, is refused before anything is launched; so is a
+    decode state sharing bytes with the token's vectors."""
+    B, H, N, dk, dv = 1, 2, 256, 64, 128
+    nk, nv = B * H * N * dk * 2, B * H * N * dv * 2
+    q, k, v, o = BW[:4]
+    g = _gamma([0.9] * H)
+    need = lib.retention_chunkwise_workspace_bytes(B, H, N, dk, dv, 64, 1)
+    for oo in (q + nk - 2, k - nv + 2, v + 64):
+        assert lib.retention_parallel(q, k, v, g, oo, B, H, N, dk, dv, 1, None, None) == -1
+        assert lib.retention_chunkwise(q, k, v, g, oo, B, H, N, dk, dv, 64, 1, None, None, None, FAKE, need,
+                                       None) == -1
+    gate = _lib.GnStruct(1e-5, None, None, o + nv // 2)
+    assert lib.retention_chunkwise(q, k, v, g, o, B, H, N, dk, dv, 64, 1, None, None, ctypes.byref(gate), FAKE,
+                                   need, None) == -1
+    snb = B * H * dk * dv * 4
+    assert lib.retention_recurrent_step(q, k, v, g, q - snb + 4, o, B, H, dk, dv, 1, None, None) == -1
+    assert lib.retention_recurrent_step(q, k, v, g, BW[4], q, B, H, dk, dv, 1, None, None) == -1
+
+
 def test_backward_rejects_gradients_that_share_bytes(lib):
     """The gradients are written while the inputs are still being read: a
     gradient sharing bytes with an input or with another gradient is refused
@@ -322,12 +344,13 @@ def test_valid_chunkwise_calls_reach_the_launchers(lib, shape):
     need = lib.retention_chunkwise_workspace_bytes(B, H, N, dk, dv, chunk, dtype)
     g = _gamma([1 - 2.0 ** (-5 - h) for h in range(H)])
     before = _launches(lib)
-    assert lib.retention_chunkwise(FAKE, FAKE, FAKE, g, FAKE, B, H, N, dk, dv, chunk, dtype, None, FAKE, None,
+    q, k, v, o = BW[:4]
+    assert lib.retention_chunkwise(q, k, v, g, o, B, H, N, dk, dv, chunk, dtype, None, FAKE, None,
                                    FAKE if need else None, need, None) == 0
     gn = _lib.GnStruct(1e-5, None, None, None)
-    assert lib.retention_chunkwise(FAKE, FAKE, FAKE, g, FAKE, B, H, N, dk, dv, chunk, dtype, FAKE, FAKE,
+    assert lib.retention_chunkwise(q, k, v, g, o, B, H, N, dk, dv, chunk, dtype, FAKE, FAKE,
                                    ctypes.byref(gn), FAKE if need else None, need, None) == 0
-    assert lib.retention_parallel(FAKE, FAKE, FAKE, g, FAKE, B, H, N, dk, dv, dtype, ctypes.byref(gn), None) == 0
+    assert lib.retention_parallel(q, k, v, g, o, B, H, N, dk, dv, dtype, ctypes.byref(gn), None) == 0
     assert _launches(lib) > before
 
 
@@ -344,7 +367,7 @@ def test_valid_backward_and_decode_calls_reach_the_launchers(lib, shape):
     before = _launches(lib)
     assert lib.retention_chunkwise_backward(*BW[:4], g, *BW[4:], B, H, N, dk, dv, chunk,
                                             dtype, FAKE, FAKE, FAKE, FAKE, need, None) == 0
-    assert lib.retention_recurrent_step(FAKE, FAKE, FAKE, g, FAKE, FAKE, B, H, dk, dv, dtype, None, None) == 0
+    assert lib.retention_recurrent_step(*BW[:3], g, BW[4], BW[5], B, H, dk, dv, dtype, None, None) == 0
     assert _launches(lib) > before
 
 
