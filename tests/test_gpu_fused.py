@@ -214,6 +214,7 @@ BACKWARD_CASES = [
     (12, 16, 600, 512, 256, True, "schedule"),   # chunk 256: four query blocks a chunk, ragged last chunk
     (12, 16, 1100, 512, 512, False, "schedule"), # chunk 512: eight query blocks, 76-row last chunk
     (12, 16, 200, 256, 64, True, "schedule"),    # dv 256: one part, dQ and dK in a single launch
+    (6, 16, 140, 1024, 64, True, "schedule"),    # dv 1024: four parts (three adding), four v tiles of dV
 ]
 
 
