@@ -278,7 +278,10 @@ int retention_xpos_rotate(const void* q, const void* k, void* q_out, void* k_out
  * 192 (head, 256-column) units in each launch, the three retentions run on
  * the single-pass kernel reading the inputs in place (reverse order, row
  * pitch; one launch for grad_v, one per 256-wide part for grad_q and grad_k
- * together, the later parts adding to the first in fp32 before rounding) and
+ * together, the later parts adding to the first in fp32 before rounding; each
+ * part's sum is rounded to the input type before the next adds to it, so
+ * where the parts of an element cancel its error is set by the parts'
+ * magnitudes, about 2^-9 of each in bf16, not by the result's) and
  * the workspace holds four fp32 state buffers and the exchange words;
  * otherwise the operands are first copied (reversed, split) into the
  * workspace. With grad_state_out given, every

@@ -215,6 +215,7 @@ BACKWARD_CASES = [
     (12, 16, 1100, 512, 512, False, "schedule"), # chunk 512: eight query blocks, 76-row last chunk
     (12, 16, 200, 256, 64, True, "schedule"),    # dv 256: one part, dQ and dK in a single launch
     (6, 16, 140, 1024, 64, True, "schedule"),    # dv 1024: four parts (three adding), four v tiles of dV
+    (12, 16, 40, 512, 512, True, "schedule"),    # one chunk shorter than a query block (40 rows)
 ]
 
 
@@ -302,6 +303,48 @@ def test_segmented_single_pass_aliased_state_and_gate():
     assert S.data_ptr() == Sd.data_ptr()
     _check(o, orc.gated_group_norm(raw, _np(gate), eps=1e-5), "gated o")
     _check(S, S_ref, "state")
+
+
+@pytest.mark.parametrize("with_state", [False, True])
+def test_backward_single_token_within_the_part_rounding(with_state):
+    """One token (every other row of each tile lies outside the sequence).
+    dQ and dK are summed over the two 256-wide parts of dO and V, each part
+    rounded to bf16 before the next adds to it; with one key the parts of an
+    element can cancel (the score over 512 columns, |s| ~ 20, against a sum
+    near zero), so their bound is the usual one plus the parts' own rounding,
+    2^-8 * (|part 0| + |part 1|), with each part the oracle's gradient of the
+    retention on that part's columns (the gradients are linear in that
+    split). dV and the state gradient take no parts: the usual bound."""
+    B, H, N, dk, dv, C = 12, 16, 1, 256, 512, 64
+    _announce(f"backward B={B} H={H} N=1 state={with_state} within the part rounding")
+    assert _is_direct_backward(B, H, N, dk, dv, C)
+    q, k, v = synthetic.make_qkv(B, H, N, dk, dv, dtype=torch.bfloat16, seed=3950)
+    g = synthetic.head_gammas(H)
+    dO = synthetic.make_qkv(B, H, N, dk, dv, dtype=torch.bfloat16, seed=3951)[2]
+    S0 = synthetic.make_state(B, H, dk, dv, seed=3952, std=0.5) if with_state else None
+    dSN = synthetic.make_state(B, H, dk, dv, seed=3953, std=0.05) if with_state else None
+    dev = lambda t: None if t is None else t.to(DEV)
+    gq, gk, gv, gs = ret.chunkwise_backward(dev(q), dev(k), dev(v), dev(dO), g, C, state_in=dev(S0),
+                                            grad_state_out=dev(dSN), grad_state_in=True)
+    torch.cuda.synchronize()
+    S0_ref = S0 if S0 is not None else torch.zeros(B, H, dk, dv)
+    refs = orc.backward(q, k, v, g, dO, state_in=S0_ref, d_state_out=dSN)
+    _check(gv, refs[2], "dv")
+    _check(gs, refs[3], "dS0")
+    parts = []
+    for p in range(2):
+        cols = slice(256 * p, 256 * (p + 1))
+        parts.append(orc.backward(q, k, v[..., cols], g, dO[..., cols],
+                                  state_in=S0_ref[..., cols],
+                                  d_state_out=None if dSN is None else dSN[..., cols]))
+    for name, got, r, idx in (("dq", gq, refs[0], 0), ("dk", gk, refs[1], 1)):
+        got = _np(got)
+        mag = np.abs(parts[0][idx]) + np.abs(parts[1][idx])
+        for b in range(B):
+            for h in range(H):
+                err = float(np.max(np.abs(got[b, h] - r[b, h])))
+                bound = TOL * float(np.max(np.abs(r[b, h]))) + 2.0 ** -8 * float(np.max(mag[b, h]))
+                assert err <= bound, f"{name} b={b} h={h}: err {err:.3e} > {bound:.3e}"
 
 
 def test_repeated_calls_are_bit_identical():
