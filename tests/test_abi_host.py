@@ -301,6 +301,16 @@ def test_backward_workspace_bytes(lib):
         lib.retention_chunkwise_workspace_bytes(B, H, N, dk, dv, 512, 0)
     # Too few heads for the single pass (16 (head, v tile) units): copies again.
     assert ws(1, 8, N, dk, dv, 512, 1) >= (2 * N * 8 * dk + 2 * N * 8 * dv) * 2
+    # dk 128 (the dQ and dK retentions would have 128-wide values) and a chunk
+    # that is no multiple of 64: copies.
+    assert ws(B, H, N, 128, dv, 64, 1) >= (2 * tok * 128 + 2 * tok * dv) * 2
+    assert ws(B, H, N, dk, dv, 96, 1) >= (2 * tok * dk + 2 * tok * dv) * 2
+    # Reverse-order offsets must stay below 2^30 bytes: (N-1) * 512 * 2 + 1024
+    # reaches it at N = 2^20, so that sequence takes the copies.
+    big = 1 << 20
+    st192 = 192 * dk * dv * 4
+    assert ws(1, 192, big - 1, dk, dv, 64, 1) == 4 * _align(st192) + _align(2 * 192 * 2048)
+    assert ws(1, 192, big, dk, dv, 64, 1) > 4 * _align(st192) + _align(2 * 192 * 2048)
     assert ws(0, H, N, dk, dv, 512, 1) == 0
     assert ws(B, H, N, dk, dv, 0, 1) == 0
 
