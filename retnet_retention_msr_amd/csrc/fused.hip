@@ -1153,6 +1153,12 @@ hipError_t launch_fused_chunkwise(const uint16_t* q, const uint16_t* k, const ui
   const FusedJob* two = lay.second;
   if (a.nseg > 1 && (lay.reverse || two)) return hipErrorInvalidValue;
   if (two && state_out) return hipErrorInvalidValue;  // the second retention leaves no final state
+  if (lay.reverse || (two && two->reverse)) {
+    // Reverse order addresses a head's rows from one descriptor with 32-bit
+    // offsets; rows past the end must come out beyond its range.
+    const int64_t widest = std::max<int64_t>({lay.ldq > 0 ? lay.ldq : d.dk, lay.ldk > 0 ? lay.ldk : d.dk, d.dv});
+    if ((static_cast<int64_t>(d.N) - 1) * widest * 2 + widest * 2 >= (int64_t{1} << 30)) return hipErrorInvalidValue;
+  }
   a.ldq = lay.ldq > 0 ? lay.ldq : d.dk;
   a.ldk = lay.ldk > 0 ? lay.ldk : d.dk;
   a.reverse = lay.reverse ? 1 : 0;
